@@ -1,0 +1,213 @@
+/*
+ * binv.h -- libbinv: batch-invariant transformer kernels for AMD Instinct MI355X (gfx950).
+ *
+ * What "batch-invariant" means here (devpress.csdn.net explainer of "Defeating
+ * Nondeterminism in LLM Inference", section 2.3; tom-jerr.github.io
+ * "Batch-Invariant Kernel", Motivation): the bits of one row's (or one
+ * sequence's) output are a function of that row's own inputs only.  For a
+ * fixed weight shape (N, K), feature size d and attention shape (Hq, Hkv, D,
+ * page size, scale) they do not depend on M, B or T, on the row's position in
+ * the batch, on which other rows share the call, on how a prefill is split
+ * into chunks, on where the sequence's pages sit in the cache, or on whether a
+ * token is processed by the prefill or the decode entry point.  Every entry
+ * point is also run-to-run deterministic: no atomics, no data-dependent
+ * scheduling.
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller.  Nothing is
+ *     retained after return and the library allocates no device memory.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ *     default stream) and runs asynchronously; no entry point synchronises.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     non-zero status means nothing was enqueued, except BINV_ERR_LAUNCH,
+ *     which reports a failed launch (hipGetLastError).
+ *   - Data pointers must be 16-byte aligned.  Leading dimensions are in
+ *     elements and must keep every row 16-byte aligned (a multiple of 8 for
+ *     bf16, of 4 for fp32).
+ *   - bf16 is the 16-bit bfloat16 format; every conversion to bf16 rounds to
+ *     nearest, ties to even.  Accumulation is fp32.
+ *   - Preconditions that live in device memory (kv_lens, cu_q, page-table
+ *     entries) cannot be checked without a synchronisation; they are the
+ *     caller's contract and are stated per entry point.
+ *   - The library keeps no mutable global state; calls from several host
+ *     threads are safe.
+ */
+#ifndef BINV_H
+#define BINV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BINV_OK = 0,
+    BINV_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad leading dimension, misalignment */
+    BINV_ERR_UNSUPPORTED = 2,   /* a size or shape outside what the kernels implement */
+    BINV_ERR_WORKSPACE = 3,     /* workspace missing or smaller than binv_attn_workspace_bytes() */
+    BINV_ERR_LAUNCH = 4         /* the HIP runtime rejected a launch */
+} binv_status;
+
+typedef enum { BINV_F32 = 0, BINV_BF16 = 1 } binv_dtype;
+
+/* Largest KV length the attention entry points accept: 512 chunks of 256
+ * tokens, i.e. the fixed merge-tree depth of 9. */
+#define BINV_ATTN_CHUNK 256
+#define BINV_ATTN_MAX_CHUNKS 512
+#define BINV_ATTN_MAX_KV_LEN (BINV_ATTN_CHUNK * BINV_ATTN_MAX_CHUNKS)
+#define BINV_PAGE_SIZE 16
+
+/* Human-readable name of a status code (static storage). */
+const char* binv_status_str(int status);
+
+/* Library version string (static storage). */
+const char* binv_version(void);
+
+/* ------------------------------------------------------------------------
+ * RMSNorm, one workgroup per row.
+ * Defines: tom-jerr.github.io "Batch-Invariant Kernel", section RMSNorm
+ * (formula and the data-parallel reduction: each row reduced inside one
+ * core); devpress.csdn.net explainer, section 3.1 RMSNorm (x * rsqrt(mean(x^2)) * weight).
+ *
+ *   y[i, j] = x[i, j] * r_i * gamma[j],   r_i = 1 / sqrt((1/d) * sum_j x[i, j]^2 + eps)
+ *
+ * x      [M, d] row-major, leading dimension ldx, dtype x_dt (BINV_F32 or BINV_BF16)
+ * gamma  [d], dtype g_dt
+ * y      [M, d] row-major, leading dimension ldy, dtype y_dt
+ * The sum of squares of a row is formed inside one workgroup in an order fixed
+ * by d alone.  d must be a multiple of 8 (bf16 x) or 4 (fp32 x), 1 <= d <= 16384
+ * for bf16 x and <= 8192 for fp32 x (else BINV_ERR_UNSUPPORTED).  M = 0 is a no-op.
+ * x and y must not overlap.
+ * ------------------------------------------------------------------------ */
+int binv_rmsnorm(const void* x, int x_dt, int64_t ldx,
+                 const void* gamma, int g_dt,
+                 void* y, int y_dt, int64_t ldy,
+                 int64_t M, int64_t d, float eps, void* stream);
+
+/* ------------------------------------------------------------------------
+ * GEMM with one fixed tile configuration and no split-K.
+ * Defines: devpress.csdn.net explainer, section 3.2 Matmul
+ * (C[i,j] = sum_k A[i,k] B[k,j]; one kernel configuration for every batch
+ * size, split-K disabled); tom-jerr.github.io "Batch-Invariant Kernel",
+ * section GEMM (fixed tiling, K strategy decoupled from M).
+ *
+ *   C[i, j] = sum_k A[i, k] * W[k, j]
+ *
+ * A  bf16 [M, K] row-major, leading dimension lda
+ * W  bf16 [K, N] row-major, leading dimension ldw
+ * C  [M, N] row-major, leading dimension ldc, dtype c_dt (BINV_BF16 or BINV_F32)
+ * Each C element is accumulated in fp32 by bf16 matrix-core instructions over
+ * k in ascending blocks of 32, one accumulator per element, whatever M is.
+ * K and N must be multiples of 8; M, N, K <= 2^31 - 1.  M = 0 or N = 0 is a
+ * no-op; K = 0 writes zeros.  C must not overlap A or W.
+ * ------------------------------------------------------------------------ */
+int binv_gemm_bf16(const void* A, int64_t lda,
+                   const void* W, int64_t ldw,
+                   void* C, int c_dt, int64_t ldc,
+                   int64_t M, int64_t N, int64_t K, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Paged KV cache layout used by both attention entry points.
+ * (The pages describe a KV cache whose reduction length is cached plus new
+ * tokens -- devpress.csdn.net explainer, section 3.3 -- but fix no layout.)
+ *
+ *   k_cache  bf16 [num_pages, Hkv, page_size, D]   (slot, then feature)
+ *   v_cache  bf16 [num_pages, Hkv, D, page_size]   (feature, then slot)
+ *   page_table int32 [B, pt_stride]
+ *   logical token t of sequence b lives in page page_table[b * pt_stride + t / page_size],
+ *   slot t % page_size.  page_size must be 16; D must be 64 or 128;
+ *   Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8, 16}.
+ *
+ * Only the first ceil(kv_lens[b] / 16) page-table entries of a sequence are
+ * read, and slots at or past kv_lens[b] are never used (they may hold any
+ * bits, NaN included).
+ *
+ * Attention computed (devpress.csdn.net explainer, section 3.3: two
+ * reductions over the KV length; fixed-size split example):
+ *   a query row of head h at absolute position p attends to keys 0..p of KV
+ *   head h / (Hq / Hkv):  out = sum_j softmax_j(scale * q . k_j) v_j.
+ *   The keys are split into fixed 256-token chunks counted from absolute
+ *   position 0 (chunk c = [256c, 256c + 256) intersected with [0, p]); each
+ *   chunk yields an fp32 partial (max, sum of weights, weighted sum of values)
+ *   and the partials are merged by a binary tree padded to a fixed depth of 9
+ *   (tom-jerr.github.io "Batch-Invariant Kernel", section Flash Attention,
+ *   fixed-size Split-KV with a chunk-count-independent tree merge).
+ *   Decode and prefill run the same chunk and merge code, so a token's output
+ *   bits are the same on either path.  An output element that is exactly zero
+ *   is written as +0.
+ *
+ * Workspace: fp32 partials, caller-owned, at least
+ *   binv_attn_workspace_bytes(n_query_tokens, Hq, D, max_kv_len) bytes.
+ * ------------------------------------------------------------------------ */
+size_t binv_attn_workspace_bytes(int64_t n_query_tokens, int Hq, int D, int64_t max_kv_len);
+
+/* Decode: one query token per sequence.
+ * q    bf16 [B, Hq, D]
+ * out  bf16 [B, Hq, D]
+ * kv_lens int32 [B]: KV length of each sequence INCLUDING the current token,
+ *   whose K/V must already be in the cache; the query sits at position
+ *   kv_lens[b] - 1.  Contract: 1 <= kv_lens[b] <= max_kv_len.
+ * max_kv_len: host-side upper bound used to size the grid (1..BINV_ATTN_MAX_KV_LEN).
+ * B = 0 is a no-op. */
+int binv_attn_decode_paged(const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* page_table, int64_t pt_stride,
+                           const int32_t* kv_lens,
+                           void* out,
+                           int64_t B, int64_t max_kv_len, int Hq, int Hkv, int D, int page_size,
+                           float scale, void* workspace, size_t ws_bytes, void* stream);
+
+/* Prefill / chunked prefill: a ragged batch of new tokens whose K/V are
+ * already written into the cache (one unified reduction over cached + new keys).
+ * q    bf16 [T, Hq, D], the new tokens of all sequences, sequence after sequence
+ * cu_q int32 [B + 1]: sequence b owns rows cu_q[b] .. cu_q[b+1]-1; cu_q[0] = 0, cu_q[B] = T
+ * kv_lens int32 [B]: KV length of sequence b after this step (cached + new)
+ * out  bf16 [T, Hq, D]
+ * Row i of sequence b sits at position kv_lens[b] - (cu_q[b+1] - cu_q[b]) + i.
+ * Contract: 0 <= cu_q[b+1] - cu_q[b] <= min(max_q_len, kv_lens[b]),
+ *           kv_lens[b] <= max_kv_len.
+ * T = 0 or B = 0 is a no-op. */
+int binv_attn_prefill_paged(const void* q, const int32_t* cu_q,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* page_table, int64_t pt_stride,
+                            const int32_t* kv_lens,
+                            void* out,
+                            int64_t B, int64_t T, int64_t max_q_len, int64_t max_kv_len,
+                            int Hq, int Hkv, int D, int page_size, float scale,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Shape-tuned comparators.  NOT batch-invariant, on purpose: they choose their
+ * reduction strategy from the batch shape the way the pages say production
+ * libraries do (devpress.csdn.net explainer, section 3.2, split-K when M is
+ * small; tom-jerr.github.io "Batch-Invariant Kernel", sections RMSNorm, GEMM
+ * and Flash Attention, shape-dependent splits).  They exist to measure the
+ * price of invariance and as positive controls for the invariance tests.
+ * Same arguments as the invariant entry points (plus a workspace for the GEMM).
+ * ------------------------------------------------------------------------ */
+size_t binv_gemm_bf16_tuned_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int binv_gemm_bf16_tuned(const void* A, int64_t lda,
+                         const void* W, int64_t ldw,
+                         void* C, int c_dt, int64_t ldc,
+                         int64_t M, int64_t N, int64_t K,
+                         void* workspace, size_t ws_bytes, void* stream);
+int binv_rmsnorm_tuned(const void* x, int x_dt, int64_t ldx,
+                       const void* gamma, int g_dt,
+                       void* y, int y_dt, int64_t ldy,
+                       int64_t M, int64_t d, float eps, void* stream);
+size_t binv_attn_decode_tuned_workspace_bytes(int64_t B, int Hq, int D, int64_t max_kv_len);
+int binv_attn_decode_paged_tuned(const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* page_table, int64_t pt_stride,
+                                 const int32_t* kv_lens,
+                                 void* out,
+                                 int64_t B, int64_t max_kv_len, int Hq, int Hkv, int D, int page_size,
+                                 float scale, void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BINV_H */

@@ -1,0 +1,183 @@
+// rmsnorm.hip -- RMSNorm with one workgroup per row (gfx950).
+//
+// Method: tom-jerr.github.io "Batch-Invariant Kernel", section RMSNorm
+// (data-parallel reduction: a row's sum of squares never leaves one core);
+// devpress.csdn.net explainer of "Defeating Nondeterminism in LLM Inference",
+// section 3.1 RMSNorm (x * rsqrt(mean(x^2) + eps) * weight).
+//
+// Reduction order of a row, fixed by d and the block size alone:
+//   1. thread t owns the 16-byte vectors t, t + NT, t + 2 NT, ... of the row
+//      and accumulates fmaf(x, x, ss) over them in that order, element by
+//      element inside each vector;
+//   2. a 64-lane xor butterfly (offsets 32, 16, ..., 1) combines the lanes of
+//      each wave; every lane ends with the same bits;
+//   3. the wave totals are added in wave order, ((w0 + w1) + w2) + ...
+// r = rsqrt(ss / d + eps); y = (x * r) * gamma, rounded once to the output type.
+// The row stays in registers between the reduction and the scaling pass, so
+// x is read from HBM exactly once.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace binv {
+
+namespace {
+
+template <bool B16, int N>
+__device__ __forceinline__ void unpack(const u32x4& v, float (&f)[N]) {
+    if constexpr (B16) {
+        static_assert(N == 8, "");
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f[2 * i] = lo_bf16(v[i]); f[2 * i + 1] = hi_bf16(v[i]); }
+    } else {
+        static_assert(N == 4, "");
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+    }
+}
+
+// load N consecutive elements (N = 4 or 8) of a bf16 or fp32 array starting at element e
+template <bool B16, int N>
+__device__ __forceinline__ void load_elems(const void* p, int64_t e, float (&f)[N]) {
+    if constexpr (B16) {
+        const bf16_t* b = reinterpret_cast<const bf16_t*>(p) + e;
+        if constexpr (N == 8) {
+            float t[8]; unpack<true, 8>(*reinterpret_cast<const u32x4*>(b), t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = t[i];
+        } else {
+            u32x2 w = *reinterpret_cast<const u32x2*>(b);
+            f[0] = lo_bf16(w[0]); f[1] = hi_bf16(w[0]); f[2] = lo_bf16(w[1]); f[3] = hi_bf16(w[1]);
+        }
+    } else {
+        const float* s = reinterpret_cast<const float*>(p) + e;
+#pragma unroll
+        for (int h = 0; h < N / 4; ++h) {
+            u32x4 w = *reinterpret_cast<const u32x4*>(s + 4 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[4 * h + i] = __uint_as_float(w[i]);
+        }
+    }
+}
+
+template <bool B16, int N>
+__device__ __forceinline__ void store_elems(void* p, int64_t e, const float (&f)[N]) {
+    if constexpr (B16) {
+        bf16_t* b = reinterpret_cast<bf16_t*>(p) + e;
+        if constexpr (N == 8) {
+            u32x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+            *reinterpret_cast<u32x4*>(b) = w;
+        } else {
+            u32x2 w;
+            w[0] = pack_bf16x2(f[0], f[1]); w[1] = pack_bf16x2(f[2], f[3]);
+            *reinterpret_cast<u32x2*>(b) = w;
+        }
+    } else {
+        float* s = reinterpret_cast<float*>(p) + e;
+#pragma unroll
+        for (int h = 0; h < N / 4; ++h) {
+            u32x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(f[4 * h + i]);
+            *reinterpret_cast<u32x4*>(s + 4 * h) = w;
+        }
+    }
+}
+
+template <bool XB, bool GB, bool YB, int NT, int MAXV>
+__global__ __launch_bounds__(NT) void rmsnorm_kernel(const void* __restrict__ x, int64_t ldx,
+                                                     const void* __restrict__ g,
+                                                     void* __restrict__ y, int64_t ldy,
+                                                     int d, float eps) {
+    constexpr int VEC = XB ? 8 : 4;                 // elements per 16-byte vector of x
+    constexpr int NW = NT / WAVE;
+    const int64_t row = blockIdx.x;
+    const int t = threadIdx.x;
+    const int nvec = d / VEC;
+    const char* xr = reinterpret_cast<const char*>(x) + row * ldx * (XB ? 2 : 4);
+
+    u32x4 xv[MAXV];
+    float ss = 0.0f;
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+        const int vi = t + v * NT;
+        if (vi < nvec) xv[v] = *reinterpret_cast<const u32x4*>(xr + (int64_t)vi * 16);
+    }
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+        const int vi = t + v * NT;
+        if (vi < nvec) {
+            float f[VEC];
+            unpack<XB, VEC>(xv[v], f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) ss = fmaf(f[e], f[e], ss);
+        }
+    }
+#pragma unroll
+    for (int off = WAVE / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+
+    __shared__ float wsum[NW];
+    if ((t & (WAVE - 1)) == 0) wsum[t / WAVE] = ss;
+    __syncthreads();
+    float tot = wsum[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) tot += wsum[w];
+    const float r = rsqrtf(tot / (float)d + eps);
+
+    char* yr = reinterpret_cast<char*>(y) + row * ldy * (YB ? 2 : 4);
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+        const int vi = t + v * NT;
+        if (vi < nvec) {
+            float f[VEC], gv[VEC], o[VEC];
+            unpack<XB, VEC>(xv[v], f);
+            load_elems<GB, VEC>(g, (int64_t)vi * VEC, gv);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[e] = (f[e] * r) * gv[e];
+            store_elems<YB, VEC>(yr, (int64_t)vi * VEC, o);
+        }
+    }
+}
+
+template <int NT, int MAXV>
+hipError_t dispatch(const void* x, int xb, int64_t ldx, const void* g, int gb, void* y, int yb,
+                    int64_t ldy, int64_t M, int d, float eps, hipStream_t s) {
+    dim3 grid((unsigned)M), block(NT);
+#define BINV_RMS(XB, GB, YB)                                                                     \
+    if (xb == XB && gb == GB && yb == YB) {                                                      \
+        hipLaunchKernelGGL((rmsnorm_kernel<XB, GB, YB, NT, MAXV>), grid, block, 0, s, x, ldx, g, \
+                           y, ldy, d, eps);                                                      \
+        return hipGetLastError();                                                                \
+    }
+    BINV_RMS(1, 1, 1) BINV_RMS(1, 1, 0) BINV_RMS(1, 0, 1) BINV_RMS(1, 0, 0)
+    BINV_RMS(0, 1, 1) BINV_RMS(0, 1, 0) BINV_RMS(0, 0, 1) BINV_RMS(0, 0, 0)
+#undef BINV_RMS
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// The invariant kernel: 256 lanes per row for every M.
+hipError_t launch_rmsnorm(const void* x, int xb, int64_t ldx, const void* g, int gb, void* y,
+                          int yb, int64_t ldy, int64_t M, int d, float eps, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    return dispatch<256, 8>(x, xb, ldx, g, gb, y, yb, ldy, M, d, eps, s);
+}
+
+// Comparator: block size picked from M (more lanes per row when there are few
+// rows, fewer when there are many), which changes the reduction tree with M.
+hipError_t launch_rmsnorm_tuned(const void* x, int xb, int64_t ldx, const void* g, int gb,
+                                void* y, int yb, int64_t ldy, int64_t M, int d, float eps,
+                                hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    const int vec = xb ? 8 : 4;
+    const int nvec = d / vec;
+    if (M <= 64 && nvec <= 1024 * 2)
+        return dispatch<1024, 2>(x, xb, ldx, g, gb, y, yb, ldy, M, d, eps, s);
+    if (M >= 4096 && nvec <= 128 * 16)
+        return dispatch<128, 16>(x, xb, ldx, g, gb, y, yb, ldy, M, d, eps, s);
+    return dispatch<256, 8>(x, xb, ldx, g, gb, y, yb, ldy, M, d, eps, s);
+}
+
+}  // namespace binv

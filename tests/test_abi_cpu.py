@@ -1,0 +1,129 @@
+"""Host-side checks of libbinv that need no GPU: the library loads, exports
+every entry point the header declares, and rejects bad arguments with the
+documented status codes before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_deterministic_fixed_amd as binv
+from invariant_deterministic_fixed_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "binv.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(binv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ["binv_gemm_bf16", "binv_rmsnorm", "binv_attn_decode_paged", "binv_attn_prefill_paged"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version():
+    assert binv.status_str(0) == "BINV_OK"
+    assert "WORKSPACE" in binv.status_str(3)
+    assert "unknown" in binv.status_str(99)
+    assert "gfx950" in binv.version()
+
+
+L = None  # null pointer
+FAKE = 1 << 20   # a 16-byte aligned non-null address; never dereferenced by these calls
+
+
+def _lib():
+    return binding.lib()
+
+
+def test_rmsnorm_validation():
+    f = _lib().binv_rmsnorm
+    assert f(L, 1, 8, L, 1, L, 1, 8, 0, 8, 1e-6, L) == OK                 # M = 0: no-op
+    assert f(L, 1, 8, L, 1, L, 1, 8, 4, 8, 1e-6, L) == INVALID            # null pointers
+    assert f(FAKE, 1, 8, FAKE, 1, FAKE, 1, 8, -1, 8, 1e-6, L) == INVALID  # negative M
+    assert f(FAKE, 1, 12, FAKE, 1, FAKE, 1, 8, 4, 8, 1e-6, L) == INVALID  # ldx not 16B multiple
+    assert f(FAKE + 2, 1, 8, FAKE, 1, FAKE, 1, 8, 4, 8, 1e-6, L) == INVALID  # misaligned x
+    assert f(FAKE, 1, 16, FAKE, 1, FAKE, 1, 16, 4, 12, 1e-6, L) == UNSUPPORTED  # d % 8
+    assert f(FAKE, 1, 32768, FAKE, 1, FAKE, 1, 32768, 4, 32768, 1e-6, L) == UNSUPPORTED
+    assert f(FAKE, 7, 8, FAKE, 1, FAKE, 1, 8, 4, 8, 1e-6, L) == INVALID   # bad dtype
+    assert f(FAKE, 1, 8, FAKE, 1, FAKE, 1, 8, 4, 8, -1.0, L) == INVALID   # negative eps
+
+
+def test_gemm_validation():
+    f = _lib().binv_gemm_bf16
+    assert f(L, 8, L, 8, L, 1, 8, 0, 8, 8, L) == OK                      # M = 0
+    assert f(L, 8, L, 8, L, 1, 8, 8, 0, 8, L) == OK                      # N = 0
+    assert f(L, 8, L, 8, L, 1, 8, 8, 8, 8, L) == INVALID                 # nulls
+    assert f(FAKE, 8, FAKE, 8, FAKE, 1, 8, 8, 8, -8, L) == INVALID       # negative K
+    assert f(FAKE, 8, FAKE, 8, FAKE, 1, 8, 8, 8, 12, L) == INVALID       # lda < K
+    assert f(FAKE, 16, FAKE, 16, FAKE, 1, 16, 8, 12, 16, L) == UNSUPPORTED  # N % 8
+    assert f(FAKE, 16, FAKE, 16, FAKE, 1, 16, 8, 16, 12, L) == UNSUPPORTED  # K % 8
+    assert f(FAKE, 9, FAKE, 8, FAKE, 1, 8, 8, 8, 8, L) == INVALID        # lda not 16B multiple
+    g = _lib().binv_gemm_bf16_tuned
+    need = _lib().binv_gemm_bf16_tuned_workspace_bytes(1, 4096, 4096)
+    assert need > 0
+    assert g(FAKE, 4096, FAKE, 4096, FAKE, 1, 4096, 1, 4096, 4096, L, 0, L) == WORKSPACE
+
+
+def _dec(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, pt=FAKE, pts=4, kl=FAKE, out=FAKE, B=2, maxl=64, Hq=8,
+             Hkv=2, D=128, page=16, scale=0.1, ws=FAKE, wsb=1 << 30, s=L)
+    a.update(over)
+    return _lib().binv_attn_decode_paged(a["q"], a["k"], a["v"], a["pt"], a["pts"], a["kl"],
+                                         a["out"], a["B"], a["maxl"], a["Hq"], a["Hkv"], a["D"],
+                                         a["page"], a["scale"], a["ws"], a["wsb"], a["s"])
+
+
+def test_attention_decode_validation():
+    assert _dec(B=0) == OK
+    assert _dec(q=L) == INVALID
+    assert _dec(Hq=6, Hkv=4) == INVALID
+    assert _dec(Hq=6, Hkv=2) == UNSUPPORTED            # group of 3
+    assert _dec(D=96) == UNSUPPORTED
+    assert _dec(page=32) == UNSUPPORTED
+    assert _dec(maxl=0) == INVALID
+    assert _dec(maxl=256 * 512 + 1) == UNSUPPORTED
+    assert _dec(wsb=16) == WORKSPACE
+    assert _dec(ws=L) == WORKSPACE
+    assert _dec(scale=float("nan")) == INVALID
+    assert _dec(B=70000) == UNSUPPORTED
+
+
+def test_attention_prefill_validation():
+    f = _lib().binv_attn_prefill_paged
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 10, 10, 64, 8, 2, 128, 16, 0.1,
+            FAKE, 1 << 30, L]
+    assert f(*args[:8], 0, *args[9:]) == OK                       # B = 0
+    assert f(*args[:9], 0, *args[10:]) == OK                      # T = 0
+    bad = list(args); bad[1] = L
+    assert f(*bad) == INVALID                                     # null cu_q
+    bad = list(args); bad[10] = 100
+    assert f(*bad) == INVALID                                     # max_q_len > max_kv_len
+    bad = list(args); bad[18] = 8
+    assert f(*bad) == WORKSPACE
+
+
+def test_workspace_sizes():
+    ws = binv.attn_workspace_bytes(256, 32, 128, 32768)
+    assert ws == 256 * 32 * 128 * (128 + 2) * 4
+    assert binv.attn_workspace_bytes(0, 32, 128, 100) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libbinv.so")
+    with pytest.raises(RuntimeError, match="no fallback"):
+        binding.lib()

@@ -1,0 +1,215 @@
+"""Paged decode / prefill attention on the GPU: parity with the fp64 oracle,
+closed forms, bitwise invariance of a target sequence to its batch
+neighbours, batch position and page placement, and bitwise equality of
+one-shot prefill, chunked prefill and decode."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_deterministic_fixed_amd as binv
+import oracle
+from invariant_deterministic_fixed_amd import synth
+from helpers import TOL_BF16, assert_bitwise_equal, f64, row_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def make_cache(lens, Hkv, D, seed, device=DEV, seqs=None, pt_stride=None):
+    if seqs is None:
+        seqs = [synth.random_kv(int(L), Hkv, D, seed + 17 * i, device) for i, L in enumerate(lens)]
+    return synth.PagedKV(seqs, Hkv, D, seed, device=device, pt_stride=pt_stride), seqs
+
+
+def decode(cache, q, scale, max_kv_len=None, **kw):
+    mkl = int(max_kv_len or max(int(x) for x in cache.lens))
+    return binv.attn_decode(q, cache.k_cache, cache.v_cache, cache.page_table, cache.kv_lens,
+                            mkl, scale, **kw)
+
+
+def oracle_decode(q, seqs, lens, scale):
+    outs = []
+    for b, (k, v) in enumerate(seqs):
+        L = int(lens[b])
+        outs.append(oracle.attention(f64(q[b:b + 1]), [L - 1], f64(k), f64(v), scale)[0])
+    return np.stack(outs)
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_decode_parity_tiny(B):
+    Hq = Hkv = 4
+    D = 64
+    lens = synth.uniform_int_lengths(B, 1, 300, synth.seed_for(1) + B)
+    cache, seqs = make_cache(lens, Hkv, D, synth.seed_for(1) + B)
+    q = synth.normal((B, Hq, D), 1.0, 77 + B, DEV)
+    scale = 1 / math.sqrt(D)
+    out = decode(cache, q, scale)
+    ref = oracle_decode(q, seqs, lens, scale)
+    err = row_rel_err(f64(out), ref)
+    assert err.max() <= TOL_BF16, err.max()
+
+
+@pytest.mark.parametrize("lens", [[1, 255, 256, 257], [1000, 5000, 16, 4096], [32768]])
+def test_decode_parity_gqa_shape(lens):
+    Hq, Hkv, D = 32, 8, 128
+    cache, seqs = make_cache(lens, Hkv, D, synth.seed_for(4) + len(lens))
+    q = synth.normal((len(lens), Hq, D), 1.0, 5, DEV)
+    scale = 1 / math.sqrt(D)
+    out = decode(cache, q, scale)
+    assert torch.isfinite(out.float()).all()
+    ref = oracle_decode(q, seqs, lens, scale)
+    err = row_rel_err(f64(out), ref)
+    assert err.max() <= TOL_BF16, err.max()
+
+
+def test_decode_single_key_returns_v0_bitwise():
+    Hq, Hkv, D = 8, 2, 128
+    cache, seqs = make_cache([1, 1, 1], Hkv, D, 3)
+    q = synth.normal((3, Hq, D), 1.0, 4, DEV)
+    out = decode(cache, q, 0.1).cpu()
+    for b in range(3):
+        v0 = seqs[b][1][0].cpu()                       # [Hkv, D]
+        for h in range(Hq):
+            assert_bitwise_equal(out[b, h], v0[h // (Hq // Hkv)], f"b={b} h={h}")
+
+
+def test_decode_two_token_closed_form():
+    # D = 64, scale = 1/8: q = e0, k0 = 0, k1 = 8 e0 -> scores [0, 1] -> weights
+    # [1 - s(1), s(1)] with s the logistic function; v0 = e0, v1 = e1
+    D, Hq, Hkv = 64, 1, 1
+    k = torch.zeros((2, 1, D), dtype=torch.bfloat16); k[1, 0, 0] = 8.0
+    v = torch.zeros((2, 1, D), dtype=torch.bfloat16); v[0, 0, 0] = 1.0; v[1, 0, 1] = 1.0
+    cache, _ = make_cache([2], Hkv, D, 1, seqs=[(k.to(DEV), v.to(DEV))])
+    q = torch.zeros((1, Hq, D), dtype=torch.bfloat16, device=DEV); q[0, 0, 0] = 1.0
+    out = f64(decode(cache, q, 1 / 8))[0, 0]
+    w1 = 1 / (1 + math.exp(-1))
+    assert abs(out[0] - (1 - w1)) < 4e-3 and abs(out[1] - w1) < 4e-3
+    assert np.all(out[2:] == 0)
+
+
+def test_decode_all_keys_equal_gives_mean_of_v():
+    Hq, Hkv, D, L = 4, 1, 128, 700
+    k = synth.normal((1, Hkv, D), 1.0, 8).expand(L, Hkv, D).contiguous()
+    v = synth.normal((L, Hkv, D), 1.0, 9)
+    cache, _ = make_cache([L], Hkv, D, 2, seqs=[(k.to(DEV), v.to(DEV))])
+    q = synth.normal((1, Hq, D), 1.0, 10, DEV)
+    out = f64(decode(cache, q, 0.09))[0]
+    mean = f64(v)[:, 0].mean(axis=0)
+    assert row_rel_err(out, np.broadcast_to(mean, out.shape)).max() <= 1e-2
+
+
+def test_decode_invariance_to_neighbours_position_and_pages():
+    Hq, Hkv, D = 32, 8, 128
+    scale = 1 / math.sqrt(D)
+    L_t = 3000
+    tk, tv = synth.random_kv(L_t, Hkv, D, synth.TARGET_SEED, DEV)
+    tq = synth.normal((1, Hq, D), 1.0, synth.TARGET_SEED + 1, DEV)
+    cache, _ = make_cache([L_t], Hkv, D, 1, seqs=[(tk, tv)])
+    alone = decode(cache, tq, scale)
+    ref = oracle_decode(tq, [(tk, tv)], [L_t], scale)
+    assert row_rel_err(f64(alone), ref).max() <= TOL_BF16
+    rng = np.random.default_rng(2024)
+    plan = [(1, 32768), (7, 32768), (31, 32768), (255, 32768), (int(rng.integers(2, 200)), 4096)]
+    for trial, (n, hi) in enumerate(plan):
+        lens = synth.log_uniform_lengths(n, 128, hi, synth.seed_for(4, trial))
+        pos = int(rng.integers(0, n + 1))
+        seqs = [synth.random_kv(int(L), Hkv, D, synth.seed_for(4, trial) + 31 * i, DEV)
+                for i, L in enumerate(lens)]
+        seqs.insert(pos, (tk, tv))
+        all_lens = [int(k.shape[0]) for k, _ in seqs]
+        cache, _ = make_cache(all_lens, Hkv, D, synth.seed_for(4, trial) + 5, seqs=seqs)
+        q = synth.normal((n + 1, Hq, D), 1.0, synth.seed_for(4, trial) + 6, DEV)
+        q[pos] = tq[0]
+        out = decode(cache, q, scale, max_kv_len=max(all_lens) + 100)
+        assert_bitwise_equal(out[pos:pos + 1], alone, f"trial {trial}: {n} neighbours, pos {pos}")
+        assert torch.isfinite(out.float()).all()
+        del cache, seqs, out
+        torch.cuda.empty_cache()
+
+
+def test_decode_run_to_run_deterministic():
+    lens = [4000, 200, 9000]
+    cache, _ = make_cache(lens, 8, 128, 44)
+    q = synth.normal((3, 32, 128), 1.0, 45, DEV)
+    a = decode(cache, q, 0.088)
+    b = decode(cache, q, 0.088)
+    assert_bitwise_equal(a, b, "repeat")
+
+
+def _prefill(cache, q, cu_q, kv_lens, max_q_len, max_kv_len, scale):
+    return binv.attn_prefill(q, torch.as_tensor(cu_q, dtype=torch.int32, device=DEV),
+                             cache.k_cache, cache.v_cache, cache.page_table,
+                             torch.as_tensor(kv_lens, dtype=torch.int32, device=DEV),
+                             max_q_len, max_kv_len, scale)
+
+
+def test_prefill_parity_ragged_batch():
+    Hq, Hkv, D = 8, 2, 128
+    lens = [300, 17, 1000, 600]
+    qlens = [300, 5, 33, 1]          # one-shot, tails of cached sequences, single token
+    cache, seqs = make_cache(lens, Hkv, D, 61)
+    T = sum(qlens)
+    q = synth.normal((T, Hq, D), 1.0, 62, DEV)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    scale = 1 / math.sqrt(D)
+    out = _prefill(cache, q, cu, lens, max(qlens), max(lens), scale)
+    for b in range(len(lens)):
+        k, v = seqs[b]
+        pos = [lens[b] - qlens[b] + i for i in range(qlens[b])]
+        ref = oracle.attention(f64(q[cu[b]:cu[b + 1]]), pos, f64(k), f64(v), scale)
+        err = row_rel_err(f64(out[cu[b]:cu[b + 1]]), ref)
+        assert err.max() <= TOL_BF16, (b, err.max())
+
+
+def test_prefill_chunked_and_decode_bitwise_equal():
+    Hq, Hkv, D, L = 32, 8, 128, 4096
+    scale = 1 / math.sqrt(D)
+    k, v = synth.random_kv(L, Hkv, D, synth.seed_for(4), DEV)
+    cache, _ = make_cache([L], Hkv, D, 9, seqs=[(k, v)])
+    q = synth.normal((L, Hq, D), 1.0, synth.seed_for(4) + 1, DEV)
+    one_shot = _prefill(cache, q, [0, L], [L], L, L, scale)
+    for step in [256, 512, 2048]:
+        parts = []
+        for s in range(0, L, step):
+            e = min(L, s + step)
+            parts.append(_prefill(cache, q[s:e].contiguous(), [0, e - s], [e], e - s, L, scale))
+        assert_bitwise_equal(torch.cat(parts), one_shot, f"chunked prefill, chunk {step}")
+    # decode of every position at once: 4096 "sequences" sharing the one page table
+    pt = cache.page_table[:1].expand(L, -1).contiguous()
+    kv_lens = torch.arange(1, L + 1, dtype=torch.int32, device=DEV)
+    dec = binv.attn_decode(q, cache.k_cache, cache.v_cache, pt, kv_lens, L, scale)
+    assert_bitwise_equal(dec, one_shot, "decode vs prefill")
+    # sampled oracle parity
+    rows = [0, 1, 255, 256, 257, 1000, 2048, 4095]
+    ref = oracle.attention(f64(q[rows]), rows, f64(k), f64(v), scale)
+    assert row_rel_err(f64(one_shot[rows]), ref).max() <= TOL_BF16
+
+
+def test_prefill_tile_positions_do_not_change_bits():
+    # the same tokens prefilled at different offsets inside the 16-row tiles
+    Hq, Hkv, D, L = 32, 8, 128, 777
+    scale = 0.09
+    k, v = synth.random_kv(L, Hkv, D, 12, DEV)
+    cache, _ = make_cache([L], Hkv, D, 13, seqs=[(k, v)])
+    q = synth.normal((L, Hq, D), 1.0, 14, DEV)
+    ref = _prefill(cache, q, [0, L], [L], L, L, scale)
+    for s in [1, 2, 3, 5, 333]:
+        part = _prefill(cache, q[s:].contiguous(), [0, L - s], [L], L - s, L, scale)
+        assert_bitwise_equal(part, ref[s:], f"offset {s}")
+
+
+def test_mha_tiny_head_dim_64_prefill_and_decode():
+    Hq = Hkv = 4
+    D, L = 64, 300
+    k, v = synth.random_kv(L, Hkv, D, 15, DEV)
+    cache, _ = make_cache([L], Hkv, D, 16, seqs=[(k, v)])
+    q = synth.normal((L, Hq, D), 1.0, 17, DEV)
+    pf = _prefill(cache, q, [0, L], [L], L, L, 0.125)
+    pt = cache.page_table[:1].expand(L, -1).contiguous()
+    dec = binv.attn_decode(q, cache.k_cache, cache.v_cache, pt,
+                           torch.arange(1, L + 1, dtype=torch.int32, device=DEV), L, 0.125)
+    assert_bitwise_equal(dec, pf, "decode vs prefill, D=64")
+    ref = oracle.attention(f64(q), list(range(L)), f64(k), f64(v), 0.125)
+    assert row_rel_err(f64(pf), ref).max() <= TOL_BF16
