@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-invariant hot path on one MI355X.
+
+One step = one pass of every hot-path kernel over one batch of synthetic input:
+  1. RMSNorm      x bf16 [8192, 4096] (N(0,3), 1% outliers at +-50) -> y bf16
+  2. GEMM         y [8192, 4096] x W bf16 [4096, 4096] (N(0,0.02)) -> C bf16
+  3. decode attn  paged, 32 query / 8 KV heads of 128, B = 256 sequences with
+                  KV lengths log-uniform in [128, 32768], pages shuffled
+  4. prefill attn one 4096-token sequence, same head shape, one shot
+Inputs are resident in HBM before the timed region.  Each leg is bracketed by
+HIP events recorded on the stream the kernels are launched on (torch's current
+stream).  The decode leg streams ~6 GB of KV, far more than the 256 MB
+last-level cache, so every leg starts from a cache the other legs have
+flushed.
+
+`value` is the GEMM leg in TFLOP/s (2*M*N*K per launch / mean launch time);
+the decode-attention GB/s (algorithmic bytes: K, V, q, out, page table) is
+reported beside it with its own roofline.  `cpu_baseline` times the fp64
+oracle on a bounded sample of the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--profile-copy]   (adds one 1 GiB device copy, the calibration kernel
+                           for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "batch-invariant GEMM TFLOP/s + decode-attn GB/s (% roofline), bitwise-invariant"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+RMS_M, HIDDEN = 8192, 4096
+GEMM_M, GEMM_N, GEMM_K = 8192, 4096, 4096
+DEC_B, HQ, HKV, HD = 256, 32, 8, 128
+DEC_LMIN, DEC_LMAX = 128, 32768
+PREFILL_T = 4096
+WORKLOAD = (f"rmsnorm {RMS_M}x{HIDDEN} bf16 -> gemm {GEMM_M}x{GEMM_N}x{GEMM_K} bf16 -> "
+            f"paged decode attn B={DEC_B} Hq={HQ} Hkv={HKV} D={HD} L~logU[{DEC_LMIN},{DEC_LMAX}] "
+            f"-> prefill attn T={PREFILL_T}")
+
+
+def build_workload(device="cuda:0", seed_base=0):
+    """All inputs of one step, resident on `device`."""
+    import torch
+
+    from invariant_deterministic_fixed_amd import synth
+    import invariant_deterministic_fixed_amd as binv
+
+    w = {}
+    s3, s2, s4 = synth.seed_for(3), synth.seed_for(2), synth.seed_for(4)
+    x = synth.normal((RMS_M, HIDDEN), 3.0, s3 + seed_base, device, dtype=torch.float32)
+    w["x"] = synth.with_outliers(x, 0.01, 50.0, s3 + 1 + seed_base).to(torch.bfloat16)
+    del x
+    w["gamma"] = synth.uniform((HIDDEN,), 0.5, 1.5, s3 + 2, device)
+    w["y"] = torch.empty((RMS_M, HIDDEN), dtype=torch.bfloat16, device=device)
+    w["W"] = synth.normal((GEMM_K, GEMM_N), 0.02, s2 + 7, device)
+    w["C"] = torch.empty((GEMM_M, GEMM_N), dtype=torch.bfloat16, device=device)
+
+    lens = synth.log_uniform_lengths(DEC_B, DEC_LMIN, DEC_LMAX, s4 + seed_base)
+    seqs = [synth.random_kv(int(L), HKV, HD, s4 + 100 + 31 * i, device) for i, L in enumerate(lens)]
+    w["dec_cache"] = synth.PagedKV(seqs, HKV, HD, s4 + 5, device=device)
+    del seqs
+    w["dec_lens"] = lens
+    w["dec_max_kv"] = int(lens.max())
+    w["dec_q"] = synth.normal((DEC_B, HQ, HD), 1.0, s4 + 6, device)
+    w["dec_out"] = torch.empty_like(w["dec_q"])
+    w["dec_ws"] = torch.empty(binv.attn_workspace_bytes(DEC_B, HQ, HD, w["dec_max_kv"]),
+                              dtype=torch.uint8, device=device)
+
+    pk, pv = synth.random_kv(PREFILL_T, HKV, HD, s4 + 9, device)
+    w["pf_kv"] = (pk, pv)
+    w["pf_cache"] = synth.PagedKV([(pk, pv)], HKV, HD, s4 + 10, device=device)
+    w["pf_q"] = synth.normal((PREFILL_T, HQ, HD), 1.0, s4 + 11, device)
+    w["pf_cu"] = torch.tensor([0, PREFILL_T], dtype=torch.int32, device=device)
+    w["pf_out"] = torch.empty_like(w["pf_q"])
+    w["pf_ws"] = torch.empty(binv.attn_workspace_bytes(PREFILL_T, HQ, HD, PREFILL_T),
+                             dtype=torch.uint8, device=device)
+    w["scale"] = 1.0 / math.sqrt(HD)
+    return w
+
+
+def run_step(w, events=None):
+    """One pass of the hot path; if `events` (5 torch.cuda.Event) is given the
+    legs are bracketed by them."""
+    import invariant_deterministic_fixed_amd as binv
+
+    ev = events or [None] * 5
+    rec = (lambda e: e.record()) if events else (lambda e: None)
+    rec(ev[0])
+    binv.rmsnorm(w["x"], w["gamma"], 1e-6, out=w["y"])
+    rec(ev[1])
+    binv.gemm(w["y"], w["W"], out=w["C"])
+    rec(ev[2])
+    c = w["dec_cache"]
+    binv.attn_decode(w["dec_q"], c.k_cache, c.v_cache, c.page_table, c.kv_lens, w["dec_max_kv"],
+                     w["scale"], out=w["dec_out"], workspace=w["dec_ws"])
+    rec(ev[3])
+    p = w["pf_cache"]
+    binv.attn_prefill(w["pf_q"], w["pf_cu"], p.k_cache, p.v_cache, p.page_table, p.kv_lens,
+                      PREFILL_T, PREFILL_T, w["scale"], out=w["pf_out"], workspace=w["pf_ws"])
+    rec(ev[4])
+
+
+def algorithmic(w):
+    """Algorithmic work per launch of each leg (what the method must move / compute)."""
+    lens = w["dec_lens"]
+    sum_l = int(lens.sum())
+    dec_bytes = (sum_l * HKV * HD * 2 * 2                   # K and V, bf16
+                 + 2 * DEC_B * HQ * HD * 2                   # q in, out
+                 + int(sum(-(-int(L) // 16) for L in lens)) * 4 + DEC_B * 4)   # page table, lens
+    return {
+        "rmsnorm_bytes": 2 * RMS_M * HIDDEN * 2 + HIDDEN * 2,
+        "gemm_flops": 2 * GEMM_M * GEMM_N * GEMM_K,
+        "gemm_bytes": 2 * (GEMM_M * GEMM_K + GEMM_K * GEMM_N + GEMM_M * GEMM_N),
+        "decode_bytes": dec_bytes,
+        "decode_sum_kv": sum_l,
+        "prefill_flops": 4 * HQ * HD * (PREFILL_T * (PREFILL_T + 1) // 2),
+    }
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(kernel_key):
+    """Measured HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or _sha(src) != rec["source_sha256"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def cpu_baseline(w, gemm_rows=2048, max_seqs=48):
+    """The fp64 oracle on a bounded sample of the same workload (the very same
+    input values, copied from HBM to the host), on the host cores."""
+    import oracle
+
+    xd = w["x"][:gemm_rows].double().cpu().numpy()
+    gd = w["gamma"].double().cpu().numpy()
+    Wd = w["W"].double().cpu().numpy()
+    t0 = time.perf_counter()
+    y = oracle.round_bf16(oracle.rmsnorm(xd, gd, 1e-6))
+    oracle.gemm(y, Wd)
+    t_gemm = time.perf_counter() - t0
+    gemm_tflops = 2.0 * gemm_rows * GEMM_N * GEMM_K / t_gemm / 1e12
+
+    lens = w["dec_lens"]
+    q = w["dec_q"].double().cpu().numpy()
+    n_seq, nbytes, t_att = 0, 0, 0.0
+    for b in range(min(DEC_B, max_seqs)):
+        k, v = w["dec_cache"].logical(b)
+        kd, vd = k.double().cpu().numpy(), v.double().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.attention(q[b:b + 1], [int(lens[b]) - 1], kd, vd, w["scale"])
+        t_att += time.perf_counter() - t0
+        n_seq += 1
+        nbytes += int(lens[b]) * HKV * HD * 2 * 2 + 2 * HQ * HD * 2
+    return {
+        "value": gemm_tflops,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 RMSNorm + GEMM of {gemm_rows} of the {GEMM_M} rows ({t_gemm:.1f} s); "
+                   f"fp64 decode attention of {n_seq} of the {DEC_B} sequences "
+                   f"({t_att:.1f} s, {nbytes / t_att / 1e9:.3f} GB/s)"),
+        "decode_attn_GBps": nbytes / t_att / 1e9,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = build_workload(dev)
+    work = algorithmic(w)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        run_step(w)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        run_step(w, evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    legs = ["rmsnorm", "gemm", "decode_attn", "prefill_attn"]
+    ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(legs)}
+    s = {n: ms[n] * 1e-3 for n in legs}
+    gemm_tflops = work["gemm_flops"] / s["gemm"] / 1e12
+    dec_gbps = work["decode_bytes"] / s["decode_attn"] / 1e9
+    rms_gbps = work["rmsnorm_bytes"] / s["rmsnorm"] / 1e9
+    pf_tflops = work["prefill_flops"] / s["prefill_attn"] / 1e12
+
+    if args.profile_copy:
+        # calibration for the HBM byte counters: one elementwise kernel that
+        # reads 1 GiB and writes 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+
+    gemm_traffic = traffic_for("gemm_bf16_kernel")
+    dec_traffic = traffic_for("attn_decode")
+    out = {
+        "metric": METRIC,
+        "value": round(gemm_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "gemm": [GEMM_M, GEMM_N, GEMM_K],
+                   "rmsnorm": [RMS_M, HIDDEN], "decode_B": DEC_B,
+                   "decode_sum_kv_tokens": work["decode_sum_kv"], "prefill_T": PREFILL_T,
+                   "heads": [HQ, HKV, HD], "page_size": 16, "split_kv_chunk": 256},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": gemm_traffic, "kernel": "gemm_bf16_kernel",
+                     "per_launch": {"flops": work["gemm_flops"], "bytes": work["gemm_bytes"]}},
+        "decode_attn": {"value": round(dec_gbps, 1), "unit": "GB/s",
+                        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1),
+                                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                     "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                                     "traffic": dec_traffic,
+                                     "kernel": "attn_chunk_kernel + attn_merge_kernel",
+                                     "per_launch": {"bytes": work["decode_bytes"]}}},
+        "legs_ms": {n: round(ms[n], 4) for n in legs},
+        "rmsnorm_GBps": round(rms_gbps, 1),
+        "rmsnorm_frac_hbm": round(rms_gbps / PEAK_HBM_GBPS, 4),
+        "prefill_attn_TFLOPs": round(pf_tflops, 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

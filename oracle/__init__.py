@@ -41,6 +41,8 @@ def _load():
     P = ctypes.POINTER(ctypes.c_double)
     PI = ctypes.POINTER(ctypes.c_int64)
     i64 = ctypes.c_int64
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
     lib.oracle_round_bf16.restype = ctypes.c_double
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
     lib.oracle_round_bf16_array.restype = None
@@ -66,6 +68,11 @@ def _f64(a):
 
 def _p(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def num_threads():
+    """OpenMP threads the oracle's row loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def round_bf16(x):
