@@ -149,7 +149,7 @@ def traffic_for(kernel_key):
     return rec["hbm_bytes_per_launch"]
 
 
-def cpu_baseline(w, gemm_rows=2048, max_seqs=48):
+def cpu_baseline(w, gemm_rows=GEMM_M, max_seqs=DEC_B, prefill_rows=512):
     """The fp64 oracle on a bounded sample of the same workload (the very same
     input values, copied from HBM to the host), on the host cores."""
     import oracle
@@ -174,6 +174,14 @@ def cpu_baseline(w, gemm_rows=2048, max_seqs=48):
         t_att += time.perf_counter() - t0
         n_seq += 1
         nbytes += int(lens[b]) * HKV * HD * 2 * 2 + 2 * HQ * HD * 2
+    pk, pv = w["pf_kv"]
+    rows = list(range(0, PREFILL_T, PREFILL_T // prefill_rows))
+    pq = w["pf_q"][rows].double().cpu().numpy()
+    kd, vd = pk.double().cpu().numpy(), pv.double().cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.attention(pq, rows, kd, vd, w["scale"])
+    t_pf = time.perf_counter() - t0
+    pf_flops = 4 * HQ * HD * sum(r + 1 for r in rows)
     return {
         "value": gemm_tflops,
         "unit": "TFLOP/s",
@@ -181,8 +189,11 @@ def cpu_baseline(w, gemm_rows=2048, max_seqs=48):
         "kind": "oracle",
         "sample": (f"fp64 RMSNorm + GEMM of {gemm_rows} of the {GEMM_M} rows ({t_gemm:.1f} s); "
                    f"fp64 decode attention of {n_seq} of the {DEC_B} sequences "
-                   f"({t_att:.1f} s, {nbytes / t_att / 1e9:.3f} GB/s)"),
+                   f"({t_att:.1f} s, {nbytes / t_att / 1e9:.3f} GB/s); fp64 prefill attention of "
+                   f"{len(rows)} of the {PREFILL_T} rows ({t_pf:.1f} s, "
+                   f"{pf_flops / t_pf / 1e12:.4f} TFLOP/s)"),
         "decode_attn_GBps": nbytes / t_att / 1e9,
+        "prefill_attn_TFLOPs": pf_flops / t_pf / 1e12,
     }
 
 
