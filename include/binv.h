@@ -100,8 +100,9 @@ int binv_rmsnorm(const void* x, int x_dt, int64_t ldx,
  * C  [M, N] row-major, leading dimension ldc, dtype c_dt (BINV_BF16 or BINV_F32)
  * Each C element is accumulated in fp32 by bf16 matrix-core instructions over
  * k in ascending blocks of 32, one accumulator per element, whatever M is.
- * K and N must be multiples of 8; M, N, K <= 2^31 - 1.  M = 0 or N = 0 is a
- * no-op; K = 0 writes zeros.  C must not overlap A or W.
+ * K and N must be multiples of 8; M, N, K <= 2^31 - 1; lda < 2^22 and
+ * ldw < 1.6e7 elements (tiles are addressed with 32-bit offsets).  M = 0 or
+ * N = 0 is a no-op; K = 0 writes zeros.  C must not overlap A or W.
  * ------------------------------------------------------------------------ */
 int binv_gemm_bf16(const void* A, int64_t lda,
                    const void* W, int64_t ldw,

@@ -45,7 +45,9 @@ int check_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, 
         return BINV_ERR_INVALID_ARG;
     if (K % 8 != 0 || N % 8 != 0) return BINV_ERR_UNSUPPORTED;
     if (M > I32MAX || N > I32MAX || K > I32MAX) return BINV_ERR_UNSUPPORTED;
-    if ((M + 127) / 128 > 65535) return BINV_ERR_UNSUPPORTED;
+    // tiles are addressed with 32-bit buffer offsets: 256 rows of A, 64 rows of W
+    if (lda >= 4194304 || ldw >= 16000000) return BINV_ERR_UNSUPPORTED;
+    if (((M + 127) / 128) * ((N + 127) / 128) > I32MAX) return BINV_ERR_UNSUPPORTED;
     return BINV_OK;
 }
 

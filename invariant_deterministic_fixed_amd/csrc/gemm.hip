@@ -9,17 +9,30 @@
 //
 // Per output element the arithmetic is one fp32 accumulator updated by
 // v_mfma_f32_16x16x32_bf16 over k-blocks [0,32), [32,64), ... in ascending
-// order.  Nothing in that chain depends on M: not the tile (BM, BN, BK are
-// constants), not the K loop, not the row's position in its tile.
+// order.  Nothing in that chain depends on M: not the tile (a constant), not
+// the K loop, not the row's position in its tile (a row's slot only decides
+// which lane carries it).  In fact no tile parameter enters the chain at all,
+// so the comparator below, which uses another tile, produces the same bits
+// whenever it does not split K.
 //
-// Tile: BM x BN x BK = 128 x 128 x 64, 256 lanes = 4 waves in a 2 x 2 grid,
-// each wave owning a 64 x 64 block = 4 x 4 MFMA tiles.
-// LDS: A tile [128][64] and the W tile stored transposed, [n][k] (128 x 64),
-// so both MFMA operands are read as 16-byte k-runs.  Rows are 128 bytes; the
-// eight 16-byte chunks of row r are XOR-swizzled by (r ^ r>>3) & 7, which keeps
-// both the 16-row fragment reads and the transposed W writes free of bank
-// conflicts.  W [K, N] is row-major in HBM, so each lane loads a 4 (k) x 8 (n)
-// block with 16-byte loads and transposes it in registers on its way to LDS.
+// Invariant kernel: tile 256 x 256 x 64, 512 lanes = 8 waves in a 2 x 4 grid,
+// each wave owning 128 x 64 outputs (8 x 4 MFMA tiles, 128 fp32 accumulators
+// per lane).  A and W travel HBM -> LDS by buffer_load ... lds (16 bytes per
+// lane, no registers, out-of-range lanes read zero, which handles ragged M, N
+// and K) into two LDS stages of 64 KB; the next K-tile streams in while the
+// current one feeds the matrix cores.
+//   * A tile [256][64]: rows of 128 bytes, 16-byte chunk c of row r stored at
+//     c ^ ((r ^ r>>3) & 7); A fragments are ds_read_b128 (conflict free).
+//   * W tile [64][256] stays k-major as in HBM; chunk c of row k stored at
+//     c ^ 2((k & 3) + 4((k >> 3) & 1)).  A B fragment (8 consecutive k of one
+//     column) is two ds_read_b64_tr_b16: in each 16-lane group, lane i of the
+//     result takes element i%4 of the 8-byte reads of lanes i/4 + 4t, t=0..3,
+//     so when lane 4t+q of the group reads row k+t, columns 4q..4q+3, lane
+//     p ends up holding rows k..k+3 of column p.  The swizzle spreads the 16
+//     rows a wave reads over all 64 banks, two lanes per bank.
+//   * Workgroup ids are dispatched round-robin over the 8 XCDs; each XCD is
+//     given a contiguous range of tiles in groups of 8 tile-rows, so tiles
+//     running together on one XCD share A and W panels in its L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,144 +40,185 @@ namespace binv {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-// byte offset of 16-byte chunk c (0..7) of row r in a [rows][64] bf16 tile
-__device__ __forceinline__ int lds_off(int r, int c) { return (r << 7) + ((c ^ swz(r)) << 4); }
+constexpr int BK = 64;
+constexpr unsigned RSRC_WORD3 = 0x00020000u;   // raw buffer: 32-bit data format, no swizzle
+constexpr int OOB = 0x7ffffff0;                // offset past any num_records: reads zero
 
-struct TileRegs {
-    u32x4 a[4];   // 4 A chunks: rows (t>>3) + 32u, chunk t&7
-    u32x4 w[4];   // 4 W rows k = 4*(t>>4) + i, 8 columns starting at 8*(t&15)
+__device__ __forceinline__ int swz_a(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz_w(int k) { return 2 * ((k & 3) + 4 * ((k >> 3) & 1)); }
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// linear workgroup id -> output tile; contiguous tile ranges per XCD, then
+// groups of GROUP_M tile-rows walked column by column
+template <int GROUP_M>
+__device__ __forceinline__ void tile_of(int i, int Mt, int Nt, int& tm, int& tn) {
+    const int T = Mt * Nt;
+    const int q = T / 8, r = T % 8;
+    const int x = i % 8, local = i / 8;
+    const int t = (x < r) ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
+    const int per_group = GROUP_M * Nt;
+    const int first_m = (t / per_group) * GROUP_M;
+    const int gsz = min(Mt - first_m, GROUP_M);
+    tm = first_m + (t % per_group) % gsz;
+    tn = (t % per_group) / gsz;
+}
+
+template <int BM, int BN, int WGM, int WGN, int GROUP_M>
+struct Tile {
+    static constexpr int BM_ = BM, BN_ = BN;
+    static constexpr int NW = WGM * WGN, NT = 64 * NW;
+    static constexpr int TM = BM / WGM, TN = BN / WGN, FM = TM / 16, FN = TN / 16;
+    static constexpr int A_BYTES = BM * BK * 2, W_BYTES = BK * BN * 2, STAGE = A_BYTES + W_BYTES;
+    static constexpr int A_PW = A_BYTES / 1024 / NW, W_PW = W_BYTES / 1024 / NW;
+    static constexpr int WROWS = 1024 / (BN * 2);        // W rows per 1 KB DMA instruction
+    static_assert(A_PW * NW * 1024 == A_BYTES && W_PW * NW * 1024 == W_BYTES, "");
+    static_assert(BN >= 128 && BN <= 512, "");
+
+    // DMA of K-tile kt into LDS stage `st`
+    __device__ static void issue(char* smem, int st, int kt, const bf16_t* A, int64_t lda,
+                                 const bf16_t* W, int64_t ldw, int m0, int n0, int M, int N, int K,
+                                 int wave, int lane) {
+        char* As = smem + st * STAGE;
+        char* Ws = As + A_BYTES;
+        const int k0 = kt * BK;
+        {
+            const int rows = min(BM, M - m0);
+            __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(A + (int64_t)m0 * lda), (short)0, (int)((int64_t)rows * lda * 2), RSRC_WORD3);
+#pragma unroll
+            for (int u = 0; u < A_PW; ++u) {
+                const int j = wave * A_PW + u;                  // 1 KB block = 8 rows
+                const int row = 8 * j + (lane >> 3);
+                const int c = (lane & 7) ^ swz_a(row);
+                const int kk = k0 + 8 * c;
+                const int off = (row < rows && kk < K) ? (row * (int)lda + kk) * 2 : OOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(As + j * 1024), 16, off, 0, 0, 0);
+            }
+        }
+        {
+            const int krows = min(BK, K - k0);
+            __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(W + (int64_t)k0 * ldw + n0), (short)0, (int)((int64_t)krows * ldw * 2),
+                RSRC_WORD3);
+#pragma unroll
+            for (int u = 0; u < W_PW; ++u) {
+                const int j = wave * W_PW + u;
+                const int row = WROWS * j + lane / (BN / 8);
+                const int c = (lane % (BN / 8)) ^ swz_w(row);
+                const int off = (row < krows && n0 + 8 * c < N) ? (row * (int)ldw + 8 * c) * 2 : OOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Ws + j * 1024), 16, off, 0, 0, 0);
+            }
+        }
+    }
+
+    __device__ static void compute(const char* As, const char* Ws, f32x4 (&acc)[FM][FN], int wm,
+                                   int wn, int lane) {
+        const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            u32x4 b[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int c = (wn * TN + 16 * j + 4 * (r & 3)) >> 3;
+                const int k_lo = 32 * ks + 8 * g + (r >> 2), k_hi = k_lo + 4;
+                const v4i16 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16*)(Ws + k_lo * BN * 2 + ((c ^ swz_w(k_lo)) << 4) + 8 * (r & 1)));
+                const v4i16 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16*)(Ws + k_hi * BN * 2 + ((c ^ swz_w(k_hi)) << 4) + 8 * (r & 1)));
+                const u32x2 p0 = __builtin_bit_cast(u32x2, h0), p1 = __builtin_bit_cast(u32x2, h1);
+                b[j] = u32x4{p0[0], p0[1], p1[0], p1[1]};
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = wm * TM + 16 * i + r;
+                const u32x4 a = *reinterpret_cast<const u32x4*>(
+                    As + (row << 7) + (((4 * ks + g) ^ swz_a(row)) << 4));
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(a, b[j], acc[i][j]);
+            }
+        }
+    }
+
+    // K-tiles [kt_begin, kt_end) of tile blockIdx.x; fp32 partials of split z
+    // go to C + z * split_stride (comparator only).
+    __device__ static void run(const bf16_t* __restrict__ A, int64_t lda,
+                               const bf16_t* __restrict__ W, int64_t ldw, void* __restrict__ C,
+                               int64_t ldc, int64_t split_stride, int M, int N, int K,
+                               int kt_per_split, int c_f32, char* smem) {
+        const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+        const int wm = wave / WGN, wn = wave % WGN;
+        int tm, tn;
+        tile_of<GROUP_M>(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int nk = (K + BK - 1) / BK;
+        const int kt_begin = blockIdx.z * kt_per_split;
+        const int kt_end = min(nk, kt_begin + kt_per_split);
+
+        f32x4 acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        if (kt_begin < kt_end) issue(smem, 0, kt_begin, A, lda, W, ldw, m0, n0, M, N, K, wave, lane);
+        for (int kt = kt_begin; kt < kt_end; ++kt) {
+            const int st = (kt - kt_begin) & 1;
+            wait_vm0();                          // this wave's part of stage kt has landed
+            __builtin_amdgcn_s_barrier();        // ... and every wave's; stage kt-1 is free
+            if (kt + 1 < kt_end) issue(smem, st ^ 1, kt + 1, A, lda, W, ldw, m0, n0, M, N, K, wave, lane);
+            const char* As = smem + st * STAGE;
+            compute(As, As + A_BYTES, acc, wm, wn, lane);
+        }
+
+        const int col_base = n0 + wn * TN + (lane & 15);
+        const int row_base = m0 + wm * TM + 4 * (lane >> 4);
+        if (c_f32) {
+            float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.z * split_stride;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int col = col_base + 16 * j;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = row_base + 16 * i + e;
+                        if (row < M && col < N) Cf[(int64_t)row * ldc + col] = acc[i][j][e];
+                    }
+                }
+        } else {
+            bf16_t* Cb = reinterpret_cast<bf16_t*>(C);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int col = col_base + 16 * j;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = row_base + 16 * i + e;
+                        if (row < M && col < N)
+                            Cb[(int64_t)row * ldc + col] = (bf16_t)f32_to_bf16(acc[i][j][e]);
+                    }
+                }
+        }
+    }
 };
 
-__device__ __forceinline__ void load_tile(TileRegs& r, const bf16_t* __restrict__ A, int64_t lda,
-                                          const bf16_t* __restrict__ W, int64_t ldw, int m0,
-                                          int n0, int k0, int M, int N, int K, int t) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const int ac = t & 7;
-    const int ka = k0 + 8 * ac;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int row = m0 + (t >> 3) + 32 * u;
-        r.a[u] = (row < M && ka < K)
-                     ? *reinterpret_cast<const u32x4*>(A + (int64_t)row * lda + ka)
-                     : zero;
-    }
-    const int n = n0 + 8 * (t & 15);
-    const int kw = k0 + 4 * (t >> 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int k = kw + i;
-        r.w[i] = (k < K && n < N) ? *reinterpret_cast<const u32x4*>(W + (int64_t)k * ldw + n)
-                                  : zero;
-    }
-}
+using InvariantTile = Tile<256, 256, 2, 4, 8>;   // the one configuration of binv_gemm_bf16
+using TunedTile = Tile<128, 128, 2, 2, 8>;       // comparator's tile
 
-__device__ __forceinline__ void store_tile(const TileRegs& r, char* As, char* Ws, int t) {
-    const int ac = t & 7;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-        *reinterpret_cast<u32x4*>(As + lds_off((t >> 3) + 32 * u, ac)) = r.a[u];
-    // transpose the 4 (k) x 8 (n) block: for column n, the 4 k values form 8 bytes
-    const int ng = t & 15, kg = t >> 4;
-    const int half = (kg & 1) * 8;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        u32x2 ev, od;
-        ev[0] = (r.w[0][w] & 0xffffu) | (r.w[1][w] << 16);
-        ev[1] = (r.w[2][w] & 0xffffu) | (r.w[3][w] << 16);
-        od[0] = (r.w[0][w] >> 16) | (r.w[1][w] & 0xffff0000u);
-        od[1] = (r.w[2][w] >> 16) | (r.w[3][w] & 0xffff0000u);
-        const int nrow = 8 * ng + 2 * w;
-        *reinterpret_cast<u32x2*>(Ws + lds_off(nrow, kg >> 1) + half) = ev;
-        *reinterpret_cast<u32x2*>(Ws + lds_off(nrow + 1, kg >> 1) + half) = od;
-    }
-}
-
-// blockIdx.z selects a K range [kt_begin, kt_end) of BK-tiles; the invariant
-// entry point always launches gridDim.z = 1 with the whole K.  With
-// gridDim.z > 1 (the comparator only) each split writes fp32 partials to
-// C + z * split_stride.
-__global__ __launch_bounds__(NT) void gemm_bf16_kernel(const bf16_t* __restrict__ A, int64_t lda,
-                                                       const bf16_t* __restrict__ W, int64_t ldw,
-                                                       void* __restrict__ C, int64_t ldc,
-                                                       int64_t split_stride, int M, int N, int K,
-                                                       int kt_per_split, int c_f32) {
-    __shared__ __attribute__((aligned(16))) char smem[(BM + BN) * BK * 2];
-    char* As = smem;
-    char* Ws = smem + BM * BK * 2;
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = blockIdx.x * BN;
-    const int m0 = blockIdx.y * BM;
-    const int nk_total = (K + BK - 1) / BK;
-    const int kt_begin = blockIdx.z * kt_per_split;
-    int kt_end = kt_begin + kt_per_split;
-    if (kt_end > nk_total) kt_end = nk_total;
-
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    TileRegs regs;
-    if (kt_begin < kt_end) load_tile(regs, A, lda, W, ldw, m0, n0, kt_begin * BK, M, N, K, t);
-    const int lrow = lane & 15, lchunk = lane >> 4;
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        store_tile(regs, As, Ws, t);
-        __syncthreads();
-        if (kt + 1 < kt_end) load_tile(regs, A, lda, W, ldw, m0, n0, (kt + 1) * BK, M, N, K, t);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            u32x4 a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const u32x4*>(As + lds_off(wm * 64 + 16 * i + lrow, 4 * ks + lchunk));
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const u32x4*>(Ws + lds_off(wn * 64 + 16 * j + lrow, 4 * ks + lchunk));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
-        }
-        __syncthreads();
-    }
-
-    // epilogue: lane holds rows 4*(lane>>4)+e of each 16x16 tile, column lane&15
-    const int col_base = n0 + wn * 64 + (lane & 15);
-    const int row_base = m0 + wm * 64 + 4 * (lane >> 4);
-    if (c_f32) {
-        float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.z * split_stride;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = col_base + 16 * j;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = row_base + 16 * i + e;
-                    if (row < M && col < N) Cf[(int64_t)row * ldc + col] = acc[i][j][e];
-                }
-            }
-    } else {
-        bf16_t* Cb = reinterpret_cast<bf16_t*>(C);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = col_base + 16 * j;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = row_base + 16 * i + e;
-                    if (row < M && col < N)
-                        Cb[(int64_t)row * ldc + col] = (bf16_t)f32_to_bf16(acc[i][j][e]);
-                }
-            }
-    }
+template <class T>
+__global__ __launch_bounds__(T::NT) void gemm_tile_kernel(const bf16_t* __restrict__ A, int64_t lda,
+                                                          const bf16_t* __restrict__ W, int64_t ldw,
+                                                          void* __restrict__ C, int64_t ldc,
+                                                          int64_t split_stride, int M, int N, int K,
+                                                          int kt_per_split, int c_f32) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+    T::run(A, lda, W, ldw, C, ldc, split_stride, M, N, K, kt_per_split, c_f32, smem);
 }
 
 // comparator only: out[i, j] = sum over splits s = 0..S-1 (ascending) of part[s][i, j]
@@ -183,23 +237,31 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         reinterpret_cast<bf16_t*>(C)[row * ldc + col] = (bf16_t)f32_to_bf16(s);
 }
 
+template <class T>
+hipError_t launch_tile(const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
+                       int64_t ldc, int64_t split_stride, int M, int N, int K, int S, int per,
+                       int c_f32, hipStream_t s) {
+    const int tiles = ((M + T::BM_ - 1) / T::BM_) * ((N + T::BN_ - 1) / T::BN_);
+    dim3 grid((unsigned)tiles, 1, (unsigned)S), block(T::NT);
+    hipLaunchKernelGGL((gemm_tile_kernel<T>), grid, block, 0, s, (const bf16_t*)A, lda,
+                       (const bf16_t*)W, ldw, C, ldc, split_stride, M, N, K, per, c_f32);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
                        int c_f32, int64_t ldc, int M, int N, int K, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     const int nk = (K + BK - 1) / BK;
-    dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, 1), block(NT);
-    hipLaunchKernelGGL(gemm_bf16_kernel, grid, block, 0, s, (const bf16_t*)A, lda,
-                       (const bf16_t*)W, ldw, C, ldc, (int64_t)0, M, N, K, nk > 0 ? nk : 1,
-                       c_f32);
-    return hipGetLastError();
+    return launch_tile<InvariantTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
+                                      c_f32, s);
 }
 
 // Comparator: split-K whose split count is chosen from the number of output
 // tiles, i.e. from M -- the strategy the invariant kernel refuses.
 static int tuned_splits(int64_t M, int64_t N, int64_t K) {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     const int64_t nk = (K + BK - 1) / BK;
     int64_t S = (512 + tiles - 1) / tiles;
     if (S > 16) S = 16;
@@ -218,14 +280,14 @@ hipError_t launch_gemm_tuned(const void* A, int64_t lda, const void* W, int64_t 
                              hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     const int S = tuned_splits(M, N, K);
-    if (S == 1) return launch_gemm(A, lda, W, ldw, C, c_f32, ldc, M, N, K, s);
     const int nk = (K + BK - 1) / BK;
+    if (S == 1)
+        return launch_tile<TunedTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
+                                      c_f32, s);
     const int per = (nk + S - 1) / S;
     const int Sused = (nk + per - 1) / per;
-    dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, Sused), block(NT);
-    hipLaunchKernelGGL(gemm_bf16_kernel, grid, block, 0, s, (const bf16_t*)A, lda,
-                       (const bf16_t*)W, ldw, ws, (int64_t)N, (int64_t)M * N, M, N, K, per, 1);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_tile<TunedTile>(A, lda, W, ldw, ws, N, (int64_t)M * N, M, N, K, Sused,
+                                          per, 1, s);
     if (e != hipSuccess) return e;
     const int64_t MN = (int64_t)M * N;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s,
