@@ -1,0 +1,283 @@
+// attn_chunk.hpp -- per-chunk attention arithmetic shared by the invariant
+// decode / prefill kernels (attention.hip) and the shape-tuned comparator
+// (attention_tuned.hip).  Sharing it is what makes a row's partial for a
+// chunk the same bits on every path.
+#pragma once
+#include "common.hpp"
+
+namespace binv {
+namespace attn {
+
+
+constexpr int CHUNK = 256;
+constexpr int PAGE = 16;
+constexpr int NT = 256;
+constexpr int ROWS = 16;
+constexpr int STACK = 10;          // binary counter slots: enough for 1023 leaves
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// P tile in LDS: [16 rows][256 keys] bf16, rows of 512 bytes = 32 chunks of 16
+// bytes; chunk ch of row r is stored at position ch ^ r.
+__device__ __forceinline__ int p_off(int r, int ch) { return (r << 9) + ((ch ^ r) << 4); }
+
+struct RowInfo {
+    int64_t token;   // global query-token index (row of q / out / partials), -1 if padding
+    int head;        // query head
+    int pos;         // absolute position of the query
+};
+
+// Row slot r of tile `qt` of sequence b:  token (r / G) of the tile, head g*G + r % G.
+template <int G>
+__device__ __forceinline__ RowInfo row_info(int r, int b, int g, int qt, int q_len,
+                                            int64_t q_start, int kv_len) {
+    constexpr int TQ = ROWS / G;
+    RowInfo ri;
+    const int tq = r / G;
+    const int i = qt * TQ + tq;                    // index among the sequence's new tokens
+    ri.head = g * G + (r % G);
+    if (tq < TQ && i < q_len) {
+        ri.token = q_start + i;
+        ri.pos = kv_len - q_len + i;
+        if (ri.pos < 0) ri.token = -1;
+    } else {
+        ri.token = -1;
+        ri.pos = -1;
+    }
+    return ri;
+}
+
+// NW = D/16 waves: for q.k each wave owns 16/NW pages (16 keys each) of the
+// chunk; for p.v each wave owns one 16-wide feature tile over all 256 keys.
+template <int D>
+struct ChunkShape {
+    static constexpr int NW = D / 16;            // 8 waves at D = 128, 4 at D = 64
+    static constexpr int NTH = 64 * NW;
+    static constexpr int JT = 16 / NW;           // pages of the chunk per wave (q.k)
+    static constexpr int KS = D / 32;            // k-steps of the q.k product
+};
+
+// Everything a workgroup knows about its (sequence, KV head, query tile).
+struct TileCtx {
+    int b, g, qt;
+    int kv_len, q_len;
+    int64_t q_start;
+    int pos_max;         // highest query position in the tile (-1: empty tile)
+    int64_t pt_row;
+    int n_pages;
+};
+
+template <int G>
+__device__ __forceinline__ TileCtx tile_ctx(int b, int g, int qt, const int32_t* cu_q,
+                                            const int32_t* kv_lens, int64_t pt_stride,
+                                            int max_kv_len) {
+    constexpr int TQ = ROWS / G;
+    TileCtx x;
+    x.b = b; x.g = g; x.qt = qt;
+    x.kv_len = min(kv_lens[b], max_kv_len);
+    if (cu_q) {
+        x.q_start = cu_q[b];
+        x.q_len = cu_q[b + 1] - cu_q[b];
+    } else {
+        x.q_start = b;
+        x.q_len = 1;
+    }
+    if (x.q_len > x.kv_len) x.q_len = x.kv_len;
+    const int last_i = min(x.q_len, (qt + 1) * TQ) - 1;
+    x.pos_max = (last_i < qt * TQ) ? -1 : x.kv_len - x.q_len + last_i;
+    x.pt_row = (int64_t)b * pt_stride;
+    x.n_pages = (x.kv_len + PAGE - 1) / PAGE;
+    return x;
+}
+
+template <int D>
+struct ChunkLds {
+    __attribute__((aligned(16))) char p[ROWS * CHUNK * 2];
+    float red_max[ChunkShape<D>::NW][ROWS];
+    int row_pos[ROWS];
+};
+
+// Result of one chunk for the workgroup's 16 rows:
+//   m[e]  max of row 4*(lane>>4)+e (every lane), -inf if the row sees no key
+//   o     p.v of those rows for features 16*wave + (lane&15)
+//   l     (threads t < 256 with t % 16 == 0) sum of p of row t >> 4, and
+//   ml_m  that row's max
+struct ChunkOut {
+    float m[4];
+    f32x4 o;
+    float l, ml_m;
+};
+
+// The per-chunk arithmetic shared by decode, prefill and the comparator: keys
+// [256c, 256c+256) of the tile's sequence, each row limited to keys <= its
+// position.  Ends with LDS free for reuse only after a __syncthreads().
+template <int D, int G>
+__device__ __forceinline__ ChunkOut chunk_compute(
+    const TileCtx& x, int c, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
+    const bf16_t* __restrict__ vc, const int32_t* __restrict__ page_table, int64_t pt_stride,
+    int Hq, int Hkv, float scale_log2, ChunkLds<D>& sh) {
+    using S = ChunkShape<D>;
+    constexpr int NW = S::NW, JT = S::JT, KS = S::KS;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int ar = lane & 15, ag = lane >> 4;
+    const int j0 = c * CHUNK;
+    const int g = x.g;
+    const int kv_len = x.kv_len;
+
+    // ---- K fragments (B operand of q.k): page 16c + JT*wave + u, key slot lane&15,
+    // features 32ks + 8(lane>>4) .. +8
+    u32x4 kf[JT][KS];
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
+        const int pidx = 16 * c + JT * wave + u;
+        const bool ok = pidx < x.n_pages && pidx < pt_stride;
+        const int64_t phys = ok ? (int64_t)page_table[x.pt_row + pidx] : 0;
+        const bf16_t* kp = kc + ((phys * Hkv + g) * PAGE + (lane & 15)) * D + 8 * ag;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[u][ks] = ok ? ld16(kp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // ---- Q fragments (A operand): row lane&15, features 32ks + 8(lane>>4) .. +8
+    const RowInfo a_row = row_info<G>(ar, x.b, g, x.qt, x.q_len, x.q_start, kv_len);
+    u32x4 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = u32x4{0u, 0u, 0u, 0u};
+        if (a_row.token >= 0)
+            qf[ks] = ld16(q + (a_row.token * Hq + a_row.head) * D + 32 * ks + 8 * ag);
+    }
+    if (t < ROWS) sh.row_pos[t] = row_info<G>(t, x.b, g, x.qt, x.q_len, x.q_start, kv_len).pos;
+
+    // ---- S = Q K^T on the matrix cores
+    f32x4 s[JT];
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
+        s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s[u] = mfma16x16x32(qf[ks], kf[u][ks], s[u]);
+    }
+
+    // ---- V fragments (B operand of p.v), issued once the q.k products are queued:
+    // feature d = 16 wave + (lane&15), keys 32ks + 8(lane>>4) .. +8, i.e.
+    // page 16c + 2ks + (ag>>1), slots 8(ag&1) .. +8; slots >= kv_len read as 0
+    u32x4 vf[8];
+    {
+        const int d = 16 * wave + (lane & 15);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int pidx = 16 * c + 2 * ks + (ag >> 1);
+            const bool ok = pidx < x.n_pages && pidx < pt_stride;
+            const int64_t phys = ok ? (int64_t)page_table[x.pt_row + pidx] : 0;
+            const int nvalid = kv_len - (pidx * PAGE + 8 * (ag & 1));
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (ok) v = ld16(vc + ((phys * Hkv + g) * D + d) * PAGE + 8 * (ag & 1));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (2 * i + 1 >= nvalid) v[i] &= (2 * i < nvalid) ? 0x0000ffffu : 0u;
+            }
+            vf[ks] = v;
+        }
+    }
+    __syncthreads();   // row_pos visible
+
+    // lane holds rows 4*(lane>>4)+e, key j0 + 16*(JT*wave + u) + (lane&15)
+    const int key_lane = j0 + 16 * JT * wave + (lane & 15);
+    ChunkOut r;
+    int rpos[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rpos[e] = sh.row_pos[4 * ag + e];
+    float mx[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        mx[e] = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < JT; ++u) {
+            const bool valid = key_lane + 16 * u <= rpos[e];
+            const float v = valid ? s[u][e] * scale_log2 : -INFINITY;
+            s[u][e] = v;
+            mx[e] = fmaxf(mx[e], v);
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], off));
+    }
+    if ((lane & 15) == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sh.red_max[wave][4 * ag + e] = mx[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int row = 4 * ag + e;
+        float mm = sh.red_max[0][row];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) mm = fmaxf(mm, sh.red_max[w][row]);
+        r.m[e] = mm;
+    }
+
+    // ---- P = bf16(exp2(s - m)) into LDS
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
+        const int key = 16 * (JT * wave + u) + (lane & 15);       // key within the chunk
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = s[u][e];
+            const float p = (v == -INFINITY) ? 0.0f : exp2f(v - r.m[e]);
+            const int row = 4 * ag + e;
+            *reinterpret_cast<bf16_t*>(sh.p + p_off(row, key >> 3) + 2 * (key & 7)) =
+                (bf16_t)f32_to_bf16(p);
+        }
+    }
+    __syncthreads();
+
+    // ---- l (threads 0..255): thread t sums keys 16(t&15) .. +15 of row t>>4 in
+    // key order, then a 4-level xor butterfly over the 16 segment sums of the row
+    r.l = 0.0f;
+    r.ml_m = -INFINITY;
+    if (t < 256) {
+        const int row = t >> 4, seg = t & 15;
+        const u32x4 p0 = *reinterpret_cast<const u32x4*>(sh.p + p_off(row, 2 * seg));
+        const u32x4 p1 = *reinterpret_cast<const u32x4*>(sh.p + p_off(row, 2 * seg + 1));
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { acc += lo_bf16(p0[i]); acc += hi_bf16(p0[i]); }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { acc += lo_bf16(p1[i]); acc += hi_bf16(p1[i]); }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
+        r.l = acc;
+        float mm = sh.red_max[0][row];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) mm = fmaxf(mm, sh.red_max[w][row]);
+        r.ml_m = mm;
+    }
+
+    // ---- O = P V on the matrix cores, keys ascending; wave owns features 16 wave ..
+    r.o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 pa = *reinterpret_cast<const u32x4*>(sh.p + p_off(ar, 4 * ks + ag));
+        r.o = mfma16x16x32(pa, vf[ks], r.o);
+    }
+    return r;
+}
+
+struct Partial {
+    float m, l;
+    float o[2];
+};
+
+// left-to-right combine of two partials (m in the log2 domain)
+template <int NO>
+__device__ __forceinline__ Partial combine(const Partial& a, const Partial& b) {
+    Partial r;
+    r.m = fmaxf(a.m, b.m);
+    const float fa = exp2f(a.m - r.m);
+    const float fb = exp2f(b.m - r.m);
+    r.l = fmaf(fa, a.l, fb * b.l);
+#pragma unroll
+    for (int i = 0; i < NO; ++i) r.o[i] = fmaf(fa, a.o[i], fb * b.o[i]);
+    return r;
+}
+
+}  // namespace attn
+}  // namespace binv

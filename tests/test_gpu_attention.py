@@ -213,3 +213,32 @@ def test_mha_tiny_head_dim_64_prefill_and_decode():
     assert_bitwise_equal(dec, pf, "decode vs prefill, D=64")
     ref = oracle.attention(f64(q), list(range(L)), f64(k), f64(v), 0.125)
     assert row_rel_err(f64(pf), ref).max() <= TOL_BF16
+
+
+def test_tuned_decode_parity_and_positive_control():
+    # the shape-tuned comparator must be right (oracle) and must NOT be
+    # invariant: a long target's bits change with the batch size
+    Hq, Hkv, D = 32, 8, 128
+    scale = 1 / math.sqrt(D)
+    L_t = 20000
+    tk, tv = synth.random_kv(L_t, Hkv, D, synth.TARGET_SEED, DEV)
+    tq = synth.normal((1, Hq, D), 1.0, synth.TARGET_SEED + 1, DEV)
+    cache, _ = make_cache([L_t], Hkv, D, 1, seqs=[(tk, tv)])
+    alone = decode(cache, tq, scale, tuned=True)
+    ref = oracle_decode(tq, [(tk, tv)], [L_t], scale)
+    assert row_rel_err(f64(alone), ref).max() <= TOL_BF16
+    lens = synth.log_uniform_lengths(255, 128, 4096, 77)
+    seqs = [synth.random_kv(int(L), Hkv, D, 500 + i, DEV) for i, L in enumerate(lens)] + [(tk, tv)]
+    cache, _ = make_cache([int(k.shape[0]) for k, _ in seqs], Hkv, D, 3, seqs=seqs)
+    q = synth.normal((256, Hq, D), 1.0, 9, DEV)
+    q[255] = tq[0]
+    out = decode(cache, q, scale, max_kv_len=L_t, tuned=True)
+    inv = decode(cache, q, scale, max_kv_len=L_t)
+    for b in [0, 100, 255]:
+        k, v = seqs[b]
+        r = oracle_decode(q[b:b + 1], [(k, v)], [int(k.shape[0])], scale)
+        assert row_rel_err(f64(out[b:b + 1]), r).max() <= TOL_BF16
+    assert not torch.equal(out[255:].view(torch.int16), alone.view(torch.int16)), \
+        "tuned decode gave identical bits for B=1 and B=256: the probe is not sensitive"
+    inv_alone = decode(make_cache([L_t], Hkv, D, 1, seqs=[(tk, tv)])[0], tq, scale)
+    assert_bitwise_equal(inv[255:], inv_alone, "invariant decode, same probe")
