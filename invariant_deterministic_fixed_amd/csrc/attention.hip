@@ -51,6 +51,8 @@ namespace binv {
 namespace {
 using namespace attn;
 
+// Grid: x = (query tile, KV head), y = chunk, z = sequence; workgroups of
+// chunks past a tile's last position exit at once.
 template <int D, int G>
 __global__ __launch_bounds__(ChunkShape<D>::NTH, 4) void attn_chunk_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
@@ -60,11 +62,14 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, 4) void attn_chunk_kernel(
     float2* __restrict__ ws_ml, int Hq, int Hkv, int n_chunks, int max_kv_len,
     float scale_log2) {
     __shared__ ChunkLds<D> sh;
+    constexpr int JT = ChunkShape<D>::JT;
     const int c = blockIdx.y;
     const TileCtx x = tile_ctx<G>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q, kv_lens,
                                   pt_stride, max_kv_len);
     if (x.pos_max < c * CHUNK) return;     // no row of the tile reaches this chunk
-    const ChunkOut r = chunk_compute<D, G>(x, c, q, kc, vc, page_table, pt_stride, Hq, Hkv,
+    int phys[JT];
+    load_phys<D>(x, c, page_table, pt_stride, phys);
+    const ChunkOut r = chunk_compute<D, G>(x, c, phys, q, kc, vc, pt_stride, Hq, Hkv,
                                            scale_log2, sh);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, ag = lane >> 4;
     const int j0 = c * CHUNK;

@@ -58,7 +58,9 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, 4) void attn_split_kernel(
     float L = 0.0f, MR = -INFINITY;
     for (int c = c0; c < c1; ++c) {
         __syncthreads();                           // LDS of the previous chunk is free
-        const ChunkOut r = chunk_compute<D, G>(x, c, q, kc, vc, page_table, pt_stride, Hq, Hkv,
+        int phys[ChunkShape<D>::JT];
+        load_phys<D>(x, c, page_table, pt_stride, phys);
+        const ChunkOut r = chunk_compute<D, G>(x, c, phys, q, kc, vc, pt_stride, Hq, Hkv,
                                                scale_log2, sh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

@@ -92,6 +92,9 @@ __device__ __forceinline__ TileCtx tile_ctx(int b, int g, int qt, const int32_t*
 
 template <int D>
 struct ChunkLds {
+    // the chunk's 16 V page blocks of this KV head, [page][D][16 slots] bf16,
+    // copied HBM -> LDS by global_load_lds (one 1 KB piece per instruction)
+    __attribute__((aligned(1024))) char v[16 * D * PAGE * 2];
     __attribute__((aligned(16))) char p[ROWS * CHUNK * 2];
     float red_max[ChunkShape<D>::NW][ROWS];
     int row_pos[ROWS];
@@ -110,11 +113,27 @@ struct ChunkOut {
 
 // The per-chunk arithmetic shared by decode, prefill and the comparator: keys
 // [256c, 256c+256) of the tile's sequence, each row limited to keys <= its
-// position.  Ends with LDS free for reuse only after a __syncthreads().
+// position.  LDS may be reused only after a __syncthreads().
+// Page-table entries of the JT pages this wave reads in chunk c (independent
+// of kv_len, so they can be fetched a chunk ahead); 0 past the table's row.
+template <int D>
+__device__ __forceinline__ void load_phys(const TileCtx& x, int c,
+                                          const int32_t* __restrict__ page_table,
+                                          int64_t pt_stride, int (&phys)[ChunkShape<D>::JT]) {
+    constexpr int JT = ChunkShape<D>::JT;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
+        const int pidx = 16 * c + JT * wave + u;
+        phys[u] = (pidx < pt_stride) ? page_table[x.pt_row + pidx] : 0;
+    }
+}
+
 template <int D, int G>
 __device__ __forceinline__ ChunkOut chunk_compute(
-    const TileCtx& x, int c, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
-    const bf16_t* __restrict__ vc, const int32_t* __restrict__ page_table, int64_t pt_stride,
+    const TileCtx& x, int c, const int (&phys_in)[ChunkShape<D>::JT],
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
+    const bf16_t* __restrict__ vc, int64_t pt_stride,
     int Hq, int Hkv, float scale_log2, ChunkLds<D>& sh) {
     using S = ChunkShape<D>;
     constexpr int NW = S::NW, JT = S::JT, KS = S::KS;
@@ -124,17 +143,40 @@ __device__ __forceinline__ ChunkOut chunk_compute(
     const int g = x.g;
     const int kv_len = x.kv_len;
 
+    // ---- this wave's JT pages; entries past the sequence's last page are not used
+    int64_t phys[JT];
+    bool page_ok[JT];
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
+        const int pidx = 16 * c + JT * wave + u;
+        page_ok[u] = pidx < x.n_pages && pidx < pt_stride;
+        phys[u] = page_ok[u] ? (int64_t)phys_in[u] : 0;
+    }
+
+    // ---- V page blocks of the same JT pages -> LDS (4 KB at D = 128, 2 KB at
+    // D = 64, 1 KB per instruction).  Pages past the sequence end copy page 0
+    // of the cache; all their slots are >= kv_len and are zeroed when read.
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
+        const int pl = JT * wave + u;                          // page within the chunk
+        const char* src = reinterpret_cast<const char*>(vc + (phys[u] * Hkv + g) * (D * PAGE));
+#pragma unroll
+        for (int part = 0; part < D * PAGE * 2 / 1024; ++part)
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(src + part * 1024 + 16 * lane),
+                (__attribute__((address_space(3))) void*)(sh.v + pl * (D * PAGE * 2) + part * 1024),
+                16, 0, 0);
+    }
+
     // ---- K fragments (B operand of q.k): page 16c + JT*wave + u, key slot lane&15,
     // features 32ks + 8(lane>>4) .. +8
     u32x4 kf[JT][KS];
 #pragma unroll
     for (int u = 0; u < JT; ++u) {
-        const int pidx = 16 * c + JT * wave + u;
-        const bool ok = pidx < x.n_pages && pidx < pt_stride;
-        const int64_t phys = ok ? (int64_t)page_table[x.pt_row + pidx] : 0;
-        const bf16_t* kp = kc + ((phys * Hkv + g) * PAGE + (lane & 15)) * D + 8 * ag;
+        const bf16_t* kp = kc + ((phys[u] * Hkv + g) * PAGE + (lane & 15)) * D + 8 * ag;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[u][ks] = ok ? ld16(kp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+        for (int ks = 0; ks < KS; ++ks)
+            kf[u][ks] = page_ok[u] ? ld16(kp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
     }
 
     // ---- Q fragments (A operand): row lane&15, features 32ks + 8(lane>>4) .. +8
@@ -156,29 +198,8 @@ __device__ __forceinline__ ChunkOut chunk_compute(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) s[u] = mfma16x16x32(qf[ks], kf[u][ks], s[u]);
     }
-
-    // ---- V fragments (B operand of p.v), issued once the q.k products are queued:
-    // feature d = 16 wave + (lane&15), keys 32ks + 8(lane>>4) .. +8, i.e.
-    // page 16c + 2ks + (ag>>1), slots 8(ag&1) .. +8; slots >= kv_len read as 0
-    u32x4 vf[8];
-    {
-        const int d = 16 * wave + (lane & 15);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int pidx = 16 * c + 2 * ks + (ag >> 1);
-            const bool ok = pidx < x.n_pages && pidx < pt_stride;
-            const int64_t phys = ok ? (int64_t)page_table[x.pt_row + pidx] : 0;
-            const int nvalid = kv_len - (pidx * PAGE + 8 * (ag & 1));
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (ok) v = ld16(vc + ((phys * Hkv + g) * D + d) * PAGE + 8 * (ag & 1));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (2 * i + 1 >= nvalid) v[i] &= (2 * i < nvalid) ? 0x0000ffffu : 0u;
-            }
-            vf[ks] = v;
-        }
-    }
-    __syncthreads();   // row_pos visible
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's V copies have landed
+    __syncthreads();   // row_pos and every wave's V pages visible
 
     // lane holds rows 4*(lane>>4)+e, key j0 + 16*(JT*wave + u) + (lane&15)
     const int key_lane = j0 + 16 * JT * wave + (lane & 15);
@@ -252,11 +273,24 @@ __device__ __forceinline__ ChunkOut chunk_compute(
     }
 
     // ---- O = P V on the matrix cores, keys ascending; wave owns features 16 wave ..
+    // V fragment: feature d = 16 wave + (lane&15), keys 32ks + 8(lane>>4) .. +8,
+    // i.e. page 2ks + (ag>>1) of the chunk, slots 8(ag&1) .. +8; slots at or
+    // past kv_len read as 0
     r.o = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+        const int d = 16 * wave + (lane & 15);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 pa = *reinterpret_cast<const u32x4*>(sh.p + p_off(ar, 4 * ks + ag));
-        r.o = mfma16x16x32(pa, vf[ks], r.o);
+        for (int ks = 0; ks < 8; ++ks) {
+            const int pl = 2 * ks + (ag >> 1);
+            u32x4 v = *reinterpret_cast<const u32x4*>(sh.v + pl * (D * PAGE * 2) + d * (PAGE * 2) + 16 * (ag & 1));
+            const int nvalid = kv_len - ((16 * c + pl) * PAGE + 8 * (ag & 1));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (2 * i + 1 >= nvalid) v[i] &= (2 * i < nvalid) ? 0x0000ffffu : 0u;
+            }
+            const u32x4 pa = *reinterpret_cast<const u32x4*>(sh.p + p_off(ar, 4 * ks + ag));
+            r.o = mfma16x16x32(pa, v, r.o);
+        }
     }
     return r;
 }
