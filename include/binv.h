@@ -207,6 +207,59 @@ int binv_attn_decode_paged_tuned(const void* q,
                                  int64_t B, int64_t max_kv_len, int Hq, int Hkv, int D, int page_size,
                                  float scale, void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Decoder glue: the pointwise and selection steps between the kernels above.
+ * Each output element is computed from its own inputs by a fixed instruction
+ * sequence, so these are batch-invariant as they stand (devpress.csdn.net
+ * explainer, section 3: pointwise operations need no change).  Argmax and
+ * top-k break ties by the lowest index (paper.xwysyy.cn "19.7", section
+ * 19.7.4: near-tied logits are where differences become different tokens).
+ * ------------------------------------------------------------------------ */
+
+/* out[t, :] = table[ids[t], :] widened to fp32.  table bf16 [V, H] row-major,
+ * out fp32 [T, H] (the residual stream).  An id outside [0, V) gives a zero row. */
+int binv_embed(const int32_t* ids, int64_t T, const void* table, int64_t V, int64_t H,
+               float* out, void* stream);
+
+/* Rotary position embedding (rotate-half form, angle p * theta^(-2i/D) for the
+ * pair (i, i + D/2), evaluated in fp64; rotation in fp32, rounded once to bf16)
+ * on the q and k heads of a fused projection row, then the K/V write into the
+ * paged cache.
+ * qkv     bf16 [T, ld_qkv]: per token Hq query heads, Hkv key heads, Hkv value
+ *         heads of D features each, in that order
+ * tok_seq, tok_pos  int32 [T]: sequence (row of page_table) and absolute position
+ * q_out   bf16 [T, Hq, D]: rotated queries
+ * k_cache, v_cache: the paged layout of the attention entry points; token
+ *         (seq, pos) goes to page page_table[seq * pt_stride + pos / 16], slot pos % 16.
+ * Contract: the page-table entries addressed are valid; no two tokens of the
+ * call share (seq, pos). */
+int binv_rope_kv_write(const void* qkv, int64_t ld_qkv, const int32_t* tok_seq,
+                       const int32_t* tok_pos, int64_t T, int Hq, int Hkv, int D, double theta,
+                       void* q_out, void* k_cache, void* v_cache, const int32_t* page_table,
+                       int64_t pt_stride, int page_size, void* stream);
+
+/* SwiGLU: out[t, j] = bf16(silu(g) * u), g = gate_up[t, j], u = gate_up[t, F + j],
+ * silu(g) = g / (1 + exp(-g)), fp32.  gate_up bf16 [T, ld_gu >= 2F], out bf16
+ * [T, ld_out >= F].  T <= 65535. */
+int binv_swiglu(const void* gate_up, int64_t ld_gu, int64_t T, int64_t F, void* out,
+                int64_t ld_out, void* stream);
+
+/* Residual update h[t, j] += x[t, j]: h fp32 [T, ldh], x bf16 [T, ldx].  T <= 65535. */
+int binv_residual_add(float* h, int64_t ldh, const void* x, int64_t ldx, int64_t T, int64_t H,
+                      void* stream);
+
+/* dst[r, :] = src[idx[r], :] for rows of `cols` elements of dtype dt, copied bit
+ * for bit.  Row sizes and pointers 4-byte aligned.  Contract: idx entries valid. */
+int binv_gather_rows(const void* src, int dt, int64_t lds, const int32_t* idx, int64_t R,
+                     void* dst, int64_t ldd, int64_t cols, void* stream);
+
+/* Exact top-K (K <= 32) of each fp32 row of x [R, ldx] over its first n entries:
+ * ids int32 [R, K] and vals fp32 [R, K], sorted by value descending, equal values
+ * by index ascending; NaN is never selected (a row with fewer than K non-NaN
+ * entries is padded with id -1, value -inf).  ids[r, 0] is the greedy argmax. */
+int binv_topk(const float* x, int64_t ldx, int64_t R, int64_t n, int K, int32_t* ids,
+              float* vals, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

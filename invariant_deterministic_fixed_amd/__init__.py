@@ -4,4 +4,5 @@ The kernels are hand-written HIP in ``csrc/`` behind the C ABI of
 ``include/binv.h``; ``binding`` marshals torch tensors into those calls.
 """
 from .binding import (BINV_BF16, BINV_F32, BinvError, attn_decode, attn_prefill,  # noqa: F401
-                      attn_workspace_bytes, gemm, lib, rmsnorm, status_str, version)
+                      attn_workspace_bytes, embed, gather_rows, gemm, lib, residual_add,
+                      rmsnorm, rope_kv_write, status_str, swiglu, topk, version)

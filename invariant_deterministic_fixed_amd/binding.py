@@ -48,6 +48,13 @@ def _declare(lib):
         "binv_attn_decode_tuned_workspace_bytes": (sz, [i64, ci, ci, i64]),
         "binv_attn_decode_paged_tuned": (ci, [vp, vp, vp, vp, i64, vp, vp, i64, i64, ci, ci, ci,
                                               ci, f32, vp, sz, vp]),
+        "binv_embed": (ci, [vp, i64, vp, i64, i64, vp, vp]),
+        "binv_rope_kv_write": (ci, [vp, i64, vp, vp, i64, ci, ci, ci, ctypes.c_double, vp, vp, vp,
+                                    vp, i64, ci, vp]),
+        "binv_swiglu": (ci, [vp, i64, i64, i64, vp, i64, vp]),
+        "binv_residual_add": (ci, [vp, i64, vp, i64, i64, i64, vp]),
+        "binv_gather_rows": (ci, [vp, ci, i64, vp, i64, vp, i64, i64, vp]),
+        "binv_topk": (ci, [vp, i64, i64, i64, ci, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -201,3 +208,81 @@ def attn_prefill(q, cu_q, k_cache, v_cache, page_table, kv_lens, max_q_len, max_
                                        D, page, float(scale), _ptr(ws), nbytes, _stream(q))
     _check(st, "binv_attn_prefill_paged")
     return out
+
+
+# ---------------------------------------------------------------- decoder glue
+def embed(ids, table, out=None):
+    """out fp32 [T, H] = table[ids] (bf16 table [V, H])."""
+    _dev(ids, table, out)
+    T = ids.shape[0]
+    V, H = table.shape
+    assert ids.dtype == torch.int32 and table.dtype == torch.bfloat16 and table.is_contiguous()
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=table.device)
+    assert out.is_contiguous()
+    _check(lib().binv_embed(_ptr(ids), T, _ptr(table), V, H, _ptr(out), _stream(table)),
+           "binv_embed")
+    return out
+
+
+def rope_kv_write(qkv, tok_seq, tok_pos, Hq, Hkv, D, theta, k_cache, v_cache, page_table,
+                  q_out=None):
+    """RoPE on the q/k heads of qkv [T, >= (Hq + 2 Hkv) D], rotated q -> q_out [T, Hq, D],
+    k and v -> the paged caches at (tok_seq, tok_pos)."""
+    _dev(qkv, tok_seq, tok_pos, k_cache, v_cache, page_table, q_out)
+    T, ld = _rows(qkv)
+    if q_out is None:
+        q_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=qkv.device)
+    st = lib().binv_rope_kv_write(_ptr(qkv), ld, _ptr(tok_seq), _ptr(tok_pos), T, Hq, Hkv, D,
+                                  float(theta), _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(page_table), page_table.stride(0), k_cache.shape[2],
+                                  _stream(qkv))
+    _check(st, "binv_rope_kv_write")
+    return q_out
+
+
+def swiglu(gate_up, out=None):
+    """out [T, F] = silu(gate_up[:, :F]) * gate_up[:, F:]."""
+    _dev(gate_up, out)
+    T, ld = _rows(gate_up)
+    F = gate_up.shape[1] // 2
+    if out is None:
+        out = torch.empty((T, F), dtype=torch.bfloat16, device=gate_up.device)
+    _, ldo = _rows(out)
+    _check(lib().binv_swiglu(_ptr(gate_up), ld, T, F, _ptr(out), ldo, _stream(gate_up)),
+           "binv_swiglu")
+    return out
+
+
+def residual_add(h, x):
+    """h (fp32) += x (bf16), in place."""
+    _dev(h, x)
+    T, ldh = _rows(h)
+    _, ldx = _rows(x)
+    _check(lib().binv_residual_add(_ptr(h), ldh, _ptr(x), ldx, T, h.shape[1], _stream(h)),
+           "binv_residual_add")
+    return h
+
+
+def gather_rows(src, idx, out=None):
+    """out[r] = src[idx[r]] (bit copy)."""
+    _dev(src, idx, out)
+    _, lds = _rows(src)
+    R = idx.shape[0]
+    if out is None:
+        out = torch.empty((R, src.shape[1]), dtype=src.dtype, device=src.device)
+    _, ldd = _rows(out)
+    _check(lib().binv_gather_rows(_ptr(src), _dt(src), lds, _ptr(idx), R, _ptr(out), ldd,
+                                  src.shape[1], _stream(src)), "binv_gather_rows")
+    return out
+
+
+def topk(x, K=20):
+    """Exact top-K per fp32 row: (ids int32 [R, K], vals fp32 [R, K])."""
+    _dev(x)
+    R, ldx = _rows(x)
+    ids = torch.empty((R, K), dtype=torch.int32, device=x.device)
+    vals = torch.empty((R, K), dtype=torch.float32, device=x.device)
+    _check(lib().binv_topk(_ptr(x), ldx, R, x.shape[1], K, _ptr(ids), _ptr(vals), _stream(x)),
+           "binv_topk")
+    return ids, vals

@@ -206,4 +206,77 @@ int binv_attn_decode_paged_tuned(const void* q, const void* k_cache, const void*
     return status_of(binv::launch_attention_decode_tuned(a, (hipStream_t)stream));
 }
 
+// ---------------------------------------------------------------- decoder glue
+
+int binv_embed(const int32_t* ids, int64_t T, const void* table, int64_t V, int64_t H,
+               float* out, void* stream) {
+    if (T < 0 || V <= 0 || H <= 0) return BINV_ERR_INVALID_ARG;
+    if (T == 0) return BINV_OK;
+    if (!ids || !table || !out) return BINV_ERR_INVALID_ARG;
+    if (T > I32MAX || H > I32MAX) return BINV_ERR_UNSUPPORTED;
+    return status_of(binv::launch_embed(ids, table, V, (int)H, T, out, (hipStream_t)stream));
+}
+
+int binv_rope_kv_write(const void* qkv, int64_t ld_qkv, const int32_t* tok_seq,
+                       const int32_t* tok_pos, int64_t T, int Hq, int Hkv, int D, double theta,
+                       void* q_out, void* k_cache, void* v_cache, const int32_t* page_table,
+                       int64_t pt_stride, int page_size, void* stream) {
+    if (T < 0) return BINV_ERR_INVALID_ARG;
+    if (T == 0) return BINV_OK;
+    if (!qkv || !tok_seq || !tok_pos || !q_out || !k_cache || !v_cache || !page_table)
+        return BINV_ERR_INVALID_ARG;
+    if (Hq <= 0 || Hkv <= 0 || pt_stride <= 0 || !(theta > 1.0) || !isfinite(theta))
+        return BINV_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return BINV_ERR_UNSUPPORTED;
+    if (page_size != BINV_PAGE_SIZE) return BINV_ERR_UNSUPPORTED;
+    if (ld_qkv < (int64_t)(Hq + 2 * Hkv) * D) return BINV_ERR_INVALID_ARG;
+    if (T > I32MAX) return BINV_ERR_UNSUPPORTED;
+    return status_of(binv::launch_rope_kv(qkv, ld_qkv, tok_seq, tok_pos, T, Hq, Hkv, D, theta,
+                                          q_out, k_cache, v_cache, page_table, pt_stride,
+                                          (hipStream_t)stream));
+}
+
+int binv_swiglu(const void* gate_up, int64_t ld_gu, int64_t T, int64_t F, void* out,
+                int64_t ld_out, void* stream) {
+    if (T < 0 || F < 0) return BINV_ERR_INVALID_ARG;
+    if (T == 0 || F == 0) return BINV_OK;
+    if (!gate_up || !out || ld_gu < 2 * F || ld_out < F) return BINV_ERR_INVALID_ARG;
+    if (T > 65535 || F > I32MAX) return BINV_ERR_UNSUPPORTED;
+    return status_of(binv::launch_swiglu(gate_up, ld_gu, T, (int)F, out, ld_out,
+                                         (hipStream_t)stream));
+}
+
+int binv_residual_add(float* h, int64_t ldh, const void* x, int64_t ldx, int64_t T, int64_t H,
+                      void* stream) {
+    if (T < 0 || H < 0) return BINV_ERR_INVALID_ARG;
+    if (T == 0 || H == 0) return BINV_OK;
+    if (!h || !x || ldh < H || ldx < H) return BINV_ERR_INVALID_ARG;
+    if (T > 65535 || H > I32MAX) return BINV_ERR_UNSUPPORTED;
+    return status_of(binv::launch_add(h, ldh, x, ldx, T, (int)H, (hipStream_t)stream));
+}
+
+int binv_gather_rows(const void* src, int dt, int64_t lds, const int32_t* idx, int64_t R,
+                     void* dst, int64_t ldd, int64_t cols, void* stream) {
+    if (R < 0 || cols < 0 || !valid_dt(dt)) return BINV_ERR_INVALID_ARG;
+    if (R == 0 || cols == 0) return BINV_OK;
+    if (!src || !idx || !dst || lds < cols || ldd < cols) return BINV_ERR_INVALID_ARG;
+    const int es = elem_size(dt);
+    if ((cols * es) % 4 != 0 || (lds * es) % 4 != 0 || (ldd * es) % 4 != 0 ||
+        (reinterpret_cast<uintptr_t>(src) & 3u) || (reinterpret_cast<uintptr_t>(dst) & 3u))
+        return BINV_ERR_INVALID_ARG;
+    if (R > I32MAX || cols * es > I32MAX) return BINV_ERR_UNSUPPORTED;
+    return status_of(binv::launch_gather(src, lds * es, idx, R, dst, ldd * es, (int)(cols * es),
+                                         (hipStream_t)stream));
+}
+
+int binv_topk(const float* x, int64_t ldx, int64_t R, int64_t n, int K, int32_t* ids,
+              float* vals, void* stream) {
+    if (R < 0 || n < 0 || K < 1) return BINV_ERR_INVALID_ARG;
+    if (K > 32) return BINV_ERR_UNSUPPORTED;
+    if (R == 0) return BINV_OK;
+    if (!x || !ids || !vals || ldx < n) return BINV_ERR_INVALID_ARG;
+    if (R > I32MAX || n > I32MAX) return BINV_ERR_UNSUPPORTED;
+    return status_of(binv::launch_topk(x, ldx, R, n, K, ids, vals, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -54,7 +54,7 @@ using namespace attn;
 // Grid: x = (query tile, KV head), y = chunk, z = sequence; workgroups of
 // chunks past a tile's last position exit at once.
 template <int D, int G>
-__global__ __launch_bounds__(ChunkShape<D>::NTH, 4) void attn_chunk_kernel(
+__global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chunk_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     const int32_t* __restrict__ page_table, int64_t pt_stride,

@@ -38,7 +38,7 @@ __device__ __forceinline__ void split_range(int n, int s_target, int s, int& c0,
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(ChunkShape<D>::NTH, 4) void attn_split_kernel(
+__global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_split_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     const int32_t* __restrict__ page_table, int64_t pt_stride, const int32_t* __restrict__ kv_lens,
     float* __restrict__ ws_o, float2* __restrict__ ws_ml, int Hq, int Hkv, int s_target,

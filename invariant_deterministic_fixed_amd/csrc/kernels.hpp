@@ -45,4 +45,19 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 size_t attn_tuned_workspace_bytes(int64_t B, int Hq, int D, int64_t max_kv_len);
 hipError_t launch_attention_decode_tuned(const AttnArgs& a, hipStream_t s);
 
+hipError_t launch_embed(const int32_t* ids, const void* table, int64_t V, int H, int64_t T,
+                        float* out, hipStream_t s);
+hipError_t launch_rope_kv(const void* qkv, int64_t ld, const int32_t* tok_seq,
+                          const int32_t* tok_pos, int64_t T, int Hq, int Hkv, int D, double theta,
+                          void* q_out, void* k_cache, void* v_cache, const int32_t* page_table,
+                          int64_t pt_stride, hipStream_t s);
+hipError_t launch_swiglu(const void* gu, int64_t ld, int64_t T, int F, void* out, int64_t ldo,
+                         hipStream_t s);
+hipError_t launch_add(float* h, int64_t ldh, const void* x, int64_t ldx, int64_t T, int H,
+                      hipStream_t s);
+hipError_t launch_gather(const void* src, int64_t lds, const int32_t* idx, int64_t R, void* dst,
+                         int64_t ldd, int row_bytes, hipStream_t s);
+hipError_t launch_topk(const float* x, int64_t ldx, int64_t R, int64_t n, int K, int32_t* ids,
+                       float* vals, hipStream_t s);
+
 }  // namespace binv

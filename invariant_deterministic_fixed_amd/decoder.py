@@ -1,0 +1,179 @@
+"""A dense pre-norm decoder whose every numeric step runs in libbinv.
+
+Host side only: weight allocation, page allocation from a shuffled free list,
+the per-step token / position arrays, and the order of library calls.  One
+`Decoder.step` runs all layers over a ragged batch of sequences, each
+contributing a run of new tokens (a prefill chunk, or one decode token), and
+returns the fp32 logits and the exact top-20 of each sequence's last token.
+
+Per layer (residual stream h in fp32; the ops of the pages' three reductions
+plus the pointwise glue, devpress.csdn.net explainer of "Defeating
+Nondeterminism in LLM Inference", section 3):
+    x = rmsnorm(h) -> bf16;  qkv = x @ Wqkv -> bf16
+    RoPE on q, k; k and v written into the paged cache
+    a = attention over cached + new keys (the unified prefill entry point;
+        a decode token is a run of length 1)
+    h += a @ Wo;  x = rmsnorm(h);  h += swiglu(x @ Wgu) @ Wd
+then logits = rmsnorm(h_last) @ Wlm (fp32) and top-20 by value, ties by index.
+RMSNorm weights are 1 (the workload fixes none).
+"""
+import math
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .synth import PAGE_SIZE
+
+CONFIG5 = dict(layers=32, hidden=4096, n_heads=32, n_kv=8, head_dim=128, ffn=14336,
+               vocab=128256, theta=5e5, eps=1e-6)
+
+
+def random_weights(cfg, seed, device, std=0.02):
+    """bf16 weights ~ N(0, std^2), drawn in fp32 from a seeded generator."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    H, Hq, Hkv, D, F, V = (cfg["hidden"], cfg["n_heads"], cfg["n_kv"], cfg["head_dim"],
+                           cfg["ffn"], cfg["vocab"])
+
+    def mk(*shape):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        for i in range(0, shape[0], 1024):          # draw in slabs to bound fp32 scratch
+            rows = min(1024, shape[0] - i)
+            t[i:i + rows] = (torch.randn((rows,) + shape[1:], generator=g, device=device,
+                                         dtype=torch.float32) * std).to(torch.bfloat16)
+        return t
+
+    w = {"embed": mk(V, H), "layers": []}
+    for _ in range(cfg["layers"]):
+        w["layers"].append({"wqkv": mk(H, (Hq + 2 * Hkv) * D), "wo": mk(Hq * D, H),
+                            "wgu": mk(H, 2 * F), "wd": mk(F, H)})
+    w["lm_head"] = mk(H, V)
+    w["norm"] = torch.ones(H, dtype=torch.bfloat16, device=device)
+    return w
+
+
+class KVPool:
+    """Per-layer paged K/V caches and one page table shared by all layers.
+
+    Pages are handed out from a free list shuffled by `seed`, so where a
+    sequence's pages sit changes from run to run."""
+
+    def __init__(self, cfg, num_pages, max_seqs, max_len, seed, device):
+        Hkv, D = cfg["n_kv"], cfg["head_dim"]
+        self.device = device
+        self.k = [torch.zeros((num_pages, Hkv, PAGE_SIZE, D), dtype=torch.bfloat16, device=device)
+                  for _ in range(cfg["layers"])]
+        self.v = [torch.zeros((num_pages, Hkv, D, PAGE_SIZE), dtype=torch.bfloat16, device=device)
+                  for _ in range(cfg["layers"])]
+        self.free = list(np.random.default_rng(int(seed)).permutation(num_pages))
+        self.pps = -(-int(max_len) // PAGE_SIZE)
+        self.table = np.zeros((max_seqs, self.pps), dtype=np.int32)
+        self.pages = [[] for _ in range(max_seqs)]
+        self.used = [False] * max_seqs
+        self.table_dev = torch.zeros((max_seqs, self.pps), dtype=torch.int32, device=device)
+        self.dirty = True
+
+    def alloc(self):
+        s = self.used.index(False)
+        self.used[s] = True
+        return s
+
+    def ensure(self, slot, length):
+        need = -(-int(length) // PAGE_SIZE)
+        if need > self.pps:
+            raise ValueError("sequence longer than the pool's max_len")
+        while len(self.pages[slot]) < need:
+            p = int(self.free.pop())
+            self.table[slot, len(self.pages[slot])] = p
+            self.pages[slot].append(p)
+            self.dirty = True
+
+    def release(self, slot):
+        self.free.extend(self.pages[slot])
+        self.pages[slot] = []
+        self.table[slot] = 0
+        self.used[slot] = False
+        self.dirty = True
+
+    def page_table(self):
+        if self.dirty:
+            self.table_dev.copy_(torch.from_numpy(self.table))
+            self.dirty = False
+        return self.table_dev
+
+
+class Decoder:
+    def __init__(self, weights, cfg, pool, max_tokens, max_seqs, max_kv_len, topk=20):
+        self.w, self.cfg, self.pool, self.topk = weights, cfg, pool, topk
+        dev = pool.device
+        H, Hq, Hkv, D, F = (cfg["hidden"], cfg["n_heads"], cfg["n_kv"], cfg["head_dim"],
+                            cfg["ffn"])
+        T = int(max_tokens)
+        bf = torch.bfloat16
+        self.h = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.x = torch.empty((T, H), dtype=bf, device=dev)
+        self.qkv = torch.empty((T, (Hq + 2 * Hkv) * D), dtype=bf, device=dev)
+        self.q = torch.empty((T, Hq, D), dtype=bf, device=dev)
+        self.a = torch.empty((T, Hq, D), dtype=bf, device=dev)
+        self.o = torch.empty((T, H), dtype=bf, device=dev)
+        self.gu = torch.empty((T, 2 * F), dtype=bf, device=dev)
+        self.s = torch.empty((T, F), dtype=bf, device=dev)
+        self.max_kv_len = int(max_kv_len)
+        self.ws = torch.empty(B.attn_workspace_bytes(T, Hq, D, self.max_kv_len),
+                              dtype=torch.uint8, device=dev)
+        self.hl = torch.empty((max_seqs, H), dtype=torch.float32, device=dev)
+        self.xl = torch.empty((max_seqs, H), dtype=bf, device=dev)
+        self.logits = torch.empty((max_seqs, cfg["vocab"]), dtype=torch.float32, device=dev)
+        self.max_tokens, self.max_seqs = T, max_seqs
+
+    def step(self, items):
+        """items: list of (slot, new token ids, start position).  Returns
+        (logits fp32 [n, V], top ids int32 [n, k], top values fp32 [n, k]) for
+        the last token of each item, as device tensors, in item order."""
+        cfg, pool, dev = self.cfg, self.pool, self.pool.device
+        H, Hq, Hkv, D, F = (cfg["hidden"], cfg["n_heads"], cfg["n_kv"], cfg["head_dim"],
+                            cfg["ffn"])
+        ids, tseq, tpos, cu, lens = [], [], [], [0], []
+        for slot, toks, start in items:
+            pool.ensure(slot, start + len(toks))
+            ids.extend(int(t) for t in toks)
+            tseq.extend([slot] * len(toks))
+            tpos.extend(range(start, start + len(toks)))
+            cu.append(cu[-1] + len(toks))
+            lens.append(start + len(toks))
+        T, nb = len(ids), len(items)
+        if T > self.max_tokens or nb > self.max_seqs or max(lens) > self.max_kv_len:
+            raise ValueError("step larger than the decoder was sized for")
+        host = np.array(ids + tseq + tpos + cu + lens + [c - 1 for c in cu[1:]], dtype=np.int32)
+        dv = torch.from_numpy(host).to(dev)
+        ids_d, tseq_d, tpos_d = dv[:T], dv[T:2 * T], dv[2 * T:3 * T]
+        cu_d = dv[3 * T:3 * T + nb + 1]
+        lens_d = dv[3 * T + nb + 1:3 * T + 2 * nb + 1]
+        last_d = dv[3 * T + 2 * nb + 1:]
+        table = pool.page_table()
+        max_q = max(len(t) for _, t, _ in items)
+        h, x, qkv, q, a, o, gu, s = (t[:T] for t in (self.h, self.x, self.qkv, self.q, self.a,
+                                                     self.o, self.gu, self.s))
+        scale = 1.0 / math.sqrt(D)
+        B.embed(ids_d, self.w["embed"], out=h)
+        for li, lw in enumerate(self.w["layers"]):
+            B.rmsnorm(h, self.w["norm"], cfg["eps"], out=x)
+            B.gemm(x, lw["wqkv"], out=qkv)
+            B.rope_kv_write(qkv, tseq_d, tpos_d, Hq, Hkv, D, cfg["theta"], pool.k[li], pool.v[li],
+                            table, q_out=q)
+            B.attn_prefill(q, cu_d, pool.k[li], pool.v[li], table, lens_d, max_q,
+                           self.max_kv_len, scale, out=a, workspace=self.ws)
+            B.gemm(a.view(T, Hq * D), lw["wo"], out=o)
+            B.residual_add(h, o)
+            B.rmsnorm(h, self.w["norm"], cfg["eps"], out=x)
+            B.gemm(x, lw["wgu"], out=gu)
+            B.swiglu(gu, out=s)
+            B.gemm(s, lw["wd"], out=o)
+            B.residual_add(h, o)
+        hl, xl, logits = self.hl[:nb], self.xl[:nb], self.logits[:nb]
+        B.gather_rows(h, last_d, out=hl)
+        B.rmsnorm(hl, self.w["norm"], cfg["eps"], out=xl)
+        B.gemm(xl, self.w["lm_head"], out=logits)
+        top_ids, top_vals = B.topk(logits, self.topk)
+        return logits, top_ids, top_vals

@@ -1,0 +1,113 @@
+"""End-to-end decoder on the GPU.
+
+* small decoder (2 layers, hidden 256): logits against the fp64 reference
+  decoder, one-shot vs chunked prefill vs decode bitwise, and bitwise
+  invariance of a greedy target under random neighbours;
+* the full random-init 8B-class decoder (32 layers, hidden 4096, 32/8 heads of
+  128, FFN 14336, vocab 128256): a 512-token target greedy-decoded for 200
+  tokens alone and with neighbours; tokens and top-20 fp32 logits must be
+  bitwise identical, and one prefill of prompt + generated tokens must
+  reproduce the last decode step's logits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from invariant_deterministic_fixed_amd import decoder as dec
+from invariant_deterministic_fixed_amd import harness
+from oracle import decoder as odec
+from helpers import TOL_F32_LOGITS, assert_bitwise_equal, f64, row_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+SMALL = dict(layers=2, hidden=256, n_heads=4, n_kv=2, head_dim=64, ffn=512, vocab=1000,
+             theta=5e5, eps=1e-6)
+
+
+@pytest.fixture(scope="module")
+def small():
+    w = dec.random_weights(SMALL, 7, DEV, std=0.05)
+    pool = dec.KVPool(SMALL, num_pages=2048, max_seqs=16, max_len=2048, seed=3, device=DEV)
+    d = dec.Decoder(w, SMALL, pool, max_tokens=2048, max_seqs=16, max_kv_len=2048)
+    ow = {"embed": f64(w["embed"]), "lm_head": f64(w["lm_head"]),
+          "layers": [{k: f64(v) for k, v in l.items()} for l in w["layers"]]}
+    return w, pool, d, ow
+
+
+def test_small_decoder_logits_match_fp64_reference(small):
+    w, pool, d, ow = small
+    r = np.random.default_rng(1)
+    prompt = r.integers(0, SMALL["vocab"], 70).tolist()
+    cont = r.integers(0, SMALL["vocab"], 5).tolist()
+    slot = pool.alloc()
+    got = [d.step([(slot, prompt, 0)])[0][0].cpu()]
+    for i, tkn in enumerate(cont):                      # teacher-forced decode steps
+        got.append(d.step([(slot, [tkn], 70 + i)])[0][0].cpu())
+    pool.release(slot)
+    ref = odec.forward(ow, SMALL, prompt + cont)[69:]
+    err = row_rel_err(torch.stack(got).double().numpy(), ref)
+    print("small decoder logits rel err per step:", err)
+    assert err.max() <= TOL_F32_LOGITS, err
+
+
+def test_small_decoder_chunked_prefill_and_decode_bitwise(small):
+    w, pool, d, _ = small
+    prompt = np.random.default_rng(2).integers(0, SMALL["vocab"], 100).tolist()
+    slot = pool.alloc()
+    one_shot = d.step([(slot, prompt, 0)])[0][0].clone()
+    pool.release(slot)
+    for chunk in [1, 7, 16, 64]:
+        slot = pool.alloc()
+        for s0 in range(0, 100, chunk):
+            lg = d.step([(slot, prompt[s0:s0 + chunk], s0)])[0][0]
+        assert_bitwise_equal(lg, one_shot, f"chunk {chunk}")
+        pool.release(slot)
+
+
+def test_small_decoder_invariance_with_neighbours(small):
+    w, pool, d, _ = small
+    r = np.random.default_rng(3)
+    prompt = r.integers(0, SMALL["vocab"], 70).tolist()
+    alone = harness.run(d, pool, prompt, 12, seed=0)
+    for trial, (n, budget) in enumerate([(1, 16), (7, 64), (15, None), (5, 7)]):
+        rr = np.random.default_rng(100 + trial)
+        nbrs = [rr.integers(0, SMALL["vocab"], int(rr.integers(16, 301))).tolist() for _ in range(n)]
+        got = harness.run(d, pool, prompt, 12, neighbours=nbrs, budget=budget, seed=trial + 1)
+        assert harness.same_bits(got, alone), f"trial {trial}: {n} neighbours, budget {budget}"
+
+
+@pytest.fixture(scope="module")
+def full():
+    cfg = dec.CONFIG5
+    torch.cuda.empty_cache()
+    w = dec.random_weights(cfg, 5, DEV)
+    max_len = 8192 + 512 + 256
+    pool = dec.KVPool(cfg, num_pages=40 * (max_len // 16), max_seqs=40, max_len=max_len, seed=11,
+                      device=DEV)
+    d = dec.Decoder(w, cfg, pool, max_tokens=2048 + 64, max_seqs=40, max_kv_len=max_len)
+    yield cfg, pool, d
+    del d, pool, w
+    torch.cuda.empty_cache()
+
+
+def test_config5_target_bitwise_across_compositions(full):
+    cfg, pool, d = full
+    r = np.random.default_rng(42)
+    prompt = r.integers(0, cfg["vocab"], 512).tolist()
+    alone = harness.run(d, pool, prompt, 200, seed=0, record_logits=True)
+    print("target alone: first tokens", alone["tokens"][:8], flush=True)
+    plan = [(1, 256), (7, 512), (31, 2048), (int(r.integers(2, 31)), 512)]
+    for trial, (n, budget) in enumerate(plan):
+        rr = np.random.default_rng(1000 + trial)
+        nbrs = [rr.integers(0, cfg["vocab"], int(rr.integers(16, 8193))).tolist() for _ in range(n)]
+        got = harness.run(d, pool, prompt, 200, neighbours=nbrs, budget=budget, seed=trial + 1)
+        print(f"composition {trial}: {n} neighbours, budget {budget}: "
+              f"equal={harness.same_bits(got, alone)}", flush=True)
+        assert harness.same_bits(got, alone), f"composition {trial}"
+    # one prefill of prompt + the first 199 generated tokens reproduces the
+    # logits that chose the 200th
+    slot = pool.alloc()
+    replay = d.step([(slot, prompt + alone["tokens"][:199], 0)])[0][0].cpu()
+    pool.release(slot)
+    assert_bitwise_equal(replay, alone["logits"][199], "prefill replay vs decode")
