@@ -54,7 +54,7 @@ def random_weights(cfg, seed, device, std=0.02):
 
 
 class KVPool:
-    """Per-layer paged K/V caches and one page table shared by all layers.
+    """Per-layer paged K/V caches and one host page table shared by all layers.
 
     Pages are handed out from a free list shuffled by `seed`, so where a
     sequence's pages sit changes from run to run."""
@@ -71,8 +71,6 @@ class KVPool:
         self.table = np.zeros((max_seqs, self.pps), dtype=np.int32)
         self.pages = [[] for _ in range(max_seqs)]
         self.used = [False] * max_seqs
-        self.table_dev = torch.zeros((max_seqs, self.pps), dtype=torch.int32, device=device)
-        self.dirty = True
 
     def alloc(self):
         s = self.used.index(False)
@@ -87,20 +85,12 @@ class KVPool:
             p = int(self.free.pop())
             self.table[slot, len(self.pages[slot])] = p
             self.pages[slot].append(p)
-            self.dirty = True
 
     def release(self, slot):
         self.free.extend(self.pages[slot])
         self.pages[slot] = []
         self.table[slot] = 0
         self.used[slot] = False
-        self.dirty = True
-
-    def page_table(self):
-        if self.dirty:
-            self.table_dev.copy_(torch.from_numpy(self.table))
-            self.dirty = False
-        return self.table_dev
 
 
 class Decoder:
@@ -134,24 +124,29 @@ class Decoder:
         cfg, pool, dev = self.cfg, self.pool, self.pool.device
         H, Hq, Hkv, D, F = (cfg["hidden"], cfg["n_heads"], cfg["n_kv"], cfg["head_dim"],
                             cfg["ffn"])
+        # sequence b of this step reads row b of the step's page table: the
+        # attention entry points and the KV write both address pages by the
+        # sequence's index in the call, not by its pool slot
         ids, tseq, tpos, cu, lens = [], [], [], [0], []
-        for slot, toks, start in items:
+        for b, (slot, toks, start) in enumerate(items):
             pool.ensure(slot, start + len(toks))
             ids.extend(int(t) for t in toks)
-            tseq.extend([slot] * len(toks))
+            tseq.extend([b] * len(toks))
             tpos.extend(range(start, start + len(toks)))
             cu.append(cu[-1] + len(toks))
             lens.append(start + len(toks))
         T, nb = len(ids), len(items)
         if T > self.max_tokens or nb > self.max_seqs or max(lens) > self.max_kv_len:
             raise ValueError("step larger than the decoder was sized for")
-        host = np.array(ids + tseq + tpos + cu + lens + [c - 1 for c in cu[1:]], dtype=np.int32)
+        rows = pool.table[[slot for slot, _, _ in items]]
+        host = np.concatenate([np.array(ids + tseq + tpos + cu + lens + [c - 1 for c in cu[1:]],
+                                        dtype=np.int32), rows.reshape(-1)])
         dv = torch.from_numpy(host).to(dev)
         ids_d, tseq_d, tpos_d = dv[:T], dv[T:2 * T], dv[2 * T:3 * T]
         cu_d = dv[3 * T:3 * T + nb + 1]
         lens_d = dv[3 * T + nb + 1:3 * T + 2 * nb + 1]
-        last_d = dv[3 * T + 2 * nb + 1:]
-        table = pool.page_table()
+        last_d = dv[3 * T + 2 * nb + 1:3 * T + 3 * nb + 1]
+        table = dv[3 * T + 3 * nb + 1:].view(nb, pool.pps)
         max_q = max(len(t) for _, t, _ in items)
         h, x, qkv, q, a, o, gu, s = (t[:T] for t in (self.h, self.x, self.qkv, self.q, self.a,
                                                      self.o, self.gu, self.s))
