@@ -7,6 +7,11 @@ One step = one pass of every hot-path kernel over one batch of synthetic input:
   3. decode attn  paged, 32 query / 8 KV heads of 128, B = 256 sequences with
                   KV lengths log-uniform in [128, 32768], pages shuffled
   4. prefill attn one 4096-token sequence, same head shape, one shot
+  5. decoder glue embedding of 8192 tokens into an fp32 residual stream,
+                  residual add of the GEMM output, RoPE + paged KV write of a
+                  4096-token fused q/k/v projection [4096, 6144], SwiGLU on a
+                  [4096, 2 x 14336] gate/up block, row gather and exact top-20
+                  of 256 rows of 128256 fp32 logits
 Inputs are resident in HBM before the timed region.  Each leg is bracketed by
 HIP events recorded on the stream the kernels are launched on (torch's current
 stream).  The decode leg streams ~6 GB of KV, far more than the 256 MB
@@ -43,9 +48,11 @@ GEMM_M, GEMM_N, GEMM_K = 8192, 4096, 4096
 DEC_B, HQ, HKV, HD = 256, 32, 8, 128
 DEC_LMIN, DEC_LMAX = 128, 32768
 PREFILL_T = 4096
+FFN, VOCAB, LOGIT_ROWS, THETA = 14336, 128256, 256, 5e5
 WORKLOAD = (f"rmsnorm {RMS_M}x{HIDDEN} bf16 -> gemm {GEMM_M}x{GEMM_N}x{GEMM_K} bf16 -> "
             f"paged decode attn B={DEC_B} Hq={HQ} Hkv={HKV} D={HD} L~logU[{DEC_LMIN},{DEC_LMAX}] "
-            f"-> prefill attn T={PREFILL_T}")
+            f"-> prefill attn T={PREFILL_T} -> decoder glue (embed, residual add, RoPE+KV write, "
+            f"SwiGLU F={FFN}, top-20 of {LOGIT_ROWS}x{VOCAB})")
 
 
 def build_workload(device="cuda:0", seed_base=0):
@@ -85,15 +92,35 @@ def build_workload(device="cuda:0", seed_base=0):
     w["pf_ws"] = torch.empty(binv.attn_workspace_bytes(PREFILL_T, HQ, HD, PREFILL_T),
                              dtype=torch.uint8, device=device)
     w["scale"] = 1.0 / math.sqrt(HD)
+
+    # decoder glue
+    g = torch.Generator(device=device)
+    g.manual_seed(s4 + 20)
+    w["ids"] = torch.randint(0, VOCAB, (GEMM_M,), generator=g, device=device, dtype=torch.int32)
+    w["embed"] = synth.normal((VOCAB, HIDDEN), 0.02, s4 + 21, device)
+    w["h"] = torch.empty((GEMM_M, HIDDEN), dtype=torch.float32, device=device)
+    w["qkv"] = synth.normal((PREFILL_T, (HQ + 2 * HKV) * HD), 1.0, s4 + 22, device)
+    w["rope_q"] = torch.empty((PREFILL_T, HQ, HD), dtype=torch.bfloat16, device=device)
+    n_pages = PREFILL_T // 16
+    w["rope_k"] = torch.zeros((n_pages, HKV, 16, HD), dtype=torch.bfloat16, device=device)
+    w["rope_v"] = torch.zeros((n_pages, HKV, HD, 16), dtype=torch.bfloat16, device=device)
+    w["rope_pt"] = torch.randperm(n_pages, generator=g, device=device).to(torch.int32).view(1, -1)
+    w["rope_seq"] = torch.zeros(PREFILL_T, dtype=torch.int32, device=device)
+    w["rope_pos"] = torch.arange(PREFILL_T, dtype=torch.int32, device=device)
+    w["gu"] = synth.normal((PREFILL_T, 2 * FFN), 1.0, s4 + 23, device)
+    w["swi"] = torch.empty((PREFILL_T, FFN), dtype=torch.bfloat16, device=device)
+    w["logits"] = synth.normal((LOGIT_ROWS, VOCAB), 3.0, s4 + 24, device, dtype=torch.float32)
+    w["rows"] = torch.randperm(GEMM_M, generator=g, device=device)[:LOGIT_ROWS].to(torch.int32)
+    w["hl"] = torch.empty((LOGIT_ROWS, HIDDEN), dtype=torch.float32, device=device)
     return w
 
 
 def run_step(w, events=None):
-    """One pass of the hot path; if `events` (5 torch.cuda.Event) is given the
+    """One pass of the hot path; if `events` (6 torch.cuda.Event) is given the
     legs are bracketed by them."""
     import invariant_deterministic_fixed_amd as binv
 
-    ev = events or [None] * 5
+    ev = events or [None] * 6
     rec = (lambda e: e.record()) if events else (lambda e: None)
     rec(ev[0])
     binv.rmsnorm(w["x"], w["gamma"], 1e-6, out=w["y"])
@@ -108,6 +135,14 @@ def run_step(w, events=None):
     binv.attn_prefill(w["pf_q"], w["pf_cu"], p.k_cache, p.v_cache, p.page_table, p.kv_lens,
                       PREFILL_T, PREFILL_T, w["scale"], out=w["pf_out"], workspace=w["pf_ws"])
     rec(ev[4])
+    binv.embed(w["ids"], w["embed"], out=w["h"])
+    binv.residual_add(w["h"], w["C"])
+    binv.rope_kv_write(w["qkv"], w["rope_seq"], w["rope_pos"], HQ, HKV, HD, THETA, w["rope_k"],
+                       w["rope_v"], w["rope_pt"], q_out=w["rope_q"])
+    binv.swiglu(w["gu"], out=w["swi"])
+    binv.gather_rows(w["h"], w["rows"], out=w["hl"])
+    binv.topk(w["logits"], 20)
+    rec(ev[5])
 
 
 def algorithmic(w):
@@ -124,6 +159,12 @@ def algorithmic(w):
         "decode_bytes": dec_bytes,
         "decode_sum_kv": sum_l,
         "prefill_flops": 4 * HQ * HD * (PREFILL_T * (PREFILL_T + 1) // 2),
+        "glue_bytes": (GEMM_M * 4 + GEMM_M * HIDDEN * (2 + 4)          # embed: ids, rows in, h out
+                       + GEMM_M * HIDDEN * (4 + 2 + 4)                  # residual add
+                       + PREFILL_T * ((HQ + 2 * HKV) * HD * 2 + HQ * HD * 2 + 2 * HKV * HD * 2 + 8)
+                       + PREFILL_T * (2 * FFN * 2 + FFN * 2)            # swiglu
+                       + LOGIT_ROWS * (4 + 2 * HIDDEN * 4)              # gather
+                       + LOGIT_ROWS * (VOCAB * 4 + 20 * 8)),            # top-20
     }
 
 
@@ -143,9 +184,12 @@ def traffic_for(kernel_key):
         return None
     if not rec:
         return None
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or _sha(src) != rec["source_sha256"]:
-        return None
+    pinned = dict(rec.get("also", {}))
+    pinned[rec["source"]] = rec["source_sha256"]
+    for rel, digest in pinned.items():
+        src = os.path.join(ROOT, rel)
+        if not os.path.exists(src) or _sha(src) != digest:
+            return None
     return rec["hbm_bytes_per_launch"]
 
 
@@ -222,7 +266,7 @@ def main():
         run_step(w)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -230,13 +274,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    legs = ["rmsnorm", "gemm", "decode_attn", "prefill_attn"]
+    legs = ["rmsnorm", "gemm", "decode_attn", "prefill_attn", "decoder_glue"]
     ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(legs)}
     s = {n: ms[n] * 1e-3 for n in legs}
     gemm_tflops = work["gemm_flops"] / s["gemm"] / 1e12
     dec_gbps = work["decode_bytes"] / s["decode_attn"] / 1e9
     rms_gbps = work["rmsnorm_bytes"] / s["rmsnorm"] / 1e9
     pf_tflops = work["prefill_flops"] / s["prefill_attn"] / 1e12
+    glue_gbps = work["glue_bytes"] / s["decoder_glue"] / 1e9
 
     if args.profile_copy:
         # calibration for the HBM byte counters: one elementwise kernel that
@@ -282,6 +327,7 @@ def main():
         "rmsnorm_GBps": round(rms_gbps, 1),
         "rmsnorm_frac_hbm": round(rms_gbps / PEAK_HBM_GBPS, 4),
         "prefill_attn_TFLOPs": round(pf_tflops, 2),
+        "decoder_glue_GBps": round(glue_gbps, 1),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

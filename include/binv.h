@@ -217,7 +217,8 @@ int binv_attn_decode_paged_tuned(const void* q,
  * ------------------------------------------------------------------------ */
 
 /* out[t, :] = table[ids[t], :] widened to fp32.  table bf16 [V, H] row-major,
- * out fp32 [T, H] (the residual stream).  An id outside [0, V) gives a zero row. */
+ * out fp32 [T, H] (the residual stream).  An id outside [0, V) gives a zero row.
+ * H % 8 == 0; table and out 16-byte aligned. */
 int binv_embed(const int32_t* ids, int64_t T, const void* table, int64_t V, int64_t H,
                float* out, void* stream);
 
@@ -240,11 +241,13 @@ int binv_rope_kv_write(const void* qkv, int64_t ld_qkv, const int32_t* tok_seq,
 
 /* SwiGLU: out[t, j] = bf16(silu(g) * u), g = gate_up[t, j], u = gate_up[t, F + j],
  * silu(g) = g / (1 + exp(-g)), fp32.  gate_up bf16 [T, ld_gu >= 2F], out bf16
- * [T, ld_out >= F].  T <= 65535. */
+ * [T, ld_out >= F].  F, ld_gu, ld_out multiples of 8, pointers 16-byte aligned;
+ * T <= 65535. */
 int binv_swiglu(const void* gate_up, int64_t ld_gu, int64_t T, int64_t F, void* out,
                 int64_t ld_out, void* stream);
 
-/* Residual update h[t, j] += x[t, j]: h fp32 [T, ldh], x bf16 [T, ldx].  T <= 65535. */
+/* Residual update h[t, j] += x[t, j]: h fp32 [T, ldh], x bf16 [T, ldx].
+ * H, ldh, ldx multiples of 4; h 16-byte and x 8-byte aligned; T <= 65535. */
 int binv_residual_add(float* h, int64_t ldh, const void* x, int64_t ldx, int64_t T, int64_t H,
                       void* stream);
 

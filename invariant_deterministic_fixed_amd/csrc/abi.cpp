@@ -213,6 +213,8 @@ int binv_embed(const int32_t* ids, int64_t T, const void* table, int64_t V, int6
     if (T < 0 || V <= 0 || H <= 0) return BINV_ERR_INVALID_ARG;
     if (T == 0) return BINV_OK;
     if (!ids || !table || !out) return BINV_ERR_INVALID_ARG;
+    if (!aligned16(table) || !aligned16(out)) return BINV_ERR_INVALID_ARG;
+    if (H % 8 != 0) return BINV_ERR_UNSUPPORTED;
     if (T > I32MAX || H > I32MAX) return BINV_ERR_UNSUPPORTED;
     return status_of(binv::launch_embed(ids, table, V, (int)H, T, out, (hipStream_t)stream));
 }
@@ -241,6 +243,8 @@ int binv_swiglu(const void* gate_up, int64_t ld_gu, int64_t T, int64_t F, void* 
     if (T < 0 || F < 0) return BINV_ERR_INVALID_ARG;
     if (T == 0 || F == 0) return BINV_OK;
     if (!gate_up || !out || ld_gu < 2 * F || ld_out < F) return BINV_ERR_INVALID_ARG;
+    if (!aligned16(gate_up) || !aligned16(out) || ld_gu % 8 || ld_out % 8) return BINV_ERR_INVALID_ARG;
+    if (F % 8 != 0) return BINV_ERR_UNSUPPORTED;
     if (T > 65535 || F > I32MAX) return BINV_ERR_UNSUPPORTED;
     return status_of(binv::launch_swiglu(gate_up, ld_gu, T, (int)F, out, ld_out,
                                          (hipStream_t)stream));
@@ -251,6 +255,9 @@ int binv_residual_add(float* h, int64_t ldh, const void* x, int64_t ldx, int64_t
     if (T < 0 || H < 0) return BINV_ERR_INVALID_ARG;
     if (T == 0 || H == 0) return BINV_OK;
     if (!h || !x || ldh < H || ldx < H) return BINV_ERR_INVALID_ARG;
+    if (!aligned16(h) || (reinterpret_cast<uintptr_t>(x) & 7u) || ldh % 4 || ldx % 4)
+        return BINV_ERR_INVALID_ARG;
+    if (H % 4 != 0) return BINV_ERR_UNSUPPORTED;
     if (T > 65535 || H > I32MAX) return BINV_ERR_UNSUPPORTED;
     return status_of(binv::launch_add(h, ldh, x, ldx, T, (int)H, (hipStream_t)stream));
 }

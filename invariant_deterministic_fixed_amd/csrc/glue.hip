@@ -18,6 +18,7 @@ namespace {
 
 // ------------------------------------------------------------------ embedding
 // out[t, :] = float(table[ids[t], :]); ids outside [0, V) give zeros.
+// H % 8 == 0: each lane moves 8 elements (16 bytes in, 32 bytes out).
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids,
                                                     const bf16_t* __restrict__ table, int64_t V,
                                                     int H, float* __restrict__ out) {
@@ -26,7 +27,14 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
     const bool ok = id >= 0 && id < V;
     const bf16_t* row = table + (ok ? (int64_t)id : 0) * H;
     float* o = out + t * H;
-    for (int j = threadIdx.x; j < H; j += 256) o[j] = ok ? bf16_to_f32(row[j]) : 0.0f;
+    for (int j = threadIdx.x * 8; j < H; j += 256 * 8) {
+        const u32x4 w = ok ? *reinterpret_cast<const u32x4*>(row + j) : u32x4{0u, 0u, 0u, 0u};
+        u32x4 a, b;
+        a[0] = w[0] << 16; a[1] = w[0] & 0xffff0000u; a[2] = w[1] << 16; a[3] = w[1] & 0xffff0000u;
+        b[0] = w[2] << 16; b[1] = w[2] & 0xffff0000u; b[2] = w[3] << 16; b[3] = w[3] & 0xffff0000u;
+        *reinterpret_cast<u32x4*>(o + j) = a;
+        *reinterpret_cast<u32x4*>(o + j + 4) = b;
+    }
 }
 
 // ------------------------------------------------------------------ RoPE + KV write
@@ -80,28 +88,39 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(
 
 // ------------------------------------------------------------------ SwiGLU
 // out[t, j] = bf16( silu(g) * u ),  g = gu[t, j], u = gu[t, F + j],
-// silu(g) = g / (1 + exp(-g)), fp32.
+// silu(g) = g / (1 + exp(-g)), fp32.  F % 8 == 0: 8 outputs per lane.
 __global__ __launch_bounds__(256) void swiglu_kernel(const bf16_t* __restrict__ gu, int64_t ld,
                                                      int F, bf16_t* __restrict__ out,
                                                      int64_t ldo) {
     const int64_t t = blockIdx.y;
-    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int j = (blockIdx.x * 256 + threadIdx.x) * 8;
     if (j >= F) return;
-    const float g = bf16_to_f32(gu[t * ld + j]);
-    const float u = bf16_to_f32(gu[t * ld + F + j]);
-    const float s = g / (1.0f + expf(-g));
-    out[t * ldo + j] = (bf16_t)f32_to_bf16(s * u);
+    const u32x4 gw = *reinterpret_cast<const u32x4*>(gu + t * ld + j);
+    const u32x4 uw = *reinterpret_cast<const u32x4*>(gu + t * ld + F + j);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float g0 = lo_bf16(gw[i]), g1 = hi_bf16(gw[i]);
+        const float u0 = lo_bf16(uw[i]), u1 = hi_bf16(uw[i]);
+        const float s0 = g0 / (1.0f + expf(-g0)), s1 = g1 / (1.0f + expf(-g1));
+        o[i] = pack_bf16x2(s0 * u0, s1 * u1);
+    }
+    *reinterpret_cast<u32x4*>(out + t * ldo + j) = o;
 }
 
 // ------------------------------------------------------------------ residual add
-// h[t, j] += float(x[t, j])  (fp32 residual stream)
+// h[t, j] += float(x[t, j])  (fp32 residual stream); H % 4 == 0: 4 per lane.
 __global__ __launch_bounds__(256) void add_kernel(float* __restrict__ h, int64_t ldh,
                                                   const bf16_t* __restrict__ x, int64_t ldx,
                                                   int H) {
     const int64_t t = blockIdx.y;
-    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (j >= H) return;
-    h[t * ldh + j] += bf16_to_f32(x[t * ldx + j]);
+    float4* hp = reinterpret_cast<float4*>(h + t * ldh + j);
+    const u32x2 xw = *reinterpret_cast<const u32x2*>(x + t * ldx + j);
+    float4 v = *hp;
+    v.x += lo_bf16(xw[0]); v.y += hi_bf16(xw[0]); v.z += lo_bf16(xw[1]); v.w += hi_bf16(xw[1]);
+    *hp = v;
 }
 
 // ------------------------------------------------------------------ row gather
@@ -119,11 +138,28 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ sr
 
 // ------------------------------------------------------------------ top-k
 // Exact top-K of one fp32 row: the K largest values, sorted by value
-// descending and, among equal values, by index ascending.  One workgroup per
-// row; each lane keeps its own sorted top-K over a strided slice, then the
-// workgroup takes K rounds of "best remaining candidate" over the lanes' lists.
+// descending and, among equal values, by index ascending; NaN never selected.
+// One workgroup per row:
+//   1. each value maps to an order-preserving 32-bit key (NaN -> 0, below every
+//      other key); four 8-bit radix passes build histograms of the candidates'
+//      next byte and walk them from the top, which pins down the exact key T of
+//      the K-th largest entry and how many entries equal to T are needed.  The
+//      histograms are integer counts (LDS increments), whose totals do not
+//      depend on the order in which lanes add;
+//   2. one pass in index order (1024-element tiles, ballots and wave prefix
+//      counts) collects every entry with key > T and the lowest-index entries
+//      with key == T;
+//   3. the <= 32 winners are sorted by (value desc, index asc).
 constexpr int TOPK_MAX = 32;
-constexpr int TOPK_NT = 256;
+constexpr int TOPK_NT = 1024;
+constexpr int TOPK_NW = TOPK_NT / 64;
+
+__device__ __forceinline__ uint32_t order_key(float v) {
+    uint32_t b = __float_as_uint(v);
+    if (v != v) return 0u;
+    if ((b & 0x7fffffffu) == 0u) b = 0u;                 // -0 and +0 are one value
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
 
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
@@ -133,59 +169,102 @@ __global__ __launch_bounds__(TOPK_NT) void topk_kernel(const float* __restrict__
                                                        int64_t n, int K,
                                                        int32_t* __restrict__ ids,
                                                        float* __restrict__ vals) {
-    __shared__ float cv[TOPK_NT * TOPK_MAX];
-    __shared__ int ci[TOPK_NT * TOPK_MAX];
-    __shared__ int head[TOPK_NT];
-    __shared__ float wv[TOPK_NT / 64];
-    __shared__ int wi[TOPK_NT / 64], wl[TOPK_NT / 64];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t s_prefix, s_need;
+    __shared__ uint32_t w_gt[TOPK_NW], w_eq[TOPK_NW];
+    __shared__ float sel_v[TOPK_MAX];
+    __shared__ int sel_i[TOPK_MAX];
     const int64_t r = blockIdx.x;
     const float* row = x + r * ldx;
-    const int t = threadIdx.x;
-    float lv[TOPK_MAX];
-    int li[TOPK_MAX];
-    int cnt = 0;
-    for (int64_t j = t; j < n; j += TOPK_NT) {
-        const float v = row[j];
-        const int idx = (int)j;
-        if (v != v) continue;                          // NaN never selected
-        if (cnt == K && !better(v, idx, lv[K - 1], li[K - 1])) continue;
-        // insertion into the lane's sorted list (indices arrive ascending)
-        int p = (cnt < K) ? cnt++ : K - 1;
-        while (p > 0 && better(v, idx, lv[p - 1], li[p - 1])) {
-            lv[p] = lv[p - 1]; li[p] = li[p - 1]; --p;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+
+    // ---- 1. radix select of the K-th largest key
+    uint32_t prefix = 0u, mask = 0u, need = (uint32_t)K;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (t < 256) hist[t] = 0u;
+        __syncthreads();
+        for (int64_t j = t; j < n; j += TOPK_NT) {
+            const uint32_t key = order_key(row[j]);
+            if (key != 0u && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
         }
-        lv[p] = v; li[p] = idx;
-    }
-    for (int k = 0; k < K; ++k) {
-        cv[t * TOPK_MAX + k] = k < cnt ? lv[k] : -INFINITY;
-        ci[t * TOPK_MAX + k] = k < cnt ? li[k] : 0x7fffffff;
-    }
-    head[t] = 0;
-    __syncthreads();
-    for (int k = 0; k < K; ++k) {
-        // best head among the lanes' lists
-        const int hd = head[t];
-        float v = hd < K ? cv[t * TOPK_MAX + hd] : -INFINITY;
-        int i = hd < K ? ci[t * TOPK_MAX + hd] : 0x7fffffff;
-        int lane_of = t;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(v, off);
-            const int oi = __shfl_xor(i, off);
-            const int ol = __shfl_xor(lane_of, off);
-            if (better(ov, oi, v, i)) { v = ov; i = oi; lane_of = ol; }
-        }
-        if ((t & 63) == 0) { wv[t >> 6] = v; wi[t >> 6] = i; wl[t >> 6] = lane_of; }
         __syncthreads();
         if (t == 0) {
-            float bv = wv[0]; int bi = wi[0], bl = wl[0];
-            for (int w = 1; w < TOPK_NT / 64; ++w)
-                if (better(wv[w], wi[w], bv, bi)) { bv = wv[w]; bi = wi[w]; bl = wl[w]; }
-            ids[r * K + k] = bi == 0x7fffffff ? -1 : bi;
-            vals[r * K + k] = bv;
-            head[bl] += 1;
+            uint32_t cum = 0u, chosen = 0u, nd = need;
+            bool found = false;
+            for (int bkt = 255; bkt >= 0; --bkt) {
+                const uint32_t h = hist[bkt];
+                if (cum + h >= need) { chosen = (uint32_t)bkt; nd = need - cum; found = true; break; }
+                cum += h;
+            }
+            // fewer than `need` candidates left: every valid entry is selected
+            s_prefix = found ? (prefix | (chosen << shift)) : 0xffffffffu;
+            s_need = found ? nd : 0u;
         }
         __syncthreads();
+        if (s_prefix == 0xffffffffu) { prefix = 0u; need = 0u; break; }
+        prefix = s_prefix;
+        need = s_need;
+        mask |= 255u << shift;
+    }
+    // T = prefix (key of the K-th entry) unless fewer than K valid entries exist
+    const bool short_row = (need == 0u);
+    const uint32_t T = short_row ? 1u : prefix;          // short row: take every key >= 1
+    const uint32_t n_eq_take = short_row ? (uint32_t)K : need;
+
+    // ---- 2. collect winners in index order
+    uint32_t run_gt = 0u, run_eq = 0u;
+    const uint32_t base_eq_slot = short_row ? 0u : (uint32_t)K - need;
+    if (t < TOPK_MAX) { sel_v[t] = -INFINITY; sel_i[t] = -1; }
+    __syncthreads();
+    for (int64_t j0 = 0; j0 < n; j0 += TOPK_NT) {
+        const int64_t j = j0 + t;
+        const uint32_t key = j < n ? order_key(row[j]) : 0u;
+        const bool gt = !short_row && key > T;
+        const bool eq = short_row ? key >= T : key == T;
+        const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        if (lane == 0) { w_gt[wave] = __popcll(bgt); w_eq[wave] = __popcll(beq); }
+        __syncthreads();
+        uint32_t off_gt = run_gt, off_eq = run_eq, tot_gt = 0u, tot_eq = 0u;
+        for (int w = 0; w < TOPK_NW; ++w) {
+            if (w < wave) { off_gt += w_gt[w]; off_eq += w_eq[w]; }
+            tot_gt += w_gt[w]; tot_eq += w_eq[w];
+        }
+        if (gt) {
+            const uint32_t slot = off_gt + __popcll(bgt & below);
+            if (slot < TOPK_MAX) { sel_v[slot] = row[j]; sel_i[slot] = (int)j; }
+        }
+        if (eq) {
+            const uint32_t k = off_eq + __popcll(beq & below);
+            if (k < n_eq_take && base_eq_slot + k < TOPK_MAX) {
+                sel_v[base_eq_slot + k] = row[j];
+                sel_i[base_eq_slot + k] = (int)j;
+            }
+        }
+        run_gt += tot_gt;
+        run_eq += tot_eq;
+        __syncthreads();
+    }
+
+    // ---- 3. order the winners
+    if (t == 0) {
+        float v[TOPK_MAX];
+        int id[TOPK_MAX];
+        for (int k = 0; k < K; ++k) { v[k] = sel_v[k]; id[k] = sel_i[k]; }
+        // insertion sort; a missing entry (id -1) sorts after every real one
+        for (int a = 1; a < K; ++a) {
+            const float va = v[a];
+            const int ia = id[a];
+            int b = a;
+            while (b > 0 && ia >= 0 && (id[b - 1] < 0 || better(va, ia, v[b - 1], id[b - 1]))) {
+                v[b] = v[b - 1]; id[b] = id[b - 1]; --b;
+            }
+            v[b] = va; id[b] = ia;
+        }
+        for (int k = 0; k < K; ++k) {
+            ids[r * K + k] = id[k];
+            vals[r * K + k] = id[k] < 0 ? -INFINITY : v[k];
+        }
     }
 }
 
@@ -213,7 +292,7 @@ hipError_t launch_rope_kv(const void* qkv, int64_t ld, const int32_t* tok_seq,
 hipError_t launch_swiglu(const void* gu, int64_t ld, int64_t T, int F, void* out, int64_t ldo,
                          hipStream_t s) {
     if (T == 0 || F == 0) return hipSuccess;
-    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((F + 255) / 256), (unsigned)T), dim3(256), 0,
+    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((F + 2047) / 2048), (unsigned)T), dim3(256), 0,
                        s, (const bf16_t*)gu, ld, F, (bf16_t*)out, ldo);
     return hipGetLastError();
 }
@@ -221,7 +300,7 @@ hipError_t launch_swiglu(const void* gu, int64_t ld, int64_t T, int F, void* out
 hipError_t launch_add(float* h, int64_t ldh, const void* x, int64_t ldx, int64_t T, int H,
                       hipStream_t s) {
     if (T == 0 || H == 0) return hipSuccess;
-    hipLaunchKernelGGL(add_kernel, dim3((unsigned)((H + 255) / 256), (unsigned)T), dim3(256), 0, s,
+    hipLaunchKernelGGL(add_kernel, dim3((unsigned)((H + 1023) / 1024), (unsigned)T), dim3(256), 0, s,
                        h, ldh, (const bf16_t*)x, ldx, H);
     return hipGetLastError();
 }

@@ -59,3 +59,23 @@ def test_prefill_sampled_rows(workload):
     rows = [0, 1, 255, 256, 2047, 4095]
     ref = oracle.attention(f64(w["pf_q"][rows]), rows, f64(k), f64(v), w["scale"])
     assert row_rel_err(f64(outs["pf_out"][rows]), ref).max() <= TOL_BF16
+
+
+def test_glue_leg_sampled(workload):
+    # the decoder-glue leg as bench.py runs it: RoPE'd queries, SwiGLU rows and
+    # the top-20 selection against the fp64 pieces; the gathered rows are exact
+    from oracle import decoder as od
+    w, _ = workload
+    rows = [0, 1000, 4095]
+    x = f64(w["qkv"][rows])
+    q_ref = od.rope(x[:, :bench.HQ * bench.HD].reshape(3, bench.HQ, bench.HD), rows, bench.THETA)
+    assert row_rel_err(f64(w["rope_q"][rows]), q_ref).max() <= TOL_BF16
+    g = f64(w["gu"][rows])
+    s_ref = od.silu(g[:, :bench.FFN]) * g[:, bench.FFN:]
+    assert row_rel_err(f64(w["swi"][rows]), s_ref).max() <= TOL_BF16
+    import invariant_deterministic_fixed_amd as binv
+    ids, _ = binv.topk(w["logits"], 20)
+    lg = w["logits"].cpu().numpy()
+    for r in [0, 255]:
+        np.testing.assert_array_equal(ids[r].cpu().numpy(), od.topk(lg[r], 20)[0])
+    assert_bitwise_equal(w["hl"], w["h"][w["rows"].long()], "gathered rows")
