@@ -52,8 +52,9 @@ namespace {
 using namespace attn;
 
 // Grid: x = (query tile, KV head), y = chunk, z = sequence; workgroups of
-// chunks past a tile's last position exit at once.
-template <int D, int G>
+// chunks past a tile's last position exit at once.  R = row tiles of 16 rows
+// per workgroup (1 for decode, 2 for prefill at D = 128).
+template <int D, int G, int R>
 __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chunk_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
@@ -61,28 +62,32 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     const int32_t* __restrict__ kv_lens, float* __restrict__ ws_o,
     float2* __restrict__ ws_ml, int Hq, int Hkv, int n_chunks, int max_kv_len,
     float scale_log2) {
-    __shared__ ChunkLds<D> sh;
+    constexpr bool VL = (R == 1);           // V through LDS for single-tile (decode) workgroups
+    __shared__ ChunkLds<D, R, VL> sh;
     constexpr int JT = ChunkShape<D>::JT;
     const int c = blockIdx.y;
-    const TileCtx x = tile_ctx<G>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q, kv_lens,
-                                  pt_stride, max_kv_len);
+    const TileCtx x = tile_ctx<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
+                                     kv_lens, pt_stride, max_kv_len);
     if (x.pos_max < c * CHUNK) return;     // no row of the tile reaches this chunk
     int phys[JT];
     load_phys<D>(x, c, page_table, pt_stride, phys);
-    const ChunkOut r = chunk_compute<D, G>(x, c, phys, q, kc, vc, pt_stride, Hq, Hkv,
-                                           scale_log2, sh);
+    const ChunkOut<R> r = chunk_compute<D, G, R, VL>(x, c, phys, page_table, q, kc, vc,
+                                                     pt_stride, Hq, Hkv, scale_log2, sh);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, ag = lane >> 4;
     const int j0 = c * CHUNK;
     // partials of the rows that see at least one key of this chunk
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const RowInfo ri = row_info<G>(4 * ag + e, x.b, x.g, x.qt, x.q_len, x.q_start, x.kv_len);
-        if (ri.token < 0 || ri.pos < j0) continue;
-        const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)n_chunks + c;
-        ws_o[slot * D + 16 * wave + (lane & 15)] = r.o[e];
-    }
-    if (t < 256 && (t & 15) == 0) {
-        const RowInfo ri = row_info<G>(t >> 4, x.b, x.g, x.qt, x.q_len, x.q_start, x.kv_len);
+    for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const RowInfo ri = row_info<G, R>(16 * rt + 4 * ag + e, x.b, x.g, x.qt, x.q_len,
+                                              x.q_start, x.kv_len);
+            if (ri.token < 0 || ri.pos < j0) continue;
+            const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)n_chunks + c;
+            ws_o[slot * D + 16 * wave + (lane & 15)] = r.o[rt][e];
+        }
+    if (t < 256 * R && (t & 15) == 0) {
+        const RowInfo ri = row_info<G, R>(t >> 4, x.b, x.g, x.qt, x.q_len, x.q_start, x.kv_len);
         if (ri.token >= 0 && ri.pos >= j0) {
             const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)n_chunks + c;
             ws_ml[slot] = make_float2(r.ml_m, r.l);
@@ -193,26 +198,35 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
     }
 }
 
-template <int D, int G>
-hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
-    constexpr int TQ = ROWS / G;
+template <int D, int G, int R>
+hipError_t launch_dgr(const AttnArgs& a, hipStream_t s) {
+    constexpr int TQ = ROWS * R / G;
     const int n_chunks = (int)((a.max_kv_len + CHUNK - 1) / CHUNK);
     const int64_t nqt = a.cu_q ? (a.max_q_len + TQ - 1) / TQ : 1;
-    const int64_t R = a.n_tokens * a.Hq;
+    const int64_t Rows = a.n_tokens * a.Hq;
     float* ws_o = a.ws;
-    float2* ws_ml = reinterpret_cast<float2*>(a.ws + R * n_chunks * a.D);
+    float2* ws_ml = reinterpret_cast<float2*>(a.ws + Rows * n_chunks * a.D);
     dim3 grid1((unsigned)(nqt * a.Hkv), (unsigned)n_chunks, (unsigned)a.B);
-    hipLaunchKernelGGL((attn_chunk_kernel<D, G>), grid1, dim3(ChunkShape<D>::NTH), 0, s, (const bf16_t*)a.q,
-                       a.cu_q, (const bf16_t*)a.k_cache, (const bf16_t*)a.v_cache, a.page_table,
-                       a.pt_stride, a.kv_lens, ws_o, ws_ml, a.Hq, a.Hkv, n_chunks,
-                       (int)a.max_kv_len, a.scale_log2);
+    hipLaunchKernelGGL((attn_chunk_kernel<D, G, R>), grid1, dim3(ChunkShape<D>::NTH), 0, s,
+                       (const bf16_t*)a.q, a.cu_q, (const bf16_t*)a.k_cache,
+                       (const bf16_t*)a.v_cache, a.page_table, a.pt_stride, a.kv_lens, ws_o,
+                       ws_ml, a.Hq, a.Hkv, n_chunks, (int)a.max_kv_len, a.scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid2((unsigned)((R + 3) / 4));
+    dim3 grid2((unsigned)((Rows + 3) / 4));
     hipLaunchKernelGGL((attn_merge_kernel<D>), grid2, dim3(NT), 0, s, a.cu_q, a.kv_lens, a.B,
                        a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len, (const float*)ws_o,
                        (const float2*)ws_ml, (bf16_t*)a.out);
     return hipGetLastError();
+}
+
+// decode: one token per sequence, one row tile; prefill: two row tiles at D = 128
+template <int D, int G>
+hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
+    if constexpr (D == 128) {
+        if (a.cu_q) return launch_dgr<D, G, 2>(a, s);
+    }
+    return launch_dgr<D, G, 1>(a, s);
 }
 
 template <int D>

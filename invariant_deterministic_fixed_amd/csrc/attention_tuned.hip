@@ -43,9 +43,9 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_spl
     const int32_t* __restrict__ page_table, int64_t pt_stride, const int32_t* __restrict__ kv_lens,
     float* __restrict__ ws_o, float2* __restrict__ ws_ml, int Hq, int Hkv, int s_target,
     int s_max, int max_kv_len, float scale_log2) {
-    __shared__ ChunkLds<D> sh;
+    __shared__ ChunkLds<D, 1, true> sh;
     const int s = blockIdx.y;
-    const TileCtx x = tile_ctx<G>(blockIdx.z, blockIdx.x, 0, nullptr, kv_lens, pt_stride, max_kv_len);
+    const TileCtx x = tile_ctx<G, 1>(blockIdx.z, blockIdx.x, 0, nullptr, kv_lens, pt_stride, max_kv_len);
     if (x.pos_max < 0) return;
     const int n = x.pos_max / CHUNK + 1;
     int c0, c1;
@@ -60,15 +60,15 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_spl
         __syncthreads();                           // LDS of the previous chunk is free
         int phys[ChunkShape<D>::JT];
         load_phys<D>(x, c, page_table, pt_stride, phys);
-        const ChunkOut r = chunk_compute<D, G>(x, c, phys, q, kc, vc, pt_stride, Hq, Hkv,
-                                               scale_log2, sh);
+        const ChunkOut<1> r = chunk_compute<D, G, 1, true>(x, c, phys, page_table, q, kc, vc,
+                                                           pt_stride, Hq, Hkv, scale_log2, sh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if (r.m[e] == -INFINITY) continue;
-            const float mn = fmaxf(M[e], r.m[e]);
+            if (r.m[0][e] == -INFINITY) continue;
+            const float mn = fmaxf(M[e], r.m[0][e]);
             const float fa = (M[e] == -INFINITY) ? 0.0f : exp2f(M[e] - mn);
-            const float fb = exp2f(r.m[e] - mn);
-            O[e] = fa * O[e] + fb * r.o[e];
+            const float fb = exp2f(r.m[0][e] - mn);
+            O[e] = fa * O[e] + fb * r.o[0][e];
             M[e] = mn;
         }
         if (t < 256 && (t & 15) == 0 && r.ml_m != -INFINITY) {
@@ -80,13 +80,13 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_spl
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const RowInfo ri = row_info<G>(4 * ag + e, x.b, x.g, 0, x.q_len, x.q_start, x.kv_len);
+        const RowInfo ri = row_info<G, 1>(4 * ag + e, x.b, x.g, 0, x.q_len, x.q_start, x.kv_len);
         if (ri.token < 0) continue;
         const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)s_max + s;
         ws_o[slot * D + 16 * wave + (lane & 15)] = O[e];
     }
     if (t < 256 && (t & 15) == 0) {
-        const RowInfo ri = row_info<G>(t >> 4, x.b, x.g, 0, x.q_len, x.q_start, x.kv_len);
+        const RowInfo ri = row_info<G, 1>(t >> 4, x.b, x.g, 0, x.q_len, x.q_start, x.kv_len);
         if (ri.token >= 0) {
             const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)s_max + s;
             ws_ml[slot] = make_float2(MR, L);

@@ -2,24 +2,29 @@
 // decode / prefill kernels (attention.hip) and the shape-tuned comparator
 // (attention_tuned.hip).  Sharing it is what makes a row's partial for a
 // chunk the same bits on every path.
+//
+// A workgroup handles R tiles of 16 query rows (R = 1 for decode, 2 for
+// prefill) against one 256-key chunk.  Nothing a row computes depends on R or
+// on the row's slot: the q.k and p.v products are per-element MFMA chains over
+// fixed k-blocks, the max is exact, and l is summed in one fixed order; R only
+// decides how many rows share one load of the chunk's K and V.
 #pragma once
 #include "common.hpp"
 
 namespace binv {
 namespace attn {
 
-
 constexpr int CHUNK = 256;
 constexpr int PAGE = 16;
 constexpr int NT = 256;
-constexpr int ROWS = 16;
+constexpr int ROWS = 16;           // rows of one MFMA row tile
 constexpr int STACK = 10;          // binary counter slots: enough for 1023 leaves
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// P tile in LDS: [16 rows][256 keys] bf16, rows of 512 bytes = 32 chunks of 16
-// bytes; chunk ch of row r is stored at position ch ^ r.
-__device__ __forceinline__ int p_off(int r, int ch) { return (r << 9) + ((ch ^ r) << 4); }
+// P tile in LDS: [16 R rows][256 keys] bf16, rows of 512 bytes = 32 chunks of
+// 16 bytes; chunk ch of row r is stored at position ch ^ (r & 31).
+__device__ __forceinline__ int p_off(int r, int ch) { return (r << 9) + ((ch ^ (r & 31)) << 4); }
 
 struct RowInfo {
     int64_t token;   // global query-token index (row of q / out / partials), -1 if padding
@@ -27,11 +32,12 @@ struct RowInfo {
     int pos;         // absolute position of the query
 };
 
-// Row slot r of tile `qt` of sequence b:  token (r / G) of the tile, head g*G + r % G.
-template <int G>
+// Row slot r (0 .. 16R-1) of tile `qt` of sequence b: token r / G of the tile,
+// head g*G + r % G; a tile holds 16R/G consecutive new tokens.
+template <int G, int R>
 __device__ __forceinline__ RowInfo row_info(int r, int b, int g, int qt, int q_len,
                                             int64_t q_start, int kv_len) {
-    constexpr int TQ = ROWS / G;
+    constexpr int TQ = ROWS * R / G;
     RowInfo ri;
     const int tq = r / G;
     const int i = qt * TQ + tq;                    // index among the sequence's new tokens
@@ -67,11 +73,11 @@ struct TileCtx {
     int n_pages;
 };
 
-template <int G>
+template <int G, int R>
 __device__ __forceinline__ TileCtx tile_ctx(int b, int g, int qt, const int32_t* cu_q,
                                             const int32_t* kv_lens, int64_t pt_stride,
                                             int max_kv_len) {
-    constexpr int TQ = ROWS / G;
+    constexpr int TQ = ROWS * R / G;
     TileCtx x;
     x.b = b; x.g = g; x.qt = qt;
     x.kv_len = min(kv_lens[b], max_kv_len);
@@ -90,32 +96,30 @@ __device__ __forceinline__ TileCtx tile_ctx(int b, int g, int qt, const int32_t*
     return x;
 }
 
-template <int D>
+template <int D, int R, bool VL>
 struct ChunkLds {
-    // the chunk's 16 V page blocks of this KV head, [page][D][16 slots] bf16,
-    // copied HBM -> LDS by global_load_lds (one 1 KB piece per instruction)
-    __attribute__((aligned(1024))) char v[16 * D * PAGE * 2];
-    __attribute__((aligned(16))) char p[ROWS * CHUNK * 2];
-    float red_max[ChunkShape<D>::NW][ROWS];
-    int row_pos[ROWS];
+    // with VL: the chunk's 16 V page blocks of this KV head, [page][D][16 slots]
+    // bf16, copied HBM -> LDS by global_load_lds (one 1 KB piece per instruction)
+    __attribute__((aligned(1024))) char v[VL ? 16 * D * PAGE * 2 : 16];
+    __attribute__((aligned(16))) char p[ROWS * R * CHUNK * 2];
+    float red_max[ChunkShape<D>::NW][ROWS * R];
+    int row_pos[ROWS * R];
 };
 
-// Result of one chunk for the workgroup's 16 rows:
-//   m[e]  max of row 4*(lane>>4)+e (every lane), -inf if the row sees no key
-//   o     p.v of those rows for features 16*wave + (lane&15)
-//   l     (threads t < 256 with t % 16 == 0) sum of p of row t >> 4, and
-//   ml_m  that row's max
+// Result of one chunk for the workgroup's 16R rows:
+//   m[rt][e]  max of row 16 rt + 4*(lane>>4) + e (every lane), -inf if the row
+//             sees no key
+//   o[rt]     p.v of those rows for features 16*wave + (lane&15)
+//   l, ml_m   (threads t < 256R with t % 16 == 0) sum of p and max of row t >> 4
+template <int R>
 struct ChunkOut {
-    float m[4];
-    f32x4 o;
+    float m[R][4];
+    f32x4 o[R];
     float l, ml_m;
 };
 
-// The per-chunk arithmetic shared by decode, prefill and the comparator: keys
-// [256c, 256c+256) of the tile's sequence, each row limited to keys <= its
-// position.  LDS may be reused only after a __syncthreads().
 // Page-table entries of the JT pages this wave reads in chunk c (independent
-// of kv_len, so they can be fetched a chunk ahead); 0 past the table's row.
+// of kv_len, so they can be fetched up front); 0 past the table's row.
 template <int D>
 __device__ __forceinline__ void load_phys(const TileCtx& x, int c,
                                           const int32_t* __restrict__ page_table,
@@ -129,14 +133,22 @@ __device__ __forceinline__ void load_phys(const TileCtx& x, int c,
     }
 }
 
-template <int D, int G>
-__device__ __forceinline__ ChunkOut chunk_compute(
+// The per-chunk arithmetic shared by decode, prefill and the comparator: keys
+// [256c, 256c+256) of the tile's sequence, each row limited to keys <= its
+// position.  LDS may be reused only after a __syncthreads().
+// VL: V reaches the matrix cores through LDS (copied while q.k runs; decode)
+// or straight from memory into registers after q.k (prefill, where 16R rows
+// share each V fragment and LDS is better spent on more workgroups per CU).
+// Either way every lane feeds the same V values into the same p.v chain.
+template <int D, int G, int R, bool VL>
+__device__ __forceinline__ ChunkOut<R> chunk_compute(
     const TileCtx& x, int c, const int (&phys_in)[ChunkShape<D>::JT],
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
-    const bf16_t* __restrict__ vc, int64_t pt_stride,
-    int Hq, int Hkv, float scale_log2, ChunkLds<D>& sh) {
+    const int32_t* __restrict__ page_table, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, int64_t pt_stride,
+    int Hq, int Hkv, float scale_log2, ChunkLds<D, R, VL>& sh) {
     using S = ChunkShape<D>;
     constexpr int NW = S::NW, JT = S::JT, KS = S::KS;
+    static_assert(S::NTH >= 256 * R, "one thread per (row, 16-key segment) for l");
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int ar = lane & 15, ag = lane >> 4;
     const int j0 = c * CHUNK;
@@ -156,16 +168,18 @@ __device__ __forceinline__ ChunkOut chunk_compute(
     // ---- V page blocks of the same JT pages -> LDS (4 KB at D = 128, 2 KB at
     // D = 64, 1 KB per instruction).  Pages past the sequence end copy page 0
     // of the cache; all their slots are >= kv_len and are zeroed when read.
+    if constexpr (VL) {
 #pragma unroll
-    for (int u = 0; u < JT; ++u) {
-        const int pl = JT * wave + u;                          // page within the chunk
-        const char* src = reinterpret_cast<const char*>(vc + (phys[u] * Hkv + g) * (D * PAGE));
+        for (int u = 0; u < JT; ++u) {
+            const int pl = JT * wave + u;                      // page within the chunk
+            const char* src = reinterpret_cast<const char*>(vc + (phys[u] * Hkv + g) * (D * PAGE));
 #pragma unroll
-        for (int part = 0; part < D * PAGE * 2 / 1024; ++part)
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(src + part * 1024 + 16 * lane),
-                (__attribute__((address_space(3))) void*)(sh.v + pl * (D * PAGE * 2) + part * 1024),
-                16, 0, 0);
+            for (int part = 0; part < D * PAGE * 2 / 1024; ++part)
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(src + part * 1024 + 16 * lane),
+                    (__attribute__((address_space(3))) void*)(sh.v + pl * (D * PAGE * 2) + part * 1024),
+                    16, 0, 0);
+        }
     }
 
     // ---- K fragments (B operand of q.k): page 16c + JT*wave + u, key slot lane&15,
@@ -179,82 +193,108 @@ __device__ __forceinline__ ChunkOut chunk_compute(
             kf[u][ks] = page_ok[u] ? ld16(kp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
     }
 
-    // ---- Q fragments (A operand): row lane&15, features 32ks + 8(lane>>4) .. +8
-    const RowInfo a_row = row_info<G>(ar, x.b, g, x.qt, x.q_len, x.q_start, kv_len);
-    u32x4 qf[KS];
+    // ---- Q fragments (A operand) of each row tile: row 16 rt + (lane&15),
+    // features 32ks + 8(lane>>4) .. +8
+    u32x4 qf[R][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        qf[ks] = u32x4{0u, 0u, 0u, 0u};
-        if (a_row.token >= 0)
-            qf[ks] = ld16(q + (a_row.token * Hq + a_row.head) * D + 32 * ks + 8 * ag);
+    for (int rt = 0; rt < R; ++rt) {
+        const RowInfo a_row = row_info<G, R>(16 * rt + ar, x.b, g, x.qt, x.q_len, x.q_start, kv_len);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
+            if (a_row.token >= 0)
+                qf[rt][ks] = ld16(q + (a_row.token * Hq + a_row.head) * D + 32 * ks + 8 * ag);
+        }
     }
-    if (t < ROWS) sh.row_pos[t] = row_info<G>(t, x.b, g, x.qt, x.q_len, x.q_start, kv_len).pos;
+    if (t < ROWS * R) sh.row_pos[t] = row_info<G, R>(t, x.b, g, x.qt, x.q_len, x.q_start, kv_len).pos;
 
     // ---- S = Q K^T on the matrix cores
-    f32x4 s[JT];
+    f32x4 s[R][JT];
 #pragma unroll
-    for (int u = 0; u < JT; ++u) {
-        s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s[u] = mfma16x16x32(qf[ks], kf[u][ks], s[u]);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's V copies have landed
-    __syncthreads();   // row_pos and every wave's V pages visible
-
-    // lane holds rows 4*(lane>>4)+e, key j0 + 16*(JT*wave + u) + (lane&15)
-    const int key_lane = j0 + 16 * JT * wave + (lane & 15);
-    ChunkOut r;
-    int rpos[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) rpos[e] = sh.row_pos[4 * ag + e];
-    float mx[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        mx[e] = -INFINITY;
+    for (int rt = 0; rt < R; ++rt)
 #pragma unroll
         for (int u = 0; u < JT; ++u) {
-            const bool valid = key_lane + 16 * u <= rpos[e];
-            const float v = valid ? s[u][e] * scale_log2 : -INFINITY;
-            s[u][e] = v;
-            mx[e] = fmaxf(mx[e], v);
+            s[rt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) s[rt][u] = mfma16x16x32(qf[rt][ks], kf[u][ks], s[rt][u]);
         }
+    // ---- without VL: V fragments straight into registers, issued once the
+    // q.k products are queued: feature d = 16 wave + (lane&15), keys
+    // 32ks + 8(lane>>4) .. +8 = page 16c + 2ks + (ag>>1), slots 8(ag&1) .. +8
+    u32x4 vreg[VL ? 1 : 8];
+    if constexpr (!VL) {
+        const int d = 16 * wave + (lane & 15);
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], off));
+        for (int ks = 0; ks < 8; ++ks) {
+            const int pidx = 16 * c + 2 * ks + (ag >> 1);
+            const bool ok = pidx < x.n_pages && pidx < pt_stride;
+            const int64_t ph = ok ? (int64_t)page_table[x.pt_row + pidx] : 0;
+            vreg[ks] = ok ? ld16(vc + ((ph * Hkv + g) * D + d) * PAGE + 8 * (ag & 1))
+                          : u32x4{0u, 0u, 0u, 0u};
+        }
     }
-    if ((lane & 15) == 0) {
+    if constexpr (VL) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // V copies landed
+    __syncthreads();   // row_pos (and with VL every wave's V pages) visible
+
+    // lane holds rows 16 rt + 4*(lane>>4) + e, key j0 + 16*(JT*wave + u) + (lane&15)
+    const int key_lane = j0 + 16 * JT * wave + (lane & 15);
+    ChunkOut<R> r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sh.red_max[wave][4 * ag + e] = mx[e];
+    for (int rt = 0; rt < R; ++rt) {
+        float mx[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int rpos = sh.row_pos[16 * rt + 4 * ag + e];
+            mx[e] = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < JT; ++u) {
+                const bool valid = key_lane + 16 * u <= rpos;
+                const float v = valid ? s[rt][u][e] * scale_log2 : -INFINITY;
+                s[rt][u][e] = v;
+                mx[e] = fmaxf(mx[e], v);
+            }
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], off));
+        }
+        if ((lane & 15) == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sh.red_max[wave][16 * rt + 4 * ag + e] = mx[e];
+        }
     }
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int row = 4 * ag + e;
-        float mm = sh.red_max[0][row];
+    for (int rt = 0; rt < R; ++rt)
 #pragma unroll
-        for (int w = 1; w < NW; ++w) mm = fmaxf(mm, sh.red_max[w][row]);
-        r.m[e] = mm;
-    }
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * rt + 4 * ag + e;
+            float mm = sh.red_max[0][row];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) mm = fmaxf(mm, sh.red_max[w][row]);
+            r.m[rt][e] = mm;
+        }
 
     // ---- P = bf16(exp2(s - m)) into LDS
 #pragma unroll
-    for (int u = 0; u < JT; ++u) {
-        const int key = 16 * (JT * wave + u) + (lane & 15);       // key within the chunk
+    for (int rt = 0; rt < R; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float v = s[u][e];
-            const float p = (v == -INFINITY) ? 0.0f : exp2f(v - r.m[e]);
-            const int row = 4 * ag + e;
-            *reinterpret_cast<bf16_t*>(sh.p + p_off(row, key >> 3) + 2 * (key & 7)) =
-                (bf16_t)f32_to_bf16(p);
+        for (int u = 0; u < JT; ++u) {
+            const int key = 16 * (JT * wave + u) + (lane & 15);       // key within the chunk
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = s[rt][u][e];
+                const float p = (v == -INFINITY) ? 0.0f : exp2f(v - r.m[rt][e]);
+                const int row = 16 * rt + 4 * ag + e;
+                *reinterpret_cast<bf16_t*>(sh.p + p_off(row, key >> 3) + 2 * (key & 7)) =
+                    (bf16_t)f32_to_bf16(p);
+            }
         }
-    }
     __syncthreads();
 
-    // ---- l (threads 0..255): thread t sums keys 16(t&15) .. +15 of row t>>4 in
-    // key order, then a 4-level xor butterfly over the 16 segment sums of the row
+    // ---- l (threads 0 .. 256R-1): thread t sums keys 16(t&15) .. +15 of row t>>4
+    // in key order, then a 4-level xor butterfly over the 16 segment sums of the row
     r.l = 0.0f;
     r.ml_m = -INFINITY;
-    if (t < 256) {
+    if (t < 256 * R) {
         const int row = t >> 4, seg = t & 15;
         const u32x4 p0 = *reinterpret_cast<const u32x4*>(sh.p + p_off(row, 2 * seg));
         const u32x4 p1 = *reinterpret_cast<const u32x4*>(sh.p + p_off(row, 2 * seg + 1));
@@ -275,21 +315,29 @@ __device__ __forceinline__ ChunkOut chunk_compute(
     // ---- O = P V on the matrix cores, keys ascending; wave owns features 16 wave ..
     // V fragment: feature d = 16 wave + (lane&15), keys 32ks + 8(lane>>4) .. +8,
     // i.e. page 2ks + (ag>>1) of the chunk, slots 8(ag&1) .. +8; slots at or
-    // past kv_len read as 0
-    r.o = f32x4{0.f, 0.f, 0.f, 0.f};
+    // past kv_len read as 0.  Each V fragment serves all R row tiles.
+#pragma unroll
+    for (int rt = 0; rt < R; ++rt) r.o[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
         const int d = 16 * wave + (lane & 15);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const int pl = 2 * ks + (ag >> 1);
-            u32x4 v = *reinterpret_cast<const u32x4*>(sh.v + pl * (D * PAGE * 2) + d * (PAGE * 2) + 16 * (ag & 1));
+            u32x4 v;
+            if constexpr (VL)
+                v = *reinterpret_cast<const u32x4*>(sh.v + pl * (D * PAGE * 2) + d * (PAGE * 2) + 16 * (ag & 1));
+            else
+                v = vreg[ks];
             const int nvalid = kv_len - ((16 * c + pl) * PAGE + 8 * (ag & 1));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (2 * i + 1 >= nvalid) v[i] &= (2 * i < nvalid) ? 0x0000ffffu : 0u;
             }
-            const u32x4 pa = *reinterpret_cast<const u32x4*>(sh.p + p_off(ar, 4 * ks + ag));
-            r.o = mfma16x16x32(pa, v, r.o);
+#pragma unroll
+            for (int rt = 0; rt < R; ++rt) {
+                const u32x4 pa = *reinterpret_cast<const u32x4*>(sh.p + p_off(16 * rt + ar, 4 * ks + ag));
+                r.o[rt] = mfma16x16x32(pa, v, r.o[rt]);
+            }
         }
     }
     return r;
