@@ -12,7 +12,9 @@ One step = one pass of every hot-path kernel over one batch of synthetic input:
                   4096-token fused q/k/v projection [4096, 6144], SwiGLU on a
                   [4096, 2 x 14336] gate/up block, row gather and exact top-20
                   of 256 rows of 128256 fp32 logits
-Inputs are resident in HBM before the timed region.  Each leg is bracketed by
+Inputs are resident in HBM before the timed region.  The GPU's clocks ramp up
+over the first second or so of sustained load, so before the W warmup steps
+the step is run untimed for --ramp-seconds (default 1 s).  Each leg is bracketed by
 HIP events recorded on the stream the kernels are launched on (torch's current
 stream).  The decode leg streams ~6 GB of KV, far more than the 256 MB
 last-level cache, so every leg starts from a cache the other legs have
@@ -23,7 +25,7 @@ the decode-attention GB/s (algorithmic bytes: K, V, q, out, page table) is
 reported beside it with its own roofline.  `cpu_baseline` times the fp64
 oracle on a bounded sample of the same workload on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--ramp-seconds S] [--no-cpu-baseline]
        [--profile-copy]   (adds one 1 GiB device copy, the calibration kernel
                            for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
 """
@@ -246,6 +248,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--ramp-seconds", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-copy", action="store_true")
     args = ap.parse_args()
@@ -262,6 +265,10 @@ def main():
     work = algorithmic(w)
     torch.cuda.synchronize()
 
+    t_ramp = time.perf_counter()
+    while time.perf_counter() - t_ramp < args.ramp_seconds:   # clock ramp, untimed
+        run_step(w)
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         run_step(w)
     torch.cuda.synchronize()

@@ -51,10 +51,15 @@ namespace binv {
 namespace {
 using namespace attn;
 
-// Grid: x = (query tile, KV head), y = chunk, z = sequence; workgroups of
-// chunks past a tile's last position exit at once.  R = row tiles of 16 rows
-// per workgroup (1 for decode, 2 for prefill at D = 128).
-template <int D, int G, int R>
+// Grid: x = (query tile, KV head), y = chunk lane, z = sequence.  With LOOP,
+// workgroup (x, y, z) takes the chunks c = y, y + gridDim.y, ... that reach
+// the tile's last position, so a grid sized for the longest allowed sequence
+// does not spend one workgroup launch per chunk slot of every short
+// sequence; without it, gridDim.y is the chunk count and the workgroup takes
+// chunk y alone.  Which workgroup takes a chunk does not enter the chunk's
+// arithmetic.  R = row tiles of 16 rows per workgroup (1 for decode, 2 for
+// prefill at D = 128).
+template <int D, int G, int R, bool LOOP>
 __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chunk_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
@@ -65,33 +70,44 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     constexpr bool VL = (R == 1);           // V through LDS for single-tile (decode) workgroups
     __shared__ ChunkLds<D, R, VL> sh;
     constexpr int JT = ChunkShape<D>::JT;
-    const int c = blockIdx.y;
-    const TileCtx x = tile_ctx<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
-                                     kv_lens, pt_stride, max_kv_len);
-    if (x.pos_max < c * CHUNK) return;     // no row of the tile reaches this chunk
-    int phys[JT];
-    load_phys<D>(x, c, page_table, pt_stride, phys);
-    const ChunkOut<R> r = chunk_compute<D, G, R, VL>(x, c, phys, page_table, q, kc, vc,
-                                                     pt_stride, Hq, Hkv, scale_log2, sh);
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, ag = lane >> 4;
-    const int j0 = c * CHUNK;
-    // partials of the rows that see at least one key of this chunk
+    const int pos_max = tile_ctx<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
+                                       kv_lens, pt_stride, max_kv_len).pos_max;
+#pragma clang loop unroll(disable)
+    for (int c = blockIdx.y; c * CHUNK <= pos_max; c += gridDim.y) {
+        // the tile context, q fragments, row maps and lane-derived addresses
+        // are re-derived per chunk (cache hits and a few ALU operations)
+        // rather than held live across chunks, which would spill
+        asm volatile("" ::: "memory");
+        int t = threadIdx.x;
+        if constexpr (LOOP) asm volatile("" : "+v"(t));
+        const int lane = t & 63, wave = t >> 6, ag = lane >> 4;
+        const TileCtx x = tile_ctx<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
+                                         kv_lens, pt_stride, max_kv_len);
+        int phys[JT];
+        load_phys<D>(x, c, page_table, pt_stride, phys, t);
+        const ChunkOut<R> r = chunk_compute<D, G, R, VL>(x, c, phys, page_table, q, kc, vc,
+                                                         pt_stride, Hq, Hkv, scale_log2, sh, t);
+        const int j0 = c * CHUNK;
+        // partials of the rows that see at least one key of this chunk
 #pragma unroll
-    for (int rt = 0; rt < R; ++rt)
+        for (int rt = 0; rt < R; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const RowInfo ri = row_info<G, R>(16 * rt + 4 * ag + e, x.b, x.g, x.qt, x.q_len,
-                                              x.q_start, x.kv_len);
-            if (ri.token < 0 || ri.pos < j0) continue;
-            const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)n_chunks + c;
-            ws_o[slot * D + 16 * wave + (lane & 15)] = r.o[rt][e];
+            for (int e = 0; e < 4; ++e) {
+                const RowInfo ri = row_info<G, R>(16 * rt + 4 * ag + e, x.b, x.g, x.qt, x.q_len,
+                                                  x.q_start, x.kv_len);
+                if (ri.token < 0 || ri.pos < j0) continue;
+                const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)n_chunks + c;
+                ws_o[slot * D + 16 * wave + (lane & 15)] = r.o[rt][e];
+            }
+        if (t < 256 * R && (t & 15) == 0) {
+            const RowInfo ri = row_info<G, R>(t >> 4, x.b, x.g, x.qt, x.q_len, x.q_start, x.kv_len);
+            if (ri.token >= 0 && ri.pos >= j0) {
+                const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)n_chunks + c;
+                ws_ml[slot] = make_float2(r.ml_m, r.l);
+            }
         }
-    if (t < 256 * R && (t & 15) == 0) {
-        const RowInfo ri = row_info<G, R>(t >> 4, x.b, x.g, x.qt, x.q_len, x.q_start, x.kv_len);
-        if (ri.token >= 0 && ri.pos >= j0) {
-            const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)n_chunks + c;
-            ws_ml[slot] = make_float2(r.ml_m, r.l);
-        }
+        if constexpr (!LOOP) break;
+        __syncthreads();                    // LDS free for the next chunk
     }
 }
 
@@ -198,6 +214,10 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
     }
 }
 
+// workgroups per (query tile, KV head) when they loop over chunks: a sequence
+// of n chunks is covered in ceil(n / CHUNK_LANES) rounds
+constexpr int CHUNK_LANES = 16;
+
 template <int D, int G, int R>
 hipError_t launch_dgr(const AttnArgs& a, hipStream_t s) {
     constexpr int TQ = ROWS * R / G;
@@ -206,8 +226,12 @@ hipError_t launch_dgr(const AttnArgs& a, hipStream_t s) {
     const int64_t Rows = a.n_tokens * a.Hq;
     float* ws_o = a.ws;
     float2* ws_ml = reinterpret_cast<float2*>(a.ws + Rows * n_chunks * a.D);
-    dim3 grid1((unsigned)(nqt * a.Hkv), (unsigned)n_chunks, (unsigned)a.B);
-    hipLaunchKernelGGL((attn_chunk_kernel<D, G, R>), grid1, dim3(ChunkShape<D>::NTH), 0, s,
+    // decode workgroups (R = 1) loop over their sequence's chunks; prefill
+    // tiles already fill the machine with one chunk per workgroup
+    constexpr bool LOOP = (R == 1);
+    dim3 grid1((unsigned)(nqt * a.Hkv),
+               (unsigned)(LOOP && n_chunks > CHUNK_LANES ? CHUNK_LANES : n_chunks), (unsigned)a.B);
+    hipLaunchKernelGGL((attn_chunk_kernel<D, G, R, LOOP>), grid1, dim3(ChunkShape<D>::NTH), 0, s,
                        (const bf16_t*)a.q, a.cu_q, (const bf16_t*)a.k_cache,
                        (const bf16_t*)a.v_cache, a.page_table, a.pt_stride, a.kv_lens, ws_o,
                        ws_ml, a.Hq, a.Hkv, n_chunks, (int)a.max_kv_len, a.scale_log2);

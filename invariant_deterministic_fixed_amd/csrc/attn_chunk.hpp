@@ -120,12 +120,14 @@ struct ChunkOut {
 
 // Page-table entries of the JT pages this wave reads in chunk c (independent
 // of kv_len, so they can be fetched up front); 0 past the table's row.
+// t = threadIdx.x, passed in so that a caller looping over chunks can keep
+// the lane-derived arithmetic inside its loop.
 template <int D>
 __device__ __forceinline__ void load_phys(const TileCtx& x, int c,
                                           const int32_t* __restrict__ page_table,
-                                          int64_t pt_stride, int (&phys)[ChunkShape<D>::JT]) {
+                                          int64_t pt_stride, int (&phys)[ChunkShape<D>::JT], int t) {
     constexpr int JT = ChunkShape<D>::JT;
-    const int wave = threadIdx.x >> 6;
+    const int wave = t >> 6;
 #pragma unroll
     for (int u = 0; u < JT; ++u) {
         const int pidx = 16 * c + JT * wave + u;
@@ -135,7 +137,7 @@ __device__ __forceinline__ void load_phys(const TileCtx& x, int c,
 
 // The per-chunk arithmetic shared by decode, prefill and the comparator: keys
 // [256c, 256c+256) of the tile's sequence, each row limited to keys <= its
-// position.  LDS may be reused only after a __syncthreads().
+// position.  LDS may be reused only after a __syncthreads().  t = threadIdx.x.
 // VL: V reaches the matrix cores through LDS (copied while q.k runs; decode)
 // or straight from memory into registers after q.k (prefill, where 16R rows
 // share each V fragment and LDS is better spent on more workgroups per CU).
@@ -145,11 +147,11 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
     const TileCtx& x, int c, const int (&phys_in)[ChunkShape<D>::JT],
     const int32_t* __restrict__ page_table, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, int64_t pt_stride,
-    int Hq, int Hkv, float scale_log2, ChunkLds<D, R, VL>& sh) {
+    int Hq, int Hkv, float scale_log2, ChunkLds<D, R, VL>& sh, int t) {
     using S = ChunkShape<D>;
     constexpr int NW = S::NW, JT = S::JT, KS = S::KS;
     static_assert(S::NTH >= 256 * R, "one thread per (row, 16-key segment) for l");
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int lane = t & 63, wave = t >> 6;
     const int ar = lane & 15, ag = lane >> 4;
     const int j0 = c * CHUNK;
     const int g = x.g;

@@ -22,7 +22,9 @@
 // and K) into two LDS stages of 64 KB; the next K-tile streams in while the
 // current one feeds the matrix cores.
 //   * A tile [256][64]: rows of 128 bytes, 16-byte chunk c of row r stored at
-//     c ^ ((r ^ r>>3) & 7); A fragments are ds_read_b128 (conflict free).
+//     c ^ (r & 7); A fragments are ds_read_b128, free of bank conflicts on
+//     gfx950's 64-bank LDS (a (r ^ r>>3) & 7 pattern measured two-way
+//     conflicts and half the read rate).
 //   * W tile [64][256] stays k-major as in HBM; chunk c of row k stored at
 //     c ^ 2((k & 3) + 4((k >> 3) & 1)).  A B fragment (8 consecutive k of one
 //     column) is two ds_read_b64_tr_b16: in each 16-lane group, lane i of the
@@ -48,7 +50,7 @@ constexpr int BK = 64;
 constexpr unsigned RSRC_WORD3 = 0x00020000u;   // raw buffer: 32-bit data format, no swizzle
 constexpr int OOB = 0x7ffffff0;                // offset past any num_records: reads zero
 
-__device__ __forceinline__ int swz_a(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz_a(int r) { return r & 7; }
 __device__ __forceinline__ int swz_w(int k) { return 2 * ((k & 3) + 4 * ((k >> 3) & 1)); }
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
