@@ -21,6 +21,9 @@ last-level cache, so every leg starts from a cache the other legs have
 flushed.
 
 `value` is the GEMM leg in TFLOP/s (2*M*N*K per launch / mean launch time);
+`rmsnorm_vs_device_copy` times a plain device copy of the RMSNorm leg's bytes
+in the same cache state (right after a full step), the practical ceiling of
+that HBM-bound leg;
 the decode-attention GB/s (algorithmic bytes: K, V, q, out, page table) is
 reported beside it with its own roofline.  `cpu_baseline` times the fp64
 oracle on a bounded sample of the same workload on the host cores.
@@ -290,6 +293,20 @@ def main():
     pf_tflops = work["prefill_flops"] / s["prefill_attn"] / 1e12
     glue_gbps = work["glue_bytes"] / s["decoder_glue"] / 1e9
 
+    # reference for the HBM-bound RMSNorm leg: a plain device copy of the same
+    # bytes (x -> y, no arithmetic), timed in the same cache state, i.e. right
+    # after a full step, where the next step's RMSNorm would start
+    cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    for k in range(args.steps):
+        run_step(w)
+        cevs[k][0].record()
+        w["y"].copy_(w["x"])
+        cevs[k][1].record()
+    torch.cuda.synchronize()
+    copy_s = sum(a.elapsed_time(b) for a, b in cevs) / args.steps * 1e-3
+    copy_gbps = work["rmsnorm_bytes"] / copy_s / 1e9
+
     if args.profile_copy:
         # calibration for the HBM byte counters: one elementwise kernel that
         # reads 1 GiB and writes 1 GiB
@@ -333,6 +350,8 @@ def main():
         "legs_ms": {n: round(ms[n], 4) for n in legs},
         "rmsnorm_GBps": round(rms_gbps, 1),
         "rmsnorm_frac_hbm": round(rms_gbps / PEAK_HBM_GBPS, 4),
+        "rmsnorm_vs_device_copy": {"copy_GBps": round(copy_gbps, 1),
+                                   "ratio": round(rms_gbps / copy_gbps, 3)},
         "prefill_attn_TFLOPs": round(pf_tflops, 2),
         "decoder_glue_GBps": round(glue_gbps, 1),
     }

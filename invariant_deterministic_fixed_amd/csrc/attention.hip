@@ -70,6 +70,15 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     constexpr bool VL = (R == 1);           // V through LDS for single-tile (decode) workgroups
     __shared__ ChunkLds<D, R, VL> sh;
     constexpr int JT = ChunkShape<D>::JT;
+    // page-table entries of the first chunk: in bounds whatever kv_len is
+    // (row b, entries < pt_stride), so they are read alongside kv_lens rather
+    // than after it; later chunks' entries are read one chunk ahead
+    int phys_next[JT];
+    {
+        TileCtx x0;
+        x0.pt_row = (int64_t)blockIdx.z * pt_stride;
+        load_phys<D>(x0, blockIdx.y, page_table, pt_stride, phys_next, threadIdx.x);
+    }
     const int pos_max = tile_ctx<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
                                        kv_lens, pt_stride, max_kv_len).pos_max;
 #pragma clang loop unroll(disable)
@@ -84,7 +93,10 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
         const TileCtx x = tile_ctx<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
                                          kv_lens, pt_stride, max_kv_len);
         int phys[JT];
-        load_phys<D>(x, c, page_table, pt_stride, phys, t);
+#pragma unroll
+        for (int u = 0; u < JT; ++u) phys[u] = phys_next[u];
+        if (LOOP && (c + (int)gridDim.y) * CHUNK <= pos_max)
+            load_phys<D>(x, c + gridDim.y, page_table, pt_stride, phys_next, t);
         const ChunkOut<R> r = chunk_compute<D, G, R, VL>(x, c, phys, page_table, q, kc, vc,
                                                          pt_stride, Hq, Hkv, scale_log2, sh, t);
         const int j0 = c * CHUNK;

@@ -119,7 +119,8 @@ struct ChunkOut {
 };
 
 // Page-table entries of the JT pages this wave reads in chunk c (independent
-// of kv_len, so they can be fetched up front); 0 past the table's row.
+// of kv_len, so they can be fetched up front; only x.pt_row is used); 0 past
+// the table's row.
 // t = threadIdx.x, passed in so that a caller looping over chunks can keep
 // the lane-derived arithmetic inside its loop.
 template <int D>
