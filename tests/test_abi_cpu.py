@@ -127,3 +127,71 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libbinv.so")
     with pytest.raises(RuntimeError, match="no fallback"):
         binding.lib()
+
+
+def test_embed_validation():
+    f = _lib().binv_embed
+    assert f(L, 0, L, 10, 8, L, L) == OK                                    # T = 0: no-op
+    assert f(FAKE, -1, FAKE, 10, 8, FAKE, L) == INVALID                     # negative T
+    assert f(FAKE, 4, FAKE, 0, 8, FAKE, L) == INVALID                       # empty table
+    assert f(L, 4, FAKE, 10, 8, FAKE, L) == INVALID                         # null ids
+    assert f(FAKE, 4, FAKE + 8, 10, 8, FAKE, L) == INVALID                  # misaligned table
+    assert f(FAKE, 4, FAKE, 10, 12, FAKE, L) == UNSUPPORTED                 # H % 8
+
+
+def test_rope_kv_write_validation():
+    f = _lib().binv_rope_kv_write
+    args = lambda **k: [k.get("qkv", FAKE), k.get("ld", 48 * 128), FAKE, FAKE, k.get("T", 4),
+                        k.get("Hq", 32), k.get("Hkv", 8), k.get("D", 128), k.get("theta", 5e5),
+                        FAKE, FAKE, FAKE, FAKE, k.get("pts", 64), k.get("page", 16), L]
+    assert f(*args(T=0)) == OK
+    assert f(*args(T=-1)) == INVALID
+    assert f(*args(qkv=L)) == INVALID
+    assert f(*args(Hkv=0)) == INVALID
+    assert f(*args(theta=1.0)) == INVALID                                   # theta must exceed 1
+    assert f(*args(theta=float("inf"))) == INVALID
+    assert f(*args(pts=0)) == INVALID
+    assert f(*args(D=96)) == UNSUPPORTED
+    assert f(*args(page=32)) == UNSUPPORTED
+    assert f(*args(ld=48 * 128 - 8)) == INVALID                             # row shorter than q|k|v
+
+
+def test_swiglu_validation():
+    f = _lib().binv_swiglu
+    assert f(L, 16, 0, 8, L, 8, L) == OK                                    # T = 0
+    assert f(FAKE, 16, 4, 0, FAKE, 8, L) == OK                              # F = 0
+    assert f(FAKE, 16, -1, 8, FAKE, 8, L) == INVALID
+    assert f(FAKE, 8, 4, 8, FAKE, 8, L) == INVALID                          # ld_gu < 2F
+    assert f(FAKE, 16, 4, 8, FAKE, 4, L) == INVALID                         # ld_out < F
+    assert f(FAKE + 8, 16, 4, 8, FAKE, 8, L) == INVALID                     # misaligned
+    assert f(FAKE, 24, 4, 12, FAKE, 16, L) == UNSUPPORTED                   # F % 8
+    assert f(FAKE, 16, 70000, 8, FAKE, 8, L) == UNSUPPORTED                 # T > 65535
+
+
+def test_residual_add_validation():
+    f = _lib().binv_residual_add
+    assert f(L, 8, L, 8, 0, 8, L) == OK
+    assert f(FAKE, 8, FAKE, 8, -2, 8, L) == INVALID
+    assert f(FAKE, 4, FAKE, 8, 2, 8, L) == INVALID                          # ldh < H
+    assert f(FAKE + 4, 8, FAKE, 8, 2, 8, L) == INVALID                      # h not 16B aligned
+    assert f(FAKE, 8, FAKE + 2, 8, 2, 8, L) == INVALID                      # x not 8B aligned
+    assert f(FAKE, 8, FAKE, 8, 2, 6, L) == UNSUPPORTED                      # H % 4
+
+
+def test_gather_rows_validation():
+    f = _lib().binv_gather_rows
+    assert f(L, 1, 8, L, 0, L, 8, 8, L) == OK                               # R = 0
+    assert f(FAKE, 7, 8, FAKE, 2, FAKE, 8, 8, L) == INVALID                 # unknown dtype
+    assert f(FAKE, 1, 8, L, 2, FAKE, 8, 8, L) == INVALID                    # null idx
+    assert f(FAKE, 1, 4, FAKE, 2, FAKE, 8, 8, L) == INVALID                 # lds < cols
+    assert f(FAKE, 1, 8, FAKE, 2, FAKE, 8, 3, L) == INVALID                 # 6-byte rows
+
+
+def test_topk_validation():
+    f = _lib().binv_topk
+    assert f(L, 16, 0, 16, 20, L, L, L) == OK                               # R = 0
+    assert f(FAKE, 16, 2, 16, 0, FAKE, FAKE, L) == INVALID                  # K < 1
+    assert f(FAKE, 16, 2, 16, 33, FAKE, FAKE, L) == UNSUPPORTED             # K > 32
+    assert f(FAKE, 8, 2, 16, 4, FAKE, FAKE, L) == INVALID                   # ldx < n
+    assert f(FAKE, 16, 2, 16, 4, L, FAKE, L) == INVALID                     # null ids
+    assert f(FAKE, 16, -1, 16, 4, FAKE, FAKE, L) == INVALID
