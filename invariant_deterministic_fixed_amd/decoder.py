@@ -57,7 +57,9 @@ class KVPool:
     """Per-layer paged K/V caches and one host page table shared by all layers.
 
     Pages are handed out from a free list shuffled by `seed`, so where a
-    sequence's pages sit changes from run to run."""
+    sequence's pages sit changes from run to run.  A page may belong to several
+    sequences (a shared prompt prefix, `share_prefix`); it returns to the free
+    list when the last of them is released."""
 
     def __init__(self, cfg, num_pages, max_seqs, max_len, seed, device):
         Hkv, D = cfg["n_kv"], cfg["head_dim"]
@@ -67,6 +69,7 @@ class KVPool:
         self.v = [torch.zeros((num_pages, Hkv, D, PAGE_SIZE), dtype=torch.bfloat16, device=device)
                   for _ in range(cfg["layers"])]
         self.free = list(np.random.default_rng(int(seed)).permutation(num_pages))
+        self.refs = np.zeros(num_pages, dtype=np.int64)
         self.pps = -(-int(max_len) // PAGE_SIZE)
         self.table = np.zeros((max_seqs, self.pps), dtype=np.int32)
         self.pages = [[] for _ in range(max_seqs)]
@@ -82,12 +85,32 @@ class KVPool:
         if need > self.pps:
             raise ValueError("sequence longer than the pool's max_len")
         while len(self.pages[slot]) < need:
+            if not self.free:
+                raise RuntimeError("KV pool out of pages")
             p = int(self.free.pop())
+            self.refs[p] = 1
             self.table[slot, len(self.pages[slot])] = p
             self.pages[slot].append(p)
 
+    def share_prefix(self, src, dst, n_tokens):
+        """Give the empty sequence `dst` the pages that hold tokens [0, n_tokens)
+        of `src`, without copying.  n_tokens must be a whole number of pages:
+        `dst` then writes its own tokens into pages of its own."""
+        n_tokens = int(n_tokens)
+        if n_tokens % PAGE_SIZE or n_tokens // PAGE_SIZE > len(self.pages[src]):
+            raise ValueError("a shared prefix must cover whole pages that src holds")
+        if self.pages[dst]:
+            raise ValueError("dst must hold no pages")
+        for i, p in enumerate(self.pages[src][:n_tokens // PAGE_SIZE]):
+            self.refs[p] += 1
+            self.table[dst, i] = p
+            self.pages[dst].append(p)
+
     def release(self, slot):
-        self.free.extend(self.pages[slot])
+        for p in self.pages[slot]:
+            self.refs[p] -= 1
+            if self.refs[p] == 0:
+                self.free.append(p)
         self.pages[slot] = []
         self.table[slot] = 0
         self.used[slot] = False

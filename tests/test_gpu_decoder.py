@@ -7,7 +7,10 @@
   128, FFN 14336, vocab 128256): a 512-token target greedy-decoded for 200
   tokens alone and with neighbours; tokens and top-20 fp32 logits must be
   bitwise identical, and one prefill of prompt + generated tokens must
-  reproduce the last decode step's logits.
+  reproduce the last decode step's logits;
+* prefix-cache reuse: a request whose prompt prefix sits in KV pages that
+  another request's (chunked, batched) prefill wrote gives the same bits as
+  the request run alone from scratch.
 """
 import numpy as np
 import pytest
@@ -69,6 +72,62 @@ def test_small_decoder_chunked_prefill_and_decode_bitwise(small):
         pool.release(slot)
 
 
+def greedy(d, slot, toks, start, n, with_neighbour=None):
+    """Prefill `toks` at position `start` in one step, then n - 1 greedy decode
+    steps.  with_neighbour = (slot, tokens) adds a sequence prefilled in the same
+    first step.  Returns the chosen tokens and the fp32 logits of every step."""
+    items = [(slot, toks, start)]
+    if with_neighbour is not None:
+        items = [(with_neighbour[0], with_neighbour[1], 0)] + items
+    logits, ids, _ = d.step(items)
+    k = len(items) - 1
+    out_t, out_l = [int(ids[k, 0])], [logits[k].cpu().clone()]
+    pos = start + len(toks)
+    for _ in range(n - 1):
+        logits, ids, _ = d.step([(slot, [out_t[-1]], pos)])
+        out_t.append(int(ids[0, 0]))
+        out_l.append(logits[0].cpu().clone())
+        pos += 1
+    return out_t, out_l
+
+
+def prefix_reuse_case(d, pool, vocab, n_prefix, n_a, n_b, n_new, seed, chunk):
+    """B = prefix + sb run alone vs B reading the prefix from pages that A's
+    chunked prefill (batched with a neighbour) wrote."""
+    r = np.random.default_rng(seed)
+    prefix = r.integers(0, vocab, n_prefix).tolist()
+    sa = r.integers(0, vocab, n_a).tolist()
+    sb = r.integers(0, vocab, n_b).tolist()
+    nb = r.integers(0, vocab, 3 * chunk + 5).tolist()
+    # reference: B alone, one-shot prefill
+    slot = pool.alloc()
+    ref_t, ref_l = greedy(d, slot, prefix + sb, 0, n_new)
+    pool.release(slot)
+    # A = prefix + sa, prefilled in chunks beside a neighbour's chunks
+    a, n = pool.alloc(), pool.alloc()
+    full = prefix + sa
+    for s0 in range(0, len(full), chunk):
+        items = [(a, full[s0:s0 + chunk], s0)]
+        if s0 < len(nb):
+            items.insert(0, (n, nb[s0:s0 + chunk], s0))
+        d.step(items)
+    # B takes A's prefix pages and prefills only its own suffix
+    b = pool.alloc()
+    pool.share_prefix(a, b, n_prefix)
+    got_t, got_l = greedy(d, b, sb, n_prefix, n_new)
+    for s in (a, n, b):
+        pool.release(s)
+    assert got_t == ref_t
+    for i, (g, e) in enumerate(zip(got_l, ref_l)):
+        assert_bitwise_equal(g, e, f"step {i}")
+
+
+def test_small_decoder_prefix_cache_reuse(small):
+    _, pool, d, _ = small
+    prefix_reuse_case(d, pool, SMALL["vocab"], n_prefix=96, n_a=37, n_b=29, n_new=8, seed=9,
+                      chunk=13)
+
+
 def test_small_decoder_invariance_with_neighbours(small):
     w, pool, d, _ = small
     r = np.random.default_rng(3)
@@ -87,9 +146,10 @@ def full():
     torch.cuda.empty_cache()
     w = dec.random_weights(cfg, 5, DEV)
     max_len = 8192 + 512 + 256
-    pool = dec.KVPool(cfg, num_pages=40 * (max_len // 16), max_seqs=40, max_len=max_len, seed=11,
-                      device=DEV)
-    d = dec.Decoder(w, cfg, pool, max_tokens=2048 + 64, max_seqs=40, max_kv_len=max_len)
+    # 32768 pages = 524288 tokens = 64 GB of bf16 K/V over 32 layers: room for a
+    # 2048-token prefill budget over 200 steps plus 255 decoding neighbours
+    pool = dec.KVPool(cfg, num_pages=32768, max_seqs=260, max_len=max_len, seed=11, device=DEV)
+    d = dec.Decoder(w, cfg, pool, max_tokens=2048 + 260 + 64, max_seqs=260, max_kv_len=max_len)
     yield cfg, pool, d
     del d, pool, w
     torch.cuda.empty_cache()
@@ -101,7 +161,7 @@ def test_config5_target_bitwise_across_compositions(full):
     prompt = r.integers(0, cfg["vocab"], 512).tolist()
     alone = harness.run(d, pool, prompt, 200, seed=0, record_logits=True)
     print("target alone: first tokens", alone["tokens"][:8], flush=True)
-    plan = [(1, 256), (7, 512), (31, 2048), (int(r.integers(2, 31)), 512)]
+    plan = [(1, 256), (7, 512), (31, 2048), (int(r.integers(2, 31)), 512), (255, 2048)]
     for trial, (n, budget) in enumerate(plan):
         rr = np.random.default_rng(1000 + trial)
         nbrs = [rr.integers(0, cfg["vocab"], int(rr.integers(16, 8193))).tolist() for _ in range(n)]
@@ -115,3 +175,9 @@ def test_config5_target_bitwise_across_compositions(full):
     replay = d.step([(slot, prompt + alone["tokens"][:199], 0)])[0][0].cpu()
     pool.release(slot)
     assert_bitwise_equal(replay, alone["logits"][199], "prefill replay vs decode")
+
+
+def test_config5_prefix_cache_reuse(full):
+    cfg, pool, d = full
+    prefix_reuse_case(d, pool, cfg["vocab"], n_prefix=512, n_a=64, n_b=48, n_new=16, seed=5,
+                      chunk=100)
