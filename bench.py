@@ -29,6 +29,9 @@ reported beside it with its own roofline.  `cpu_baseline` times the fp64
 oracle on a bounded sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--ramp-seconds S] [--no-cpu-baseline]
+       python bench.py --sweep   (per-shape figures of every workload family, invariant
+                                  kernels beside the shape-tuned comparators, one JSON line
+                                  per case)
        [--profile-copy]   (adds one 1 GiB device copy, the calibration kernel
                            for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
 """
@@ -246,6 +249,187 @@ def cpu_baseline(w, gemm_rows=GEMM_M, max_seqs=DEC_B, prefill_rows=512):
     }
 
 
+# ---------------------------------------------------------------- sweep mode
+def _cold_ms(fns, reps=20):
+    """Mean ms of one call, cycling over `fns` (each bound to its own copy of
+    the inputs, together larger than the 256 MB last-level cache, so no call
+    finds its operands cached), events around each call."""
+    import torch
+    for f in fns[:2]:
+        f()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for k in range(reps):
+        evs[k][0].record()
+        fns[k % len(fns)]()
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+def _copies(nbytes, floor=640 << 20):
+    return max(1, min(64, -(-floor // max(1, nbytes))))
+
+
+def sweep(dev="cuda:0"):
+    """Per-shape figures of every workload family, invariant kernels beside
+    the shape-tuned comparators (and torch.mm, i.e. hipBLASLt, for the GEMM):
+    one JSON object per line."""
+    import numpy as np
+    import torch
+    import invariant_deterministic_fixed_amd as binv
+    from invariant_deterministic_fixed_amd import synth, decoder as dec
+
+    def paged(lens, seed):
+        seqs = [synth.random_kv(int(L), HKV, HD, seed + 31 * i, dev) for i, L in enumerate(lens)]
+        return synth.PagedKV(seqs, HKV, HD, seed + 5, device=dev)
+
+    def emit(**kv):
+        print(json.dumps(kv), flush=True)
+
+    # clock ramp
+    a = torch.randn((8192, 4096), device=dev).to(torch.bfloat16)
+    b = torch.randn((4096, 4096), device=dev).to(torch.bfloat16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        binv.gemm(a, b)
+        torch.cuda.synchronize()
+    del a, b
+
+    # GEMM: invariant vs tuned vs torch.mm, per M and weight shape
+    for (N, K, c32) in [(4096, 4096, False), (14336, 4096, False), (4096, 14336, False),
+                        (128256, 4096, True)]:
+        nw = _copies(2 * N * K)
+        Ws = [synth.normal((K, N), 0.02, 7 + i, dev) for i in range(nw)]
+        for M in [1, 2, 7, 16, 64, 256, 1024, 2048, 8192]:
+            if c32 and M > 256:
+                continue
+            A = synth.normal((M, K), 1.0, 3, dev)
+            od = torch.float32 if c32 else torch.bfloat16
+            C = torch.empty((M, N), dtype=od, device=dev)
+            ws = torch.empty(binv.lib().binv_gemm_bf16_tuned_workspace_bytes(M, N, K),
+                             dtype=torch.uint8, device=dev)
+            t_inv = _cold_ms([lambda W=W: binv.gemm(A, W, out=C) for W in Ws])
+            t_tun = _cold_ms([lambda W=W: binv.gemm(A, W, out=C, tuned=True, workspace=ws)
+                              for W in Ws])
+            t_mm = None
+            if not c32:
+                t_mm = _cold_ms([lambda W=W: torch.mm(A, W, out=C) for W in Ws])
+            flops = 2.0 * M * N * K
+            nbytes = 2 * (M * K + K * N) + (4 if c32 else 2) * M * N
+            roof_ms = max(flops / PEAK_BF16_TFLOPS / 1e9, nbytes / PEAK_HBM_GBPS / 1e6)
+            emit(sweep="gemm", M=M, N=N, K=K, out="fp32" if c32 else "bf16",
+                 invariant_TFLOPs=round(flops / t_inv / 1e9, 2),
+                 tuned_TFLOPs=round(flops / t_tun / 1e9, 2),
+                 torch_mm_TFLOPs=None if t_mm is None else round(flops / t_mm / 1e9, 2),
+                 roofline_frac=round(roof_ms / t_inv, 4),
+                 slowdown_vs_tuned=round(t_inv / t_tun, 3))
+            del A, C, ws
+        del Ws
+        torch.cuda.empty_cache()
+
+    # RMSNorm: invariant vs tuned, per M and d
+    for d in [4096, 5120]:
+        g = synth.uniform((d,), 0.5, 1.5, 5, dev).to(torch.bfloat16)
+        for M in [1, 64, 1024, 4096, 8192, 16384]:
+            n = _copies(4 * M * d)
+            xs = [synth.normal((M, d), 3.0, 11 + i, dev).to(torch.bfloat16) for i in range(n)]
+            y = torch.empty_like(xs[0])
+            t_inv = _cold_ms([lambda x=x: binv.rmsnorm(x, g, 1e-6, out=y) for x in xs])
+            t_tun = _cold_ms([lambda x=x: binv.rmsnorm(x, g, 1e-6, out=y, tuned=True) for x in xs])
+            nbytes = 4 * M * d + 2 * d
+            emit(sweep="rmsnorm", M=M, d=d, invariant_GBps=round(nbytes / t_inv / 1e6, 1),
+                 tuned_GBps=round(nbytes / t_tun / 1e6, 1),
+                 roofline_frac=round(nbytes / t_inv / 1e6 / PEAK_HBM_GBPS, 4),
+                 slowdown_vs_tuned=round(t_inv / t_tun, 3))
+            del xs, y
+        torch.cuda.empty_cache()
+
+    # decode attention: invariant vs tuned, per batch size (log-uniform lengths)
+    for B in [1, 4, 16, 64, 256]:
+        lens = synth.log_uniform_lengths(B, DEC_LMIN, DEC_LMAX, synth.seed_for(4) + B)
+        kv_bytes = int(lens.sum()) * HKV * HD * 4
+        caches = [paged(lens, synth.seed_for(4) + 1000 * i) for i in range(_copies(kv_bytes))]
+        q = synth.normal((B, HQ, HD), 1.0, 9, dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(binv.attn_workspace_bytes(B, HQ, HD, DEC_LMAX), dtype=torch.uint8,
+                         device=dev)
+        wst = torch.empty(binv.lib().binv_attn_decode_tuned_workspace_bytes(B, HQ, HD, DEC_LMAX),
+                          dtype=torch.uint8, device=dev)
+        scale = 1.0 / math.sqrt(HD)
+        t_inv = _cold_ms([lambda c=c: binv.attn_decode(q, c.k_cache, c.v_cache, c.page_table,
+                                                        c.kv_lens, DEC_LMAX, scale, out=out,
+                                                        workspace=ws) for c in caches])
+        t_tun = _cold_ms([lambda c=c: binv.attn_decode(q, c.k_cache, c.v_cache, c.page_table,
+                                                        c.kv_lens, DEC_LMAX, scale, out=out,
+                                                        workspace=wst, tuned=True)
+                          for c in caches])
+        nbytes = kv_bytes + 4 * B * HQ * HD + 4 * sum(-(-int(L) // 16) for L in lens)
+        emit(sweep="decode_attn", B=B, sum_kv_tokens=int(lens.sum()),
+             invariant_GBps=round(nbytes / t_inv / 1e6, 1), tuned_GBps=round(nbytes / t_tun / 1e6, 1),
+             roofline_frac=round(nbytes / t_inv / 1e6 / PEAK_HBM_GBPS, 4),
+             slowdown_vs_tuned=round(t_inv / t_tun, 3))
+        del caches, q, out, ws, wst
+        torch.cuda.empty_cache()
+
+    # prefill attention: one 4096-token sequence, one shot and in chunks
+    T = PREFILL_T
+    c = paged([T], synth.seed_for(4) + 3)
+    q = synth.normal((T, HQ, HD), 1.0, 13, dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(binv.attn_workspace_bytes(T, HQ, HD, T), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(HD)
+    for chunk in [T, 2048, 512, 256]:
+        parts = []
+        for s0 in range(0, T, chunk):
+            n = min(chunk, T - s0)
+            parts.append((s0, n, torch.tensor([0, n], dtype=torch.int32, device=dev),
+                          torch.tensor([s0 + n], dtype=torch.int32, device=dev)))
+
+        def run(parts=parts):
+            for s0, n, cu, kvl in parts:
+                binv.attn_prefill(q[s0:s0 + n], cu, c.k_cache, c.v_cache, c.page_table, kvl, n, T,
+                                  scale, out=out[s0:s0 + n], workspace=ws)
+        t = _cold_ms([run], reps=5)
+        flops = 4.0 * HQ * HD * sum(p + 1 for p in range(T))
+        emit(sweep="prefill_attn", T=T, chunk=chunk, TFLOPs=round(flops / t / 1e9, 2))
+    del c, q, out, ws
+    torch.cuda.empty_cache()
+
+    # 8B-class decoder: decode tokens/s at batch B with 1024-token contexts
+    cfg = dec.CONFIG5
+    w = dec.random_weights(cfg, 5, dev)
+    for B in [1, 16, 64]:
+        res = {}
+        for tuned in (False, True):
+            pool = dec.KVPool(cfg, num_pages=B * (1024 + 64) // 16 + B, max_seqs=B,
+                              max_len=1024 + 64, seed=11, device=dev)
+            d = dec.Decoder(w, cfg, pool, max_tokens=max(1024, B), max_seqs=B,
+                            max_kv_len=1024 + 64, tuned=tuned)
+            r = np.random.default_rng(42)
+            slots = [pool.alloc() for _ in range(B)]
+            toks = {}
+            for sl in slots:                          # prefill, untimed
+                _, ids, _ = d.step([(sl, r.integers(0, cfg["vocab"], 1024).tolist(), 0)])
+                toks[sl] = int(ids[0, 0])
+            torch.cuda.synchronize()
+            steps = 8
+            t0 = time.perf_counter()
+            for k in range(steps):
+                _, ids, _ = d.step([(sl, [toks[sl]], 1024 + k) for sl in slots])
+                ids = ids.cpu()
+                for i, sl in enumerate(slots):
+                    toks[sl] = int(ids[i, 0])
+            torch.cuda.synchronize()
+            res[tuned] = B * steps / (time.perf_counter() - t0)
+            del d, pool
+            torch.cuda.empty_cache()
+        emit(sweep="decoder_8b_decode", B=B, context=1024, invariant_tokens_per_s=round(res[False], 1),
+             tuned_tokens_per_s=round(res[True], 1),
+             slowdown_vs_tuned=round(res[True] / res[False], 3))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +438,8 @@ def main():
     ap.add_argument("--ramp-seconds", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-copy", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="per-shape figures (one JSON line per case) instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -264,6 +450,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.sweep:
+        sweep(dev)
+        return
     w = build_workload(dev)
     work = algorithmic(w)
     torch.cuda.synchronize()

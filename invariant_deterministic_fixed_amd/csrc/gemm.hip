@@ -1,26 +1,33 @@
-// gemm.hip -- bf16 GEMM with one fixed tile configuration and no split-K (gfx950).
+// gemm.hip -- bf16 GEMM with one fixed reduction per element and no split-K (gfx950).
 //
 // Method: devpress.csdn.net explainer of "Defeating Nondeterminism in LLM
 // Inference", section 3.2 Matmul (C = A B as elementwise products plus a
 // reduction over k; 2-D output tiles, each reducing the whole K inside one
-// core; a single kernel configuration for every batch size, split-K
-// disabled); tom-jerr.github.io "Batch-Invariant Kernel", section GEMM (fixed
-// tiling, the K strategy decoupled from M).
+// core; split-K disabled, because splitting the reduction by batch size is
+// what makes the bits depend on the batch); tom-jerr.github.io
+// "Batch-Invariant Kernel", section GEMM (fixed tiling, the K strategy
+// decoupled from M).
 //
 // Per output element the arithmetic is one fp32 accumulator updated by
 // v_mfma_f32_16x16x32_bf16 over k-blocks [0,32), [32,64), ... in ascending
-// order.  Nothing in that chain depends on M: not the tile (a constant), not
-// the K loop, not the row's position in its tile (a row's slot only decides
-// which lane carries it).  In fact no tile parameter enters the chain at all,
-// so the comparator below, which uses another tile, produces the same bits
-// whenever it does not split K.
+// order, with K padded by zeros to a multiple of 64.  On the pages a single
+// tile configuration is what pins that order; here no tile parameter enters
+// the chain at all (a row's slot in a tile only decides which lane carries
+// it), so the output tile can follow the shape without the bits following:
+//   * 256 x 256 tiles when that gives >= 192 tiles (large M),
+//   * 16-column strips for M <= 64 (decode batches; gemm_skinny_kernel),
+//   * 128 x 128 tiles otherwise.
+// Tests check a row's bits across M = 1 .. 8192, i.e. across all three.  The
+// comparator below (128 x 128 with split-K chosen from the tile count) is the
+// one that does change with M.
 //
-// Invariant kernel: tile 256 x 256 x 64, 512 lanes = 8 waves in a 2 x 4 grid,
-// each wave owning 128 x 64 outputs (8 x 4 MFMA tiles, 128 fp32 accumulators
-// per lane).  A and W travel HBM -> LDS by buffer_load ... lds (16 bytes per
-// lane, no registers, out-of-range lanes read zero, which handles ragged M, N
-// and K) into two LDS stages of 64 KB; the next K-tile streams in while the
-// current one feeds the matrix cores.
+// Tile kernel (256 x 256 shown; 128 x 128 is the same code with 4 waves):
+// 512 lanes = 8 waves in a 2 x 4 grid, each wave owning 128 x 64 outputs
+// (8 x 4 MFMA tiles, 128 fp32 accumulators per lane).  A and W travel
+// HBM -> LDS by buffer_load ... lds (16 bytes per lane, no registers,
+// out-of-range lanes read zero, which handles ragged M, N and K) into two LDS
+// stages of 64 KB; the next K-tile streams in while the current one feeds the
+// matrix cores.
 //   * A tile [256][64]: rows of 128 bytes, 16-byte chunk c of row r stored at
 //     c ^ (r & 7); A fragments are ds_read_b128, free of bank conflicts on
 //     gfx950's 64-bank LDS (a (r ^ r>>3) & 7 pattern measured two-way
@@ -210,8 +217,140 @@ struct Tile {
     }
 };
 
-using InvariantTile = Tile<256, 256, 2, 4, 8>;   // the one configuration of binv_gemm_bf16
-using TunedTile = Tile<128, 128, 2, 2, 8>;       // comparator's tile
+
+// ------------------------------------------------------------------ few rows
+// M <= 64 (decode batches).  The 256 x 256 tile would give N / 256 workgroups
+// (16 for N = 4096) and stream the weights through as many CUs.  Here a
+// workgroup is one wave owning a 16-column strip of W and all M (<= 16 FM)
+// rows; N / 16 strips keep every CU streaming.  Each element's arithmetic is
+// the invariant kernel's exactly: one fp32 accumulator, the same
+// v_mfma_f32_16x16x32_bf16 over the same 32-wide k-blocks in ascending order,
+// the same zero padding of a ragged K-tile of 64 -- so a row's bits do not
+// change when M crosses from this path to the 256 x 256 one.
+//   * LDS ring of NS stages (A [16 FM][64] as in the big tile; W [64][16],
+//     rows of 32 bytes); NS - 1 K-tiles stream in while one is consumed, so
+//     a wave keeps (NS - 1) x (2 FM + 2) KB of loads in flight.
+//   * W row k of a stage sits at row k ^ 4 ((k >> 3) & 1), so the 16 rows one
+//     ds_read_b64_tr_b16 touches spread over all 64 banks.
+//   * 4 consecutive strips (one 128-byte line of a W row) go to one XCD.
+//   * The transposing LDS reads are issued as inline asm: for the builtin the
+//     compiler waits for every outstanding global -> LDS copy first
+//     (vmcnt(0)), which would drain the ring on each K-tile.  The lgkmcnt
+//     wait that follows them takes their results as operands, so nothing
+//     reads the registers before the data has arrived.
+__device__ __forceinline__ int skinny_row(int k) { return k ^ (((k >> 3) & 1) << 2); }
+
+__device__ __forceinline__ u32x2 ds_read_tr_b64(const char* p) {
+    u32x2 v;
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a) : "memory");
+    return v;
+}
+
+template <int FM, int NS>
+__global__ __launch_bounds__(64) void gemm_skinny_kernel(const bf16_t* __restrict__ A, int64_t lda,
+                                                         const bf16_t* __restrict__ W, int64_t ldw,
+                                                         void* __restrict__ C, int64_t ldc, int M,
+                                                         int N, int K, int c_f32) {
+    constexpr int A_BYTES = 16 * FM * BK * 2, W_BYTES = BK * 16 * 2, STAGE = A_BYTES + W_BYTES;
+    constexpr int PA = A_BYTES / 1024, PW = W_BYTES / 1024, P = PA + PW;   // DMA per stage
+    static_assert((NS - 2) * P <= 63, "vmcnt holds 6 bits");
+    __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+    const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
+    const int b = blockIdx.x, x = b & 7, local = b >> 3;
+    const int n0 = ((((local >> 2) << 3) + x) * 4 + (local & 3)) * 16;
+    if (n0 >= N) return;
+    const int nk = (K + BK - 1) / BK;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)A, (short)0, (int)((int64_t)M * lda * 2), RSRC_WORD3);
+
+    auto issue = [&](int st, int kt) {
+        char* As = smem + st * STAGE;
+        char* Ws = As + A_BYTES;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int u = 0; u < PA; ++u) {                  // 8 rows of A per 1 KB
+            const int row = 8 * u + (lane >> 3);
+            const int c = (lane & 7) ^ swz_a(row);
+            const int kk = k0 + 8 * c;
+            const int off = (row < M && kk < K) ? (row * (int)lda + kk) * 2 : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(As + u * 1024), 16, off, 0, 0, 0);
+        }
+        const int krows = min(BK, K - k0);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(W + (int64_t)k0 * ldw + n0), (short)0, (int)((int64_t)krows * ldw * 2),
+            RSRC_WORD3);
+#pragma unroll
+        for (int u = 0; u < PW; ++u) {                  // 32 rows of the strip per 1 KB
+            const int kr = skinny_row(32 * u + (lane >> 1));    // logical row of this slot
+            const int pc = lane & 1;
+            const int off = (kr < krows && n0 + 8 * pc < N) ? (kr * (int)ldw + 8 * pc) * 2 : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(Ws + u * 1024), 16, off, 0, 0, 0);
+        }
+    };
+
+    f32x4 acc[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+        if (st < nk) issue(st, st);
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + NS - 2 < nk)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"((NS - 2) * P) : "memory");
+        else
+            wait_vm0();
+        const char* As = smem + (kt % NS) * STAGE;
+        const char* Ws = As + A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            const int k_lo = 32 * ks + 8 * g + (r >> 2), k_hi = k_lo + 4;
+            const int cb = ((r & 3) >> 1) * 16 + 8 * (r & 1);
+            u32x2 p0 = ds_read_tr_b64(Ws + skinny_row(k_lo) * 32 + cb);
+            u32x2 p1 = ds_read_tr_b64(Ws + skinny_row(k_hi) * 32 + cb);
+            u32x4 a[FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = 16 * i + r;
+                a[i] = *reinterpret_cast<const u32x4*>(As + (row << 7) +
+                                                       (((4 * ks + g) ^ swz_a(row)) << 4));
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(p0), "+v"(p1) : : "memory");
+            const u32x4 bf = u32x4{p0[0], p0[1], p1[0], p1[1]};
+#pragma unroll
+            for (int i = 0; i < FM; ++i) acc[i] = mfma16x16x32(a[i], bf, acc[i]);
+        }
+        // the slot of K-tile kt - 1 was consumed by the MFMAs above: refill it
+        if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
+    }
+
+    const int col = n0 + r;
+    if (col >= N) return;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * i + 4 * g + e;
+            if (row >= M) continue;
+            if (c_f32)
+                reinterpret_cast<float*>(C)[(int64_t)row * ldc + col] = acc[i][e];
+            else
+                reinterpret_cast<bf16_t*>(C)[(int64_t)row * ldc + col] = (bf16_t)f32_to_bf16(acc[i][e]);
+        }
+}
+
+template <int FM, int NS>
+hipError_t launch_skinny(const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
+                         int64_t ldc, int M, int N, int K, int c_f32, hipStream_t s) {
+    const int strips = (N + 15) / 16;
+    const int grid = (strips + 31) / 32 * 32;          // whole groups of 8 XCDs x 4 strips
+    hipLaunchKernelGGL((gemm_skinny_kernel<FM, NS>), dim3((unsigned)grid), dim3(64), 0, s,
+                       (const bf16_t*)A, lda, (const bf16_t*)W, ldw, C, ldc, M, N, K, c_f32);
+    return hipGetLastError();
+}
+
+using BigTile = Tile<256, 256, 2, 4, 8>;
+using MidTile = Tile<128, 128, 2, 2, 8>;         // also the comparator's tile
 
 template <class T>
 __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(const bf16_t* __restrict__ A, int64_t lda,
@@ -252,12 +391,24 @@ hipError_t launch_tile(const void* A, int64_t lda, const void* W, int64_t ldw, v
 
 }  // namespace
 
+// Which kernel computes the outputs is chosen from the shape (the 256 x 256
+// tile once it gives at least 192 tiles, i.e. fills most of the 256 CUs;
+// else 16-column strips for M <= 64; else 128 x 128 tiles).  All three run
+// the same per-element arithmetic -- one accumulator, one MFMA chain over the
+// same ascending 32-wide k-blocks and the same zero-padded K-tiles of 64 --
+// so the choice, and with it M, never reaches the bits.
 hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
                        int c_f32, int64_t ldc, int M, int N, int K, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     const int nk = (K + BK - 1) / BK;
-    return launch_tile<InvariantTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
-                                      c_f32, s);
+    const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+    if (big_tiles >= 192)
+        return launch_tile<BigTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
+                                    c_f32, s);
+    if (M <= 16) return launch_skinny<1, 16>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
+    if (M <= 32) return launch_skinny<2, 12>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
+    if (M <= 64) return launch_skinny<4, 8>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
+    return launch_tile<MidTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1, c_f32, s);
 }
 
 // Comparator: split-K whose split count is chosen from the number of output
@@ -284,11 +435,11 @@ hipError_t launch_gemm_tuned(const void* A, int64_t lda, const void* W, int64_t 
     const int S = tuned_splits(M, N, K);
     const int nk = (K + BK - 1) / BK;
     if (S == 1)
-        return launch_tile<TunedTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
+        return launch_tile<MidTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
                                       c_f32, s);
     const int per = (nk + S - 1) / S;
     const int Sused = (nk + per - 1) / per;
-    hipError_t e = launch_tile<TunedTile>(A, lda, W, ldw, ws, N, (int64_t)M * N, M, N, K, Sused,
+    hipError_t e = launch_tile<MidTile>(A, lda, W, ldw, ws, N, (int64_t)M * N, M, N, K, Sused,
                                           per, 1, s);
     if (e != hipSuccess) return e;
     const int64_t MN = (int64_t)M * N;

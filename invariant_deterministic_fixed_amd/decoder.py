@@ -117,8 +117,15 @@ class KVPool:
 
 
 class Decoder:
-    def __init__(self, weights, cfg, pool, max_tokens, max_seqs, max_kv_len, topk=20):
-        self.w, self.cfg, self.pool, self.topk = weights, cfg, pool, topk
+    """tuned=True swaps in the shape-tuned comparators (not batch-invariant):
+    split-K GEMM and block-size-by-M RMSNorm everywhere, and the split-by-batch
+    decode attention on steps where every sequence brings one token; prefill
+    steps keep the invariant attention, the only prefill kernel there is.  It
+    exists to measure what invariance costs."""
+
+    def __init__(self, weights, cfg, pool, max_tokens, max_seqs, max_kv_len, topk=20,
+                 tuned=False):
+        self.w, self.cfg, self.pool, self.topk, self.tuned = weights, cfg, pool, topk, tuned
         dev = pool.device
         H, Hq, Hkv, D, F = (cfg["hidden"], cfg["n_heads"], cfg["n_kv"], cfg["head_dim"],
                             cfg["ffn"])
@@ -174,24 +181,30 @@ class Decoder:
         h, x, qkv, q, a, o, gu, s = (t[:T] for t in (self.h, self.x, self.qkv, self.q, self.a,
                                                      self.o, self.gu, self.s))
         scale = 1.0 / math.sqrt(D)
+        tn = self.tuned
+        decode_only = tn and max_q == 1
         B.embed(ids_d, self.w["embed"], out=h)
         for li, lw in enumerate(self.w["layers"]):
-            B.rmsnorm(h, self.w["norm"], cfg["eps"], out=x)
-            B.gemm(x, lw["wqkv"], out=qkv)
+            B.rmsnorm(h, self.w["norm"], cfg["eps"], out=x, tuned=tn)
+            B.gemm(x, lw["wqkv"], out=qkv, tuned=tn)
             B.rope_kv_write(qkv, tseq_d, tpos_d, Hq, Hkv, D, cfg["theta"], pool.k[li], pool.v[li],
                             table, q_out=q)
-            B.attn_prefill(q, cu_d, pool.k[li], pool.v[li], table, lens_d, max_q,
-                           self.max_kv_len, scale, out=a, workspace=self.ws)
-            B.gemm(a.view(T, Hq * D), lw["wo"], out=o)
+            if decode_only:
+                B.attn_decode(q, pool.k[li], pool.v[li], table, lens_d, self.max_kv_len, scale,
+                              out=a, tuned=True)
+            else:
+                B.attn_prefill(q, cu_d, pool.k[li], pool.v[li], table, lens_d, max_q,
+                               self.max_kv_len, scale, out=a, workspace=self.ws)
+            B.gemm(a.view(T, Hq * D), lw["wo"], out=o, tuned=tn)
             B.residual_add(h, o)
-            B.rmsnorm(h, self.w["norm"], cfg["eps"], out=x)
-            B.gemm(x, lw["wgu"], out=gu)
+            B.rmsnorm(h, self.w["norm"], cfg["eps"], out=x, tuned=tn)
+            B.gemm(x, lw["wgu"], out=gu, tuned=tn)
             B.swiglu(gu, out=s)
-            B.gemm(s, lw["wd"], out=o)
+            B.gemm(s, lw["wd"], out=o, tuned=tn)
             B.residual_add(h, o)
         hl, xl, logits = self.hl[:nb], self.xl[:nb], self.logits[:nb]
         B.gather_rows(h, last_d, out=hl)
-        B.rmsnorm(hl, self.w["norm"], cfg["eps"], out=xl)
-        B.gemm(xl, self.w["lm_head"], out=logits)
+        B.rmsnorm(hl, self.w["norm"], cfg["eps"], out=xl, tuned=tn)
+        B.gemm(xl, self.w["lm_head"], out=logits, tuned=tn)
         top_ids, top_vals = B.topk(logits, self.topk)
         return logits, top_ids, top_vals

@@ -20,7 +20,8 @@ def ints(shape, seed, lo=-4, hi=4):
     return torch.from_numpy(r.integers(lo, hi + 1, size=shape).astype(np.float32)).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (7, 136, 264), (130, 256, 512), (257, 392, 1032)])
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (7, 136, 264), (16, 24, 200), (33, 4104, 136),
+                                   (64, 8, 72), (130, 256, 512), (257, 392, 1032)])
 def test_integer_inputs_exact(M, N, K):
     # |sum| <= K * 16 < 2^24: every fp32 partial sum is exact in any order
     A, W = ints((M, K), 1 + M), ints((K, N), 2 + N)
@@ -101,6 +102,27 @@ def test_row0_bitwise_invariant_over_M(N, K):
             ref16, ref32 = c16.clone(), c32.clone()
         assert_bitwise_equal(c16, ref16, f"bf16 M={M}")
         assert_bitwise_equal(c32, ref32, f"fp32 M={M}")
+
+
+@pytest.mark.parametrize("N,K", [(24, 72), (4104, 200), (4096, 4160), (136, 4096)])
+def test_kernels_chosen_by_shape_agree_bitwise(N, K):
+    # M <= 64 runs on 16-column strips, mid-size M on 128 x 128 tiles and
+    # large M x N on 256 x 256 tiles; every element must come out with the
+    # same bits on all of them, ragged N and K, zero and negative-zero rows
+    # against an all-negative column included
+    W = synth.normal((K, N), 0.02, 41 + N)
+    W[:, 3] = -W[:, 3].abs() - 0.01
+    W = W.to(DEV)
+    big_m = 8192 if N >= 4096 else 130                  # 256 x 256 tiles when N allows
+    A = synth.normal((big_m, K), 1.0, 43 + K)
+    A[5] = 0.0
+    A[6] = -0.0
+    Ad = A.to(DEV)
+    ref32 = binv.gemm(Ad, W, out_dtype=torch.float32)
+    ref16 = binv.gemm(Ad, W)
+    for M in [1, 7, 16, 17, 32, 33, 64, 65, 130]:
+        assert_bitwise_equal(binv.gemm(Ad[:M], W, out_dtype=torch.float32), ref32[:M], f"fp32 M={M}")
+        assert_bitwise_equal(binv.gemm(Ad[:M], W), ref16[:M], f"bf16 M={M}")
 
 
 def test_target_row_at_every_tile_position():
