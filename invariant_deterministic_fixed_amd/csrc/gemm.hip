@@ -221,18 +221,22 @@ struct Tile {
 // ------------------------------------------------------------------ few rows
 // M <= 64 (decode batches).  The 256 x 256 tile would give N / 256 workgroups
 // (16 for N = 4096) and stream the weights through as many CUs.  Here a
-// workgroup is one wave owning a 16-column strip of W and all M (<= 16 FM)
-// rows; N / 16 strips keep every CU streaming.  Each element's arithmetic is
-// the invariant kernel's exactly: one fp32 accumulator, the same
-// v_mfma_f32_16x16x32_bf16 over the same 32-wide k-blocks in ascending order,
-// the same zero padding of a ragged K-tile of 64 -- so a row's bits do not
-// change when M crosses from this path to the 256 x 256 one.
-//   * LDS ring of NS stages (A [16 FM][64] as in the big tile; W [64][16],
-//     rows of 32 bytes); NS - 1 K-tiles stream in while one is consumed, so
-//     a wave keeps (NS - 1) x (2 FM + 2) KB of loads in flight.
-//   * W row k of a stage sits at row k ^ 4 ((k >> 3) & 1), so the 16 rows one
-//     ds_read_b64_tr_b16 touches spread over all 64 banks.
-//   * 4 consecutive strips (one 128-byte line of a W row) go to one XCD.
+// workgroup is one wave owning a strip of 16 FN columns of W and all M
+// (<= 16 FM) rows; FN is the widest of 1, 2, 4 that still gives >= 192
+// strips (wider strips read longer pieces of each W row and spend fewer
+// instructions per byte; narrower ones spread N = 4096 over all CUs).  Each
+// element's arithmetic is the tile kernel's exactly: one fp32 accumulator, the
+// same v_mfma_f32_16x16x32_bf16 over the same 32-wide k-blocks in ascending
+// order, the same zero padding of a ragged K-tile of 64 -- so a row's bits do
+// not change when M crosses from this path to a tile one.
+//   * LDS ring of NS stages (A [16 FM][64] as in the big tile; W [64][16 FN]);
+//     each iteration first refills the slot the previous K-tile used, then
+//     waits for its own K-tile and reads both of its k-steps' fragments in one
+//     LDS round trip.
+//   * Bank spreading of the 16 W rows one ds_read_b64_tr_b16 touches: FN = 1
+//     (32-byte rows) stores row k at row k ^ 4 ((k >> 3) & 1); FN >= 2 XORs the
+//     16-byte chunk index with a function of k instead.
+//   * Strips that share 128-byte lines of a W row go to the same XCD.
 //   * The transposing LDS reads are issued as inline asm: for the builtin the
 //     compiler waits for every outstanding global -> LDS copy first
 //     (vmcnt(0)), which would drain the ring on each K-tile.  The lgkmcnt
@@ -247,29 +251,37 @@ __device__ __forceinline__ u32x2 ds_read_tr_b64(const char* p) {
     return v;
 }
 
-template <int FM, int NS>
+template <int FM, int FN, int NS>
 __global__ __launch_bounds__(64) void gemm_skinny_kernel(const bf16_t* __restrict__ A, int64_t lda,
                                                          const bf16_t* __restrict__ W, int64_t ldw,
                                                          void* __restrict__ C, int64_t ldc, int M,
                                                          int N, int K, int c_f32) {
-    constexpr int A_BYTES = 16 * FM * BK * 2, W_BYTES = BK * 16 * 2, STAGE = A_BYTES + W_BYTES;
-    constexpr int PA = A_BYTES / 1024, PW = W_BYTES / 1024, P = PA + PW;   // DMA per stage
-    static_assert((NS - 2) * P <= 63, "vmcnt holds 6 bits");
+    constexpr int BN = 16 * FN, RB = 2 * BN;                 // row bytes of the W strip
+    constexpr int A_BYTES = 16 * FM * BK * 2, W_BYTES = BK * RB, STAGE = A_BYTES + W_BYTES;
+    constexpr int PA = A_BYTES / 1024, PW = W_BYTES / 1024, P = PA + PW;
+    constexpr int RPI = 1024 / RB, LPR = RB / 16;             // rows per DMA, lanes per row
+    static_assert((NS - 1) * P <= 63, "vmcnt holds 6 bits");
     __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
     const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
     const int b = blockIdx.x, x = b & 7, local = b >> 3;
-    const int n0 = ((((local >> 2) << 3) + x) * 4 + (local & 3)) * 16;
+    constexpr int GS = (FN >= 8) ? 1 : 8 / FN;                // strips per 128-byte line group
+    const int n0 = ((local / GS) * 8 * GS + x * GS + (local % GS)) * BN;
     if (n0 >= N) return;
     const int nk = (K + BK - 1) / BK;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void*)A, (short)0, (int)((int64_t)M * lda * 2), RSRC_WORD3);
-
+    // physical chunk of (row k, chunk c): FN = 1 permutes rows, FN >= 2 XORs chunks
+    auto wpos = [&](int k, int c) -> int {
+        if constexpr (FN == 1) return skinny_row(k) * RB + c * 16;
+        else if constexpr (FN == 2) return k * RB + ((c ^ (2 * ((k >> 3) & 1))) << 4);
+        else return k * RB + ((c ^ (2 * (((k >> 1) & 1) + 2 * ((k >> 3) & 1)))) << 4);
+    };
     auto issue = [&](int st, int kt) {
         char* As = smem + st * STAGE;
         char* Ws = As + A_BYTES;
         const int k0 = kt * BK;
 #pragma unroll
-        for (int u = 0; u < PA; ++u) {                  // 8 rows of A per 1 KB
+        for (int u = 0; u < PA; ++u) {
             const int row = 8 * u + (lane >> 3);
             const int c = (lane & 7) ^ swz_a(row);
             const int kk = k0 + 8 * c;
@@ -278,73 +290,93 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(const bf16_t* __restric
         }
         const int krows = min(BK, K - k0);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(W + (int64_t)k0 * ldw + n0), (short)0, (int)((int64_t)krows * ldw * 2),
-            RSRC_WORD3);
+            (void*)(W + (int64_t)k0 * ldw + n0), (short)0, (int)((int64_t)krows * ldw * 2), RSRC_WORD3);
 #pragma unroll
-        for (int u = 0; u < PW; ++u) {                  // 32 rows of the strip per 1 KB
-            const int kr = skinny_row(32 * u + (lane >> 1));    // logical row of this slot
-            const int pc = lane & 1;
+        for (int u = 0; u < PW; ++u) {
+            // physical slot: row pr, chunk pcpos; find which logical (k, c) lives there
+            const int pr = RPI * u + lane / LPR, pcpos = lane % LPR;
+            int kr, pc;
+            if constexpr (FN == 1) { kr = skinny_row(pr); pc = pcpos; }
+            else if constexpr (FN == 2) { kr = pr; pc = pcpos ^ (2 * ((pr >> 3) & 1)); }
+            else { kr = pr; pc = pcpos ^ (2 * (((pr >> 1) & 1) + 2 * ((pr >> 3) & 1))); }
             const int off = (kr < krows && n0 + 8 * pc < N) ? (kr * (int)ldw + 8 * pc) * 2 : OOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(Ws + u * 1024), 16, off, 0, 0, 0);
         }
     };
-
-    f32x4 acc[FM];
+    f32x4 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st)
         if (st < nk) issue(st, st);
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + NS - 2 < nk)
-            asm volatile("s_waitcnt vmcnt(%0)" :: "n"((NS - 2) * P) : "memory");
+        // refill the slot K-tile kt - 1 used (its fragments were consumed by
+        // the MFMAs of the previous iteration) before waiting on K-tile kt
+        if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
+        if (kt + NS - 1 < nk)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"((NS - 1) * P) : "memory");
         else
             wait_vm0();
         const char* As = smem + (kt % NS) * STAGE;
         const char* Ws = As + A_BYTES;
+        u32x2 p0[2][FN], p1[2][FN];
+        u32x4 a[2][FM];
 #pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
+        for (int ks = 0; ks < 2; ++ks) {
             const int k_lo = 32 * ks + 8 * g + (r >> 2), k_hi = k_lo + 4;
-            const int cb = ((r & 3) >> 1) * 16 + 8 * (r & 1);
-            u32x2 p0 = ds_read_tr_b64(Ws + skinny_row(k_lo) * 32 + cb);
-            u32x2 p1 = ds_read_tr_b64(Ws + skinny_row(k_hi) * 32 + cb);
-            u32x4 a[FM];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int c = 2 * j + ((r & 3) >> 1);
+                p0[ks][j] = ds_read_tr_b64(Ws + wpos(k_lo, c) + 8 * (r & 1));
+                p1[ks][j] = ds_read_tr_b64(Ws + wpos(k_hi, c) + 8 * (r & 1));
+            }
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int row = 16 * i + r;
-                a[i] = *reinterpret_cast<const u32x4*>(As + (row << 7) +
-                                                       (((4 * ks + g) ^ swz_a(row)) << 4));
+                a[ks][i] = *reinterpret_cast<const u32x4*>(As + (row << 7) + (((4 * ks + g) ^ swz_a(row)) << 4));
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(p0), "+v"(p1) : : "memory");
-            const u32x4 bf = u32x4{p0[0], p0[1], p1[0], p1[1]};
-#pragma unroll
-            for (int i = 0; i < FM; ++i) acc[i] = mfma16x16x32(a[i], bf, acc[i]);
         }
-        // the slot of K-tile kt - 1 was consumed by the MFMAs above: refill it
-        if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(p0[ks][j]), "+v"(p1[ks][j]) : : "memory");
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const u32x4 bf = u32x4{p0[ks][j][0], p0[ks][j][1], p1[ks][j][0], p1[ks][j][1]};
+#pragma unroll
+                for (int i = 0; i < FM; ++i) acc[i][j] = mfma16x16x32(a[ks][i], bf, acc[i][j]);
+            }
     }
-
-    const int col = n0 + r;
-    if (col >= N) return;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j) {
+        const int col = n0 + 16 * j + r;
+        if (col >= N) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * i + 4 * g + e;
-            if (row >= M) continue;
-            if (c_f32)
-                reinterpret_cast<float*>(C)[(int64_t)row * ldc + col] = acc[i][e];
-            else
-                reinterpret_cast<bf16_t*>(C)[(int64_t)row * ldc + col] = (bf16_t)f32_to_bf16(acc[i][e]);
-        }
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * i + 4 * g + e;
+                if (row >= M) continue;
+                if (c_f32)
+                    reinterpret_cast<float*>(C)[(int64_t)row * ldc + col] = acc[i][j][e];
+                else
+                    reinterpret_cast<bf16_t*>(C)[(int64_t)row * ldc + col] = (bf16_t)f32_to_bf16(acc[i][j][e]);
+            }
+    }
 }
 
-template <int FM, int NS>
+template <int FM, int FN, int NS>
 hipError_t launch_skinny(const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
                          int64_t ldc, int M, int N, int K, int c_f32, hipStream_t s) {
-    const int strips = (N + 15) / 16;
-    const int grid = (strips + 31) / 32 * 32;          // whole groups of 8 XCDs x 4 strips
-    hipLaunchKernelGGL((gemm_skinny_kernel<FM, NS>), dim3((unsigned)grid), dim3(64), 0, s,
+    const int strips = (N + 16 * FN - 1) / (16 * FN);
+    constexpr int GS = (FN >= 8) ? 1 : 8 / FN;
+    const int grid = (strips + 8 * GS - 1) / (8 * GS) * (8 * GS);
+    hipLaunchKernelGGL((gemm_skinny_kernel<FM, FN, NS>), dim3((unsigned)grid), dim3(64), 0, s,
                        (const bf16_t*)A, lda, (const bf16_t*)W, ldw, C, ldc, M, N, K, c_f32);
     return hipGetLastError();
 }
@@ -405,9 +437,19 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, v
     if (big_tiles >= 192)
         return launch_tile<BigTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
                                     c_f32, s);
-    if (M <= 16) return launch_skinny<1, 16>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
-    if (M <= 32) return launch_skinny<2, 12>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
-    if (M <= 64) return launch_skinny<4, 8>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
+    if (M <= 64) {
+        const int fn = (N / 64 >= 192) ? 4 : (N / 32 >= 192) ? 2 : 1;
+#define BINV_SKINNY(FM, NS1, NS2, NS4)                                                        \
+    switch (fn) {                                                                          \
+        case 4: return launch_skinny<FM, 4, NS4>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s); \
+        case 2: return launch_skinny<FM, 2, NS2>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s); \
+        default: return launch_skinny<FM, 1, NS1>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s); \
+    }
+        if (M <= 16) { BINV_SKINNY(1, 4, 6, 6) }
+        if (M <= 32) { BINV_SKINNY(2, 4, 4, 4) }
+        BINV_SKINNY(4, 4, 4, 4)
+#undef BINV_SKINNY
+    }
     return launch_tile<MidTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1, c_f32, s);
 }
 

@@ -104,12 +104,13 @@ def test_row0_bitwise_invariant_over_M(N, K):
         assert_bitwise_equal(c32, ref32, f"fp32 M={M}")
 
 
-@pytest.mark.parametrize("N,K", [(24, 72), (4104, 200), (4096, 4160), (136, 4096)])
+@pytest.mark.parametrize("N,K", [(24, 72), (4104, 200), (4096, 4160), (136, 4096), (6152, 200),
+                                 (14344, 136)])
 def test_kernels_chosen_by_shape_agree_bitwise(N, K):
-    # M <= 64 runs on 16-column strips, mid-size M on 128 x 128 tiles and
-    # large M x N on 256 x 256 tiles; every element must come out with the
-    # same bits on all of them, ragged N and K, zero and negative-zero rows
-    # against an all-negative column included
+    # M <= 64 runs on strips of 16, 32 or 64 columns (by N), mid-size M on
+    # 128 x 128 tiles and large M x N on 256 x 256 tiles; every element must
+    # come out with the same bits on all of them, ragged N and K, zero and
+    # negative-zero rows against an all-negative column included
     W = synth.normal((K, N), 0.02, 41 + N)
     W[:, 3] = -W[:, 3].abs() - 0.01
     W = W.to(DEV)
