@@ -87,11 +87,11 @@ int binv_rmsnorm(const void* x, int x_dt, int64_t ldx,
                  int64_t M, int64_t d, float eps, void* stream);
 
 /* ------------------------------------------------------------------------
- * GEMM with one fixed tile configuration and no split-K.
+ * GEMM with one fixed per-element reduction and no split-K.
  * Defines: devpress.csdn.net explainer, section 3.2 Matmul
- * (C[i,j] = sum_k A[i,k] B[k,j]; one kernel configuration for every batch
- * size, split-K disabled); tom-jerr.github.io "Batch-Invariant Kernel",
- * section GEMM (fixed tiling, K strategy decoupled from M).
+ * (C[i,j] = sum_k A[i,k] B[k,j]; the reduction of every element fixed for
+ * every batch size, split-K disabled); tom-jerr.github.io "Batch-Invariant
+ * Kernel", section GEMM (fixed tiling, K strategy decoupled from M).
  *
  *   C[i, j] = sum_k A[i, k] * W[k, j]
  *
@@ -99,7 +99,10 @@ int binv_rmsnorm(const void* x, int x_dt, int64_t ldx,
  * W  bf16 [K, N] row-major, leading dimension ldw
  * C  [M, N] row-major, leading dimension ldc, dtype c_dt (BINV_BF16 or BINV_F32)
  * Each C element is accumulated in fp32 by bf16 matrix-core instructions over
- * k in ascending blocks of 32, one accumulator per element, whatever M is.
+ * k in ascending blocks of 32 (K zero-padded to a multiple of 64), one
+ * accumulator per element, whatever M is.  Which lanes and workgroups carry
+ * which elements (the output tiling) follows the shape; it never enters an
+ * element's arithmetic, so a row's bits do not depend on M.
  * K and N must be multiples of 8; M, N, K <= 2^31 - 1; lda < 2^22 and
  * ldw < 1.6e7 elements (tiles are addressed with 32-bit offsets).  M = 0 or
  * N = 0 is a no-op; K = 0 writes zeros.  C must not overlap A or W.
