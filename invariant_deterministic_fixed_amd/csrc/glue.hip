@@ -139,20 +139,29 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ sr
 // ------------------------------------------------------------------ top-k
 // Exact top-K of one fp32 row: the K largest values, sorted by value
 // descending and, among equal values, by index ascending; NaN never selected.
-// One workgroup per row:
-//   1. each value maps to an order-preserving 32-bit key (NaN -> 0, below every
-//      other key); four 8-bit radix passes build histograms of the candidates'
-//      next byte and walk them from the top, which pins down the exact key T of
-//      the K-th largest entry and how many entries equal to T are needed.  The
-//      histograms are integer counts (LDS increments), whose totals do not
-//      depend on the order in which lanes add;
-//   2. one pass in index order (1024-element tiles, ballots and wave prefix
-//      counts) collects every entry with key > T and the lowest-index entries
-//      with key == T;
-//   3. the <= 32 winners are sorted by (value desc, index asc).
+// One workgroup per row.  Each value maps to an order-preserving 32-bit key
+// (NaN -> 0, below every other key; -0 and +0 one key).  Let T be the key of
+// the K-th largest entry: the result is every entry with key > T plus the
+// lowest-index entries with key == T, which is what both paths below select.
+//   fast path (two reads of the row):
+//     1. histogram of the keys' top byte (LDS increments: integer counts, so
+//        the totals do not depend on the order in which lanes add) -> the
+//        bucket b holding T and how many entries above it are winners;
+//     2. one pass in index order (1024-element tiles, ballots and wave prefix
+//        counts) keeps the entries above bucket b and gathers bucket b's
+//        entries, still in index order, into LDS;
+//     3. radix passes over bytes 2, 1, 0 of the gathered keys pin down T, and
+//        an index-ordered pass over them takes the keys > T and the first
+//        keys == T;
+//   fallback (a row with fewer than K non-NaN entries, or more than
+//   TOPK_CAND entries in bucket b): the same radix select over bytes 3..0 and
+//   the index-ordered collection, both reading the row.
+// The <= 32 winners are then sorted by (value desc, index asc).
 constexpr int TOPK_MAX = 32;
 constexpr int TOPK_NT = 1024;
 constexpr int TOPK_NW = TOPK_NT / 64;
+constexpr int TOPK_CAND = 4096;
+constexpr int TOPK_E = 8;            // entries per thread per tile in the gathering pass
 
 __device__ __forceinline__ uint32_t order_key(float v) {
     uint32_t b = __float_as_uint(v);
@@ -165,92 +174,223 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
 
-__global__ __launch_bounds__(TOPK_NT) void topk_kernel(const float* __restrict__ x, int64_t ldx,
-                                                       int64_t n, int K,
-                                                       int32_t* __restrict__ ids,
-                                                       float* __restrict__ vals) {
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t s_prefix, s_need;
-    __shared__ uint32_t w_gt[TOPK_NW], w_eq[TOPK_NW];
-    __shared__ float sel_v[TOPK_MAX];
-    __shared__ int sel_i[TOPK_MAX];
-    const int64_t r = blockIdx.x;
-    const float* row = x + r * ldx;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+struct TopkShared {
+    uint32_t hist[256];
+    uint32_t s_prefix, s_need;
+    uint32_t w_a[TOPK_NW], w_b[TOPK_NW];
+    uint32_t w_ea[TOPK_E][TOPK_NW], w_eb[TOPK_E][TOPK_NW];
+    float sel_v[TOPK_MAX];
+    int sel_i[TOPK_MAX];
+    float cand_v[TOPK_CAND];
+    int cand_i[TOPK_CAND];
+};
 
-    // ---- 1. radix select of the K-th largest key
-    uint32_t prefix = 0u, mask = 0u, need = (uint32_t)K;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (t < 256) hist[t] = 0u;
+// Radix select over `m` values read by get(j): keys with (key & mask) == prefix
+// are refined byte by byte, shifts `shift`, shift - 8, ..., `last`.  Returns
+// false if fewer than `need` such keys exist.  Otherwise prefix holds the
+// bytes fixed so far of the need-th largest key (all of T when last = 0) and
+// need how many entries with that prefix are still to be taken.  Every thread
+// returns the same values.
+template <class Get>
+__device__ bool radix_select(TopkShared& sh, Get get, int64_t m, int shift, int last,
+                             uint32_t& prefix, uint32_t& mask, uint32_t& need) {
+    const int t = threadIdx.x;
+    for (; shift >= last; shift -= 8) {
+        if (t < 256) sh.hist[t] = 0u;
         __syncthreads();
-        for (int64_t j = t; j < n; j += TOPK_NT) {
-            const uint32_t key = order_key(row[j]);
-            if (key != 0u && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        for (int64_t j0 = 0; j0 < m; j0 += (int64_t)TOPK_E * TOPK_NT) {
+            float v[TOPK_E];
+#pragma unroll
+            for (int e = 0; e < TOPK_E; ++e) {
+                const int64_t j = j0 + e * TOPK_NT + t;
+                v[e] = j < m ? get(j) : __uint_as_float(0x7fc00000u);
+            }
+#pragma unroll
+            for (int e = 0; e < TOPK_E; ++e) {
+                const uint32_t key = order_key(v[e]);
+                if (key != 0u && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+            }
         }
         __syncthreads();
         if (t == 0) {
             uint32_t cum = 0u, chosen = 0u, nd = need;
             bool found = false;
             for (int bkt = 255; bkt >= 0; --bkt) {
-                const uint32_t h = hist[bkt];
+                const uint32_t h = sh.hist[bkt];
                 if (cum + h >= need) { chosen = (uint32_t)bkt; nd = need - cum; found = true; break; }
                 cum += h;
             }
-            // fewer than `need` candidates left: every valid entry is selected
-            s_prefix = found ? (prefix | (chosen << shift)) : 0xffffffffu;
-            s_need = found ? nd : 0u;
+            sh.s_prefix = found ? (prefix | (chosen << shift)) : 0xffffffffu;
+            sh.s_need = found ? nd : 0u;
         }
         __syncthreads();
-        if (s_prefix == 0xffffffffu) { prefix = 0u; need = 0u; break; }
-        prefix = s_prefix;
-        need = s_need;
+        if (sh.s_prefix == 0xffffffffu) return false;
+        prefix = sh.s_prefix;
+        need = sh.s_need;
         mask |= 255u << shift;
     }
-    // T = prefix (key of the K-th entry) unless fewer than K valid entries exist
-    const bool short_row = (need == 0u);
-    const uint32_t T = short_row ? 1u : prefix;          // short row: take every key >= 1
-    const uint32_t n_eq_take = short_row ? (uint32_t)K : need;
+    return true;
+}
 
-    // ---- 2. collect winners in index order
+// One index-ordered pass over m values: entries whose key satisfies gt() go
+// to sel slots gt_base + (their rank), the first n_eq entries satisfying eq()
+// go to slots eq_base + rank.  Returns nothing; sel is complete afterwards.
+template <class Get, class Gt, class Eq>
+__device__ void collect(TopkShared& sh, Get get, int64_t m, Gt gt_of, Eq eq_of, uint32_t gt_base,
+                        uint32_t eq_base, uint32_t n_eq) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t run_gt = 0u, run_eq = 0u;
-    const uint32_t base_eq_slot = short_row ? 0u : (uint32_t)K - need;
-    if (t < TOPK_MAX) { sel_v[t] = -INFINITY; sel_i[t] = -1; }
-    __syncthreads();
-    for (int64_t j0 = 0; j0 < n; j0 += TOPK_NT) {
+    for (int64_t j0 = 0; j0 < m; j0 += TOPK_NT) {
         const int64_t j = j0 + t;
-        const uint32_t key = j < n ? order_key(row[j]) : 0u;
-        const bool gt = !short_row && key > T;
-        const bool eq = short_row ? key >= T : key == T;
+        const float v = j < m ? get(j) : 0.0f;
+        const uint32_t key = j < m ? order_key(v) : 0u;
+        const bool gt = gt_of(key), eq = eq_of(key);
         const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
-        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        if (lane == 0) { w_gt[wave] = __popcll(bgt); w_eq[wave] = __popcll(beq); }
+        if (lane == 0) { sh.w_a[wave] = __popcll(bgt); sh.w_b[wave] = __popcll(beq); }
         __syncthreads();
         uint32_t off_gt = run_gt, off_eq = run_eq, tot_gt = 0u, tot_eq = 0u;
         for (int w = 0; w < TOPK_NW; ++w) {
-            if (w < wave) { off_gt += w_gt[w]; off_eq += w_eq[w]; }
-            tot_gt += w_gt[w]; tot_eq += w_eq[w];
+            if (w < wave) { off_gt += sh.w_a[w]; off_eq += sh.w_b[w]; }
+            tot_gt += sh.w_a[w]; tot_eq += sh.w_b[w];
         }
         if (gt) {
-            const uint32_t slot = off_gt + __popcll(bgt & below);
-            if (slot < TOPK_MAX) { sel_v[slot] = row[j]; sel_i[slot] = (int)j; }
+            const uint32_t slot = gt_base + off_gt + __popcll(bgt & below);
+            if (slot < TOPK_MAX) { sh.sel_v[slot] = v; sh.sel_i[slot] = (int)j; }
         }
         if (eq) {
             const uint32_t k = off_eq + __popcll(beq & below);
-            if (k < n_eq_take && base_eq_slot + k < TOPK_MAX) {
-                sel_v[base_eq_slot + k] = row[j];
-                sel_i[base_eq_slot + k] = (int)j;
-            }
+            if (k < n_eq && eq_base + k < TOPK_MAX) { sh.sel_v[eq_base + k] = v; sh.sel_i[eq_base + k] = (int)j; }
         }
         run_gt += tot_gt;
         run_eq += tot_eq;
         __syncthreads();
     }
+}
 
-    // ---- 3. order the winners
+__global__ __launch_bounds__(TOPK_NT) void topk_kernel(const float* __restrict__ x, int64_t ldx,
+                                                       int64_t n, int K,
+                                                       int32_t* __restrict__ ids,
+                                                       float* __restrict__ vals) {
+    __shared__ TopkShared sh;
+    const int64_t r = blockIdx.x;
+    const float* row = x + r * ldx;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    auto from_row = [&](int64_t j) { return row[j]; };
+    if (t < TOPK_MAX) { sh.sel_v[t] = -INFINITY; sh.sel_i[t] = -1; }
+
+    // ---- 1. top byte
+    uint32_t prefix = 0u, mask = 0u, need = (uint32_t)K;
+    bool fast = radix_select(sh, from_row, n, 24, 24, prefix, mask, need);
+    const uint32_t top = prefix >> 24, gt1 = (uint32_t)K - need;
+
+    // ---- 2. winners above the bucket, the bucket's entries gathered in index
+    // order; tiles of E x 1024 entries, entry j0 + e * 1024 + t read by thread t
+    // (all E loads in flight at once), ranked in (e, t) = index order
+    uint32_t n_cand = 0u;
+    if (fast) {
+        constexpr int E = TOPK_E;
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        uint32_t run_gt = 0u, run_c = 0u;
+        for (int64_t j0 = 0; j0 < n; j0 += (int64_t)E * TOPK_NT) {
+            float v[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int64_t j = j0 + e * TOPK_NT + t;
+                v[e] = j < n ? row[j] : __uint_as_float(0x7fc00000u);   // NaN: never flagged
+            }
+            uint64_t bgt[E], bcd[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint32_t key = order_key(v[e]);
+                bgt[e] = __ballot(key != 0u && (key >> 24) > top);
+                bcd[e] = __ballot(key != 0u && (key >> 24) == top);
+                if (lane == 0) { sh.w_ea[e][wave] = __popcll(bgt[e]); sh.w_eb[e][wave] = __popcll(bcd[e]); }
+            }
+            __syncthreads();
+            uint32_t off_gt = run_gt, off_c = run_c;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                uint32_t pre_gt = 0u, pre_c = 0u, tot_gt = 0u, tot_c = 0u;
+                for (int w = 0; w < TOPK_NW; ++w) {
+                    if (w < wave) { pre_gt += sh.w_ea[e][w]; pre_c += sh.w_eb[e][w]; }
+                    tot_gt += sh.w_ea[e][w]; tot_c += sh.w_eb[e][w];
+                }
+                const int64_t j = j0 + e * TOPK_NT + t;
+                if ((bgt[e] >> lane) & 1ull) {
+                    const uint32_t slot = off_gt + pre_gt + __popcll(bgt[e] & below);
+                    if (slot < TOPK_MAX) { sh.sel_v[slot] = v[e]; sh.sel_i[slot] = (int)j; }
+                }
+                if ((bcd[e] >> lane) & 1ull) {
+                    const uint32_t c = off_c + pre_c + __popcll(bcd[e] & below);
+                    if (c < (uint32_t)TOPK_CAND) { sh.cand_v[c] = v[e]; sh.cand_i[c] = (int)j; }
+                }
+                off_gt += tot_gt;
+                off_c += tot_c;
+            }
+            run_gt = off_gt;
+            run_c = off_c;
+            __syncthreads();
+        }
+        n_cand = run_c;
+        fast = n_cand <= (uint32_t)TOPK_CAND;
+    }
+
+    if (fast) {
+        // ---- 3. bytes 2..0 over the gathered entries, then take them in index order
+        auto from_cand = [&](int64_t c) { return sh.cand_v[c]; };
+        radix_select(sh, from_cand, (int64_t)n_cand, 16, 0, prefix, mask, need);  // T: >= need entries
+        const uint32_t T = prefix;
+        // (the gt1 winners above the bucket are in sel slots [0, gt1) already)
+        {
+            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            uint32_t run_gt = 0u, run_eq = 0u;
+            for (int64_t c0 = 0; c0 < (int64_t)n_cand; c0 += TOPK_NT) {
+                const int64_t c = c0 + t;
+                const float v = c < (int64_t)n_cand ? sh.cand_v[c] : 0.0f;
+                const uint32_t key = c < (int64_t)n_cand ? order_key(v) : 0u;
+                const bool gt = key > T, eq = key == T && key != 0u;
+                const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
+                __syncthreads();                          // w_a / w_b of the last tile read
+                if (lane == 0) { sh.w_a[wave] = __popcll(bgt); sh.w_b[wave] = __popcll(beq); }
+                __syncthreads();
+                uint32_t off_gt = run_gt, off_eq = run_eq, tot_gt = 0u, tot_eq = 0u;
+                for (int w = 0; w < TOPK_NW; ++w) {
+                    if (w < wave) { off_gt += sh.w_a[w]; off_eq += sh.w_b[w]; }
+                    tot_gt += sh.w_a[w]; tot_eq += sh.w_b[w];
+                }
+                if (gt) {
+                    const uint32_t slot = gt1 + off_gt + __popcll(bgt & below);
+                    if (slot < TOPK_MAX) { sh.sel_v[slot] = v; sh.sel_i[slot] = sh.cand_i[c]; }
+                }
+                if (eq) {
+                    const uint32_t k = off_eq + __popcll(beq & below);
+                    const uint32_t slot = (uint32_t)K - need + k;
+                    if (k < need && slot < TOPK_MAX) { sh.sel_v[slot] = v; sh.sel_i[slot] = sh.cand_i[c]; }
+                }
+                run_gt += tot_gt;
+                run_eq += tot_eq;
+            }
+        }
+    } else {
+        // ---- fallback: full radix select and collection over the row
+        if (t < TOPK_MAX) { sh.sel_v[t] = -INFINITY; sh.sel_i[t] = -1; }
+        prefix = 0u; mask = 0u; need = (uint32_t)K;
+        const bool found = radix_select(sh, from_row, n, 24, 0, prefix, mask, need);
+        // a row with fewer than K valid entries: every valid entry is selected
+        const uint32_t T = found ? prefix : 1u;
+        const uint32_t n_eq = found ? need : (uint32_t)K;
+        const uint32_t eq_base = found ? (uint32_t)K - need : 0u;
+        collect(sh, from_row, n, [&](uint32_t k) { return found && k > T; },
+                [&](uint32_t k) { return found ? k == T : k >= T; }, 0u, eq_base, n_eq);
+    }
+    __syncthreads();
+
+    // ---- 4. order the winners
     if (t == 0) {
         float v[TOPK_MAX];
         int id[TOPK_MAX];
-        for (int k = 0; k < K; ++k) { v[k] = sel_v[k]; id[k] = sel_i[k]; }
+        for (int k = 0; k < K; ++k) { v[k] = sh.sel_v[k]; id[k] = sh.sel_i[k]; }
         // insertion sort; a missing entry (id -1) sorts after every real one
         for (int a = 1; a < K; ++a) {
             const float va = v[a];

@@ -78,19 +78,27 @@ def test_gather_rows_bit_copy():
 
 
 def test_topk_exact_with_ties_and_nan():
-    x = synth.normal((5, 128256), 3.0, 8, DEV, dtype=torch.float32)
+    x = synth.normal((7, 128256), 3.0, 8, DEV, dtype=torch.float32)
     x[1, 100:140] = 50.0                       # a block of ties above everything else
     x[2, 5] = float("nan")
     x[3, :] = -1.0                             # every entry tied
+    # distinct values that all share one exponent: more same-bucket entries than
+    # the kernel gathers, so it falls back to radix passes over the whole row
+    x[5] = 1.0 + torch.rand(128256, generator=torch.Generator(device=DEV).manual_seed(3),
+                            device=DEV)
+    # the 20th place falls inside a tie: 10 entries at 100, 30 tied at 99
+    x[6, 1000:1010] = 100.0
+    x[6, 5000:5030] = 99.0
     ids, vals = binv.topk(x, 20)
     xc = x.cpu().numpy()
-    for r in range(5):
+    for r in range(7):
         row = np.where(np.isnan(xc[r]), -np.inf, xc[r])
         want_ids, want_vals = od.topk(row, 20)
         np.testing.assert_array_equal(ids[r].cpu().numpy(), want_ids)
         np.testing.assert_array_equal(vals[r].cpu().numpy(), want_vals.astype(np.float32))
     assert ids[1].tolist() == list(range(100, 120))
     assert ids[3].tolist() == list(range(20))
+    assert ids[6].tolist() == list(range(1000, 1010)) + list(range(5000, 5010))
 
 
 def test_topk_signed_zero_and_short_rows():
