@@ -15,13 +15,17 @@
 // the chain at all (a row's slot in a tile only decides which lane carries
 // it), so the output tile can follow the shape without the bits following:
 //   * 256 x 256 tiles when that gives >= 192 tiles (large M),
-//   * 16-column strips for M <= 64 (decode batches; gemm_skinny_kernel),
-//   * 128 x 128 tiles otherwise.
+//   * strips of 16, 32 or 64 columns for M <= 64 (decode batches;
+//     gemm_skinny_kernel),
+//   * 128 x 128 tiles when that gives >= 192 tiles,
+//   * 64 x 64 tiles (4 waves of 32 x 32, four LDS stages) otherwise.
 // Tests check a row's bits across M = 1 .. 8192, i.e. across all three.  The
 // comparator below (128 x 128 with split-K chosen from the tile count) is the
 // one that does change with M.
 //
-// Tile kernel (256 x 256 shown; 128 x 128 is the same code with 4 waves):
+// Tile kernel (256 x 256 shown; 128 x 128 and 64 x 64 are the same code with
+// 4 waves, 64 x 64 with four LDS stages and 64-column W rows swizzled by
+// swz_w64):
 // 512 lanes = 8 waves in a 2 x 4 grid, each wave owning 128 x 64 outputs
 // (8 x 4 MFMA tiles, 128 fp32 accumulators per lane).  A and W travel
 // HBM -> LDS by buffer_load ... lds (16 bytes per lane, no registers,
@@ -59,6 +63,9 @@ constexpr int OOB = 0x7ffffff0;                // offset past any num_records: r
 
 __device__ __forceinline__ int swz_a(int r) { return r & 7; }
 __device__ __forceinline__ int swz_w(int k) { return 2 * ((k & 3) + 4 * ((k >> 3) & 1)); }
+// 64-column W tiles (rows of 128 bytes, 8 chunks): rows of one parity share a
+// bank group, so the chunk index is XORed with a function of bits 1 and 3 of k
+__device__ __forceinline__ int swz_w64(int k) { return 2 * (((k >> 1) & 1) + 2 * ((k >> 3) & 1)); }
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -77,7 +84,7 @@ __device__ __forceinline__ void tile_of(int i, int Mt, int Nt, int& tm, int& tn)
     tn = (t % per_group) / gsz;
 }
 
-template <int BM, int BN, int WGM, int WGN, int GROUP_M>
+template <int BM, int BN, int WGM, int WGN, int GROUP_M, int NS = 2>
 struct Tile {
     static constexpr int BM_ = BM, BN_ = BN;
     static constexpr int NW = WGM * WGN, NT = 64 * NW;
@@ -86,7 +93,11 @@ struct Tile {
     static constexpr int A_PW = A_BYTES / 1024 / NW, W_PW = W_BYTES / 1024 / NW;
     static constexpr int WROWS = 1024 / (BN * 2);        // W rows per 1 KB DMA instruction
     static_assert(A_PW * NW * 1024 == A_BYTES && W_PW * NW * 1024 == W_BYTES, "");
-    static_assert(BN >= 128 && BN <= 512, "");
+    static_assert(BN >= 64 && BN <= 512, "");
+    static constexpr int NS_ = NS;                       // LDS stages (K-tiles in flight + 1)
+    static constexpr int PW = A_PW + W_PW;               // DMA instructions per wave per stage
+    static_assert((NS - 2) * PW <= 63, "vmcnt holds 6 bits");
+    __device__ static int swzw(int k) { return BN == 64 ? swz_w64(k) : swz_w(k); }
 
     // DMA of K-tile kt into LDS stage `st`
     __device__ static void issue(char* smem, int st, int kt, const bf16_t* A, int64_t lda,
@@ -118,7 +129,7 @@ struct Tile {
             for (int u = 0; u < W_PW; ++u) {
                 const int j = wave * W_PW + u;
                 const int row = WROWS * j + lane / (BN / 8);
-                const int c = (lane % (BN / 8)) ^ swz_w(row);
+                const int c = (lane % (BN / 8)) ^ swzw(row);
                 const int off = (row < krows && n0 + 8 * c < N) ? (row * (int)ldw + 8 * c) * 2 : OOB;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(Ws + j * 1024), 16, off, 0, 0, 0);
             }
@@ -136,9 +147,9 @@ struct Tile {
                 const int c = (wn * TN + 16 * j + 4 * (r & 3)) >> 3;
                 const int k_lo = 32 * ks + 8 * g + (r >> 2), k_hi = k_lo + 4;
                 const v4i16 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16*)(Ws + k_lo * BN * 2 + ((c ^ swz_w(k_lo)) << 4) + 8 * (r & 1)));
+                    (lds_v4i16*)(Ws + k_lo * BN * 2 + ((c ^ swzw(k_lo)) << 4) + 8 * (r & 1)));
                 const v4i16 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16*)(Ws + k_hi * BN * 2 + ((c ^ swz_w(k_hi)) << 4) + 8 * (r & 1)));
+                    (lds_v4i16*)(Ws + k_hi * BN * 2 + ((c ^ swzw(k_hi)) << 4) + 8 * (r & 1)));
                 const u32x2 p0 = __builtin_bit_cast(u32x2, h0), p1 = __builtin_bit_cast(u32x2, h1);
                 b[j] = u32x4{p0[0], p0[1], p1[0], p1[1]};
             }
@@ -174,12 +185,26 @@ struct Tile {
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        if (kt_begin < kt_end) issue(smem, 0, kt_begin, A, lda, W, ldw, m0, n0, M, N, K, wave, lane);
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s)
+            if (kt_begin + s < kt_end)
+                issue(smem, s, kt_begin + s, A, lda, W, ldw, m0, n0, M, N, K, wave, lane);
         for (int kt = kt_begin; kt < kt_end; ++kt) {
-            const int st = (kt - kt_begin) & 1;
-            wait_vm0();                          // this wave's part of stage kt has landed
+            const int st = (kt - kt_begin) % NS;
+            // this wave's part of stage kt has landed (the NS - 2 later stages
+            // may still be in flight) ...
+            if constexpr (NS > 2) {
+                if (kt + NS - 2 < kt_end)
+                    asm volatile("s_waitcnt vmcnt(%0)" :: "n"((NS - 2) * PW) : "memory");
+                else
+                    wait_vm0();
+            } else {
+                wait_vm0();
+            }
             __builtin_amdgcn_s_barrier();        // ... and every wave's; stage kt-1 is free
-            if (kt + 1 < kt_end) issue(smem, st ^ 1, kt + 1, A, lda, W, ldw, m0, n0, M, N, K, wave, lane);
+            if (kt + NS - 1 < kt_end)
+                issue(smem, (kt - kt_begin + NS - 1) % NS, kt + NS - 1, A, lda, W, ldw, m0, n0, M,
+                      N, K, wave, lane);
             const char* As = smem + st * STAGE;
             compute(As, As + A_BYTES, acc, wm, wn, lane);
         }
@@ -383,6 +408,7 @@ hipError_t launch_skinny(const void* A, int64_t lda, const void* W, int64_t ldw,
 
 using BigTile = Tile<256, 256, 2, 4, 8>;
 using MidTile = Tile<128, 128, 2, 2, 8>;         // also the comparator's tile
+using SmallTile = Tile<64, 64, 2, 2, 8, 4>;      // 4 waves of 32 x 32, four stages
 
 template <class T>
 __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(const bf16_t* __restrict__ A, int64_t lda,
@@ -390,7 +416,7 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(const bf16_t* __restri
                                                           void* __restrict__ C, int64_t ldc,
                                                           int64_t split_stride, int M, int N, int K,
                                                           int kt_per_split, int c_f32) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[T::NS_ * T::STAGE];
     T::run(A, lda, W, ldw, C, ldc, split_stride, M, N, K, kt_per_split, c_f32, smem);
 }
 
@@ -423,9 +449,10 @@ hipError_t launch_tile(const void* A, int64_t lda, const void* W, int64_t ldw, v
 
 }  // namespace
 
-// Which kernel computes the outputs is chosen from the shape (the 256 x 256
-// tile once it gives at least 192 tiles, i.e. fills most of the 256 CUs;
-// else 16-column strips for M <= 64; else 128 x 128 tiles).  All three run
+// Which kernel computes the outputs is chosen from the shape: the 256 x 256
+// tile once it gives at least 192 tiles (fills most of the 256 CUs); else
+// strips for M <= 64; else 128 x 128 tiles if they give at least 192; else
+// 64 x 64 tiles.  All of them run
 // the same per-element arithmetic -- one accumulator, one MFMA chain over the
 // same ascending 32-wide k-blocks and the same zero-padded K-tiles of 64 --
 // so the choice, and with it M, never reaches the bits.
@@ -437,7 +464,15 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, v
     if (big_tiles >= 192)
         return launch_tile<BigTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
                                     c_f32, s);
-    if (M <= 64) {
+    if (M > 64) {
+        const int64_t mid_tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+        if (mid_tiles >= 192)
+            return launch_tile<MidTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
+                                        c_f32, s);
+        return launch_tile<SmallTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
+                                      c_f32, s);
+    }
+    {
         const int fn = (N / 64 >= 192) ? 4 : (N / 32 >= 192) ? 2 : 1;
 #define BINV_SKINNY(FM, NS1, NS2, NS4)                                                        \
     switch (fn) {                                                                          \
@@ -450,7 +485,7 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, v
         BINV_SKINNY(4, 4, 4, 4)
 #undef BINV_SKINNY
     }
-    return launch_tile<MidTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1, c_f32, s);
+    return hipErrorInvalidValue;        // not reached
 }
 
 // Comparator: split-K whose split count is chosen from the number of output

@@ -121,7 +121,7 @@ def test_kernels_chosen_by_shape_agree_bitwise(N, K):
     Ad = A.to(DEV)
     ref32 = binv.gemm(Ad, W, out_dtype=torch.float32)
     ref16 = binv.gemm(Ad, W)
-    for M in [1, 7, 16, 17, 32, 33, 64, 65, 130]:
+    for M in [1, 7, 16, 17, 32, 33, 64, 65, 130, 300]:
         assert_bitwise_equal(binv.gemm(Ad[:M], W, out_dtype=torch.float32), ref32[:M], f"fp32 M={M}")
         assert_bitwise_equal(binv.gemm(Ad[:M], W), ref16[:M], f"bf16 M={M}")
 
