@@ -181,3 +181,24 @@ def test_config5_prefix_cache_reuse(full):
     cfg, pool, d = full
     prefix_reuse_case(d, pool, cfg["vocab"], n_prefix=512, n_a=64, n_b=48, n_new=16, seed=5,
                       chunk=100)
+
+
+def test_config5_tuned_comparators_are_not_invariant(full):
+    # positive control for the whole decoder: the same weights and schedule with
+    # the shape-tuned comparators (split-K GEMM chosen from M, RMSNorm block size
+    # chosen from M, split-by-batch decode attention) must change the target's
+    # logits bits when neighbours join its batch
+    cfg, pool, d = full
+    tuned = dec.Decoder(d.w, cfg, pool, max_tokens=d.max_tokens, max_seqs=d.max_seqs,
+                        max_kv_len=d.max_kv_len, tuned=True)
+    r = np.random.default_rng(42)
+    prompt = r.integers(0, cfg["vocab"], 512).tolist()
+    alone = harness.run(tuned, pool, prompt, 8, seed=0, record_logits=True)
+    rr = np.random.default_rng(77)
+    nbrs = [rr.integers(0, cfg["vocab"], int(rr.integers(16, 600))).tolist() for _ in range(7)]
+    got = harness.run(tuned, pool, prompt, 8, neighbours=nbrs, budget=512, seed=1,
+                      record_logits=True)
+    differ = [not torch.equal(a.view(torch.int32), b.view(torch.int32))
+              for a, b in zip(alone["logits"], got["logits"])]
+    print("tuned decoder, logits differ per step:", differ, flush=True)
+    assert any(differ)
