@@ -397,18 +397,22 @@ def sweep(dev="cuda:0"):
     del c, q, out, ws
     torch.cuda.empty_cache()
 
-    # 8B-class decoder: decode tokens/s at batch B with 1024-token contexts
+    # 8B-class decoder: decode tokens/s at batch B with 1024-token contexts, all
+    # invariant, all tuned, and one locked request among tuned neighbours
     cfg = dec.CONFIG5
     w = dec.random_weights(cfg, 5, dev)
     for B in [1, 16, 64]:
         res = {}
-        for tuned in (False, True):
+        for mode in ("invariant", "tuned", "locked"):
+            if mode == "locked" and B == 1:
+                continue
             pool = dec.KVPool(cfg, num_pages=B * (1024 + 64) // 16 + B, max_seqs=B,
                               max_len=1024 + 64, seed=11, device=dev)
             d = dec.Decoder(w, cfg, pool, max_tokens=max(1024, B), max_seqs=B,
-                            max_kv_len=1024 + 64, tuned=tuned)
+                            max_kv_len=1024 + 64, tuned=(mode == "tuned"))
             r = np.random.default_rng(42)
             slots = [pool.alloc() for _ in range(B)]
+            prot = {slots[0]} if mode == "locked" else None
             toks = {}
             for sl in slots:                          # prefill, untimed
                 _, ids, _ = d.step([(sl, r.integers(0, cfg["vocab"], 1024).tolist(), 0)])
@@ -417,17 +421,19 @@ def sweep(dev="cuda:0"):
             steps = 8
             t0 = time.perf_counter()
             for k in range(steps):
-                _, ids, _ = d.step([(sl, [toks[sl]], 1024 + k) for sl in slots])
+                _, ids, _ = d.step([(sl, [toks[sl]], 1024 + k) for sl in slots], protected=prot)
                 ids = ids.cpu()
                 for i, sl in enumerate(slots):
                     toks[sl] = int(ids[i, 0])
             torch.cuda.synchronize()
-            res[tuned] = B * steps / (time.perf_counter() - t0)
+            res[mode] = B * steps / (time.perf_counter() - t0)
             del d, pool
             torch.cuda.empty_cache()
-        emit(sweep="decoder_8b_decode", B=B, context=1024, invariant_tokens_per_s=round(res[False], 1),
-             tuned_tokens_per_s=round(res[True], 1),
-             slowdown_vs_tuned=round(res[True] / res[False], 3))
+        emit(sweep="decoder_8b_decode", B=B, context=1024,
+             invariant_tokens_per_s=round(res["invariant"], 1),
+             tuned_tokens_per_s=round(res["tuned"], 1),
+             locked_one_tokens_per_s=round(res["locked"], 1) if "locked" in res else None,
+             slowdown_vs_tuned=round(res["tuned"] / res["invariant"], 3))
 
 
 def main():

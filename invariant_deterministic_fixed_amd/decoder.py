@@ -121,7 +121,14 @@ class Decoder:
     split-K GEMM and block-size-by-M RMSNorm everywhere, and the split-by-batch
     decode attention on steps where every sequence brings one token; prefill
     steps keep the invariant attention, the only prefill kernel there is.  It
-    exists to measure what invariance costs."""
+    exists to measure what invariance costs.
+
+    step(items, protected=slots) is selective locking (the BlockLock post's
+    per-request locking, BlockLock modes): the rows of the protected sequences
+    run through the invariant RMSNorm and GEMM, every other row through the
+    tuned comparators, and attention stays invariant for all.  A protected
+    sequence's bits are then those of an all-invariant run; the others'
+    are not batch-invariant."""
 
     def __init__(self, weights, cfg, pool, max_tokens, max_seqs, max_kv_len, topk=20,
                  tuned=False):
@@ -147,11 +154,19 @@ class Decoder:
         self.logits = torch.empty((max_seqs, cfg["vocab"]), dtype=torch.float32, device=dev)
         self.max_tokens, self.max_seqs = T, max_seqs
 
-    def step(self, items):
+    def step(self, items, protected=None):
         """items: list of (slot, new token ids, start position).  Returns
         (logits fp32 [n, V], top ids int32 [n, k], top values fp32 [n, k]) for
-        the last token of each item, as device tensors, in item order."""
+        the last token of each item, as device tensors, in item order.
+        protected: a set of slots to run locked (see the class note)."""
         cfg, pool, dev = self.cfg, self.pool, self.pool.device
+        order = None
+        if protected is not None:
+            # protected sequences first, so their rows form one leading block
+            order = sorted(range(len(items)), key=lambda i: items[i][0] not in protected)
+            items = [items[i] for i in order]
+            n_prot = sum(1 for slot, _, _ in items if slot in protected)
+            t_prot = sum(len(t) for _, t, _ in items[:n_prot])
         H, Hq, Hkv, D, F = (cfg["hidden"], cfg["n_heads"], cfg["n_kv"], cfg["head_dim"],
                             cfg["ffn"])
         # sequence b of this step reads row b of the step's page table: the
@@ -183,10 +198,31 @@ class Decoder:
         scale = 1.0 / math.sqrt(D)
         tn = self.tuned
         decode_only = tn and max_q == 1
+        locked = protected is not None
+
+        def split(n_lead):
+            # (rows, tuned) blocks: leading protected rows invariant, the rest tuned
+            if not locked:
+                return [(slice(0, None), tn)]
+            return [(sl, t) for sl, t, n in ((slice(0, n_lead), False, n_lead),
+                                             (slice(n_lead, None), True, 1)) if n > 0]
+
+        rows_tok = split(t_prot if locked else 0)
+
+        def norm(src, dst, blocks):
+            for sl, t in blocks:
+                if src[sl].shape[0]:
+                    B.rmsnorm(src[sl], self.w["norm"], cfg["eps"], out=dst[sl], tuned=t)
+
+        def mm(src, wt, dst, blocks):
+            for sl, t in blocks:
+                if src[sl].shape[0]:
+                    B.gemm(src[sl], wt, out=dst[sl], tuned=t)
+
         B.embed(ids_d, self.w["embed"], out=h)
         for li, lw in enumerate(self.w["layers"]):
-            B.rmsnorm(h, self.w["norm"], cfg["eps"], out=x, tuned=tn)
-            B.gemm(x, lw["wqkv"], out=qkv, tuned=tn)
+            norm(h, x, rows_tok)
+            mm(x, lw["wqkv"], qkv, rows_tok)
             B.rope_kv_write(qkv, tseq_d, tpos_d, Hq, Hkv, D, cfg["theta"], pool.k[li], pool.v[li],
                             table, q_out=q)
             if decode_only:
@@ -195,16 +231,20 @@ class Decoder:
             else:
                 B.attn_prefill(q, cu_d, pool.k[li], pool.v[li], table, lens_d, max_q,
                                self.max_kv_len, scale, out=a, workspace=self.ws)
-            B.gemm(a.view(T, Hq * D), lw["wo"], out=o, tuned=tn)
+            mm(a.view(T, Hq * D), lw["wo"], o, rows_tok)
             B.residual_add(h, o)
-            B.rmsnorm(h, self.w["norm"], cfg["eps"], out=x, tuned=tn)
-            B.gemm(x, lw["wgu"], out=gu, tuned=tn)
+            norm(h, x, rows_tok)
+            mm(x, lw["wgu"], gu, rows_tok)
             B.swiglu(gu, out=s)
-            B.gemm(s, lw["wd"], out=o, tuned=tn)
+            mm(s, lw["wd"], o, rows_tok)
             B.residual_add(h, o)
         hl, xl, logits = self.hl[:nb], self.xl[:nb], self.logits[:nb]
+        rows_seq = split(n_prot if locked else 0)
         B.gather_rows(h, last_d, out=hl)
-        B.rmsnorm(hl, self.w["norm"], cfg["eps"], out=xl, tuned=tn)
-        B.gemm(xl, self.w["lm_head"], out=logits, tuned=tn)
+        norm(hl, xl, rows_seq)
+        mm(xl, self.w["lm_head"], logits, rows_seq)
         top_ids, top_vals = B.topk(logits, self.topk)
+        if order is not None:                     # back to the caller's item order
+            inv = torch.as_tensor(np.argsort(order), device=dev)
+            return logits[inv], top_ids[inv], top_vals[inv]
         return logits, top_ids, top_vals

@@ -27,10 +27,12 @@ class Seq:
 
 
 def run(decoder, pool, target_prompt, n_new, neighbours=(), budget=None, seed=0,
-        record_logits=False):
+        record_logits=False, lock_target=False):
     """Greedy-decode `n_new` tokens of the target (slot order and batch order
     randomised by `seed`).  neighbours: list of prompts, each decoded greedily
     alongside.  budget: max prompt tokens per step (None: whole prompts at once).
+    lock_target: run the target locked and everyone else on the tuned
+    comparators (Decoder.step's selective locking).
     Returns a dict with the target's tokens, top-20 ids / values per token
     (host tensors) and, if asked, the full logits rows."""
     rng = np.random.default_rng(int(seed))
@@ -64,7 +66,8 @@ def run(decoder, pool, target_prompt, n_new, neighbours=(), budget=None, seed=0,
         perm = rng.permutation(len(items))
         items = [items[i] for i in perm]
         owners = [owners[i] for i in perm]
-        logits, top_ids, top_vals = decoder.step(items)
+        logits, top_ids, top_vals = decoder.step(
+            items, protected={target.slot} if lock_target else None)
         ids_h = top_ids.cpu()
         for k, (s, kind, n) in enumerate(owners):
             if kind == "prefill":

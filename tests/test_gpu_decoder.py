@@ -128,6 +128,18 @@ def test_small_decoder_prefix_cache_reuse(small):
                       chunk=13)
 
 
+def test_small_decoder_selective_locking(small):
+    # the target locked (invariant kernels on its rows) beside neighbours on the
+    # tuned comparators gives the bits of the all-invariant target run alone
+    _, pool, d, _ = small
+    r = np.random.default_rng(13)
+    prompt = r.integers(0, SMALL["vocab"], 70).tolist()
+    alone = harness.run(d, pool, prompt, 12, seed=0)
+    nbrs = [r.integers(0, SMALL["vocab"], int(r.integers(5, 200))).tolist() for _ in range(6)]
+    got = harness.run(d, pool, prompt, 12, neighbours=nbrs, budget=64, seed=3, lock_target=True)
+    assert harness.same_bits(got, alone)
+
+
 def test_small_decoder_invariance_with_neighbours(small):
     w, pool, d, _ = small
     r = np.random.default_rng(3)
@@ -202,3 +214,14 @@ def test_config5_tuned_comparators_are_not_invariant(full):
               for a, b in zip(alone["logits"], got["logits"])]
     print("tuned decoder, logits differ per step:", differ, flush=True)
     assert any(differ)
+
+
+def test_config5_selective_locking(full):
+    cfg, pool, d = full
+    r = np.random.default_rng(42)
+    prompt = r.integers(0, cfg["vocab"], 512).tolist()
+    alone = harness.run(d, pool, prompt, 12, seed=0)
+    rr = np.random.default_rng(91)
+    nbrs = [rr.integers(0, cfg["vocab"], int(rr.integers(16, 2000))).tolist() for _ in range(15)]
+    got = harness.run(d, pool, prompt, 12, neighbours=nbrs, budget=512, seed=4, lock_target=True)
+    assert harness.same_bits(got, alone)
