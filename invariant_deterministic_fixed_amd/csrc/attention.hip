@@ -51,15 +51,48 @@ namespace binv {
 namespace {
 using namespace attn;
 
-// Grid: x = (query tile, KV head), y = chunk lane, z = sequence.  With LOOP,
-// workgroup (x, y, z) takes the chunks c = y, y + gridDim.y, ... that reach
-// the tile's last position, so a grid sized for the longest allowed sequence
-// does not spend one workgroup launch per chunk slot of every short
-// sequence; without it, gridDim.y is the chunk count and the workgroup takes
-// chunk y alone.  Which workgroup takes a chunk does not enter the chunk's
-// arithmetic.  R = row tiles of 16 rows per workgroup (1 for decode, 2 for
-// prefill at D = 128).
-template <int D, int G, int R, bool LOOP>
+// workgroups per (query tile, KV head) of a decode sequence; they loop over
+// the sequence's nodes
+constexpr int CHUNK_LANES = 16;
+
+// Level of the merge tree at which a decode row's partials are handed from
+// the chunk kernel to the merge kernel, from the row's chunk count n: the
+// level that keeps the longest chain of chunks one workgroup computes in
+// sequence, ceil(n / (CHUNK_LANES 2^L)) 2^L, shortest, and among those the
+// highest (fewest partials).  Both kernels evaluate it for the row; the root
+// is the same for every level.
+template <int GMAX>
+__device__ __forceinline__ int node_level(int n) {
+    int best = 0, best_chain = (n + CHUNK_LANES - 1) / CHUNK_LANES;
+#pragma unroll
+    for (int L = 1; L <= GMAX; ++L) {
+        const int per = CHUNK_LANES << L;
+        const int chain = ((n + per - 1) / per) << L;
+        if (chain <= best_chain) { best = L; best_chain = chain; }
+    }
+    return best;
+}
+
+// Grid: x = (query tile, KV head), y = lane, z = sequence.
+//
+// Decode (R = 1, no cu_q) workgroups write nodes of the merge tree at level
+// L = node_level(n): node j covers the aligned chunks [2^L j, 2^L (j + 1)).
+// Workgroup (x, y, z) takes the nodes j = y, y + gridDim.y, ... that reach
+// the sequence's position; for each it computes the node's chunks in order
+// and merges them with the merge kernel's binary counter and combine, so the
+// node is the subtree value that kernel would have formed from the leaves (a
+// node's chunks past the sequence end are identity leaves, which leave a
+// subtree unchanged).  Which workgroup takes a node, and the level at which
+// the tree is handed over, do not enter any row's arithmetic; a higher level
+// writes and re-reads fewer partials.  gridDim.y is capped at CHUNK_LANES, so
+// a grid sized for the longest allowed sequence does not spend a workgroup
+// per empty node slot of every short sequence.
+// Prefill (cu_q given; R = 2 at D = 128): leaves (L = 0); without looping
+// gridDim.y = the chunk count and a workgroup takes chunk y alone.
+//
+// Partials: slot (token * n_chunks + node) * Hq + head of ws_o [.., D] and
+// ws_ml [..] (the G heads of one tile are adjacent).
+template <int D, int G, int R, bool LOOP, int GMAX>
 __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chunk_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
@@ -68,39 +101,80 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     float2* __restrict__ ws_ml, int Hq, int Hkv, int n_chunks, int max_kv_len,
     float scale_log2) {
     constexpr bool VL = (R == 1);           // V through LDS for single-tile (decode) workgroups
+    static_assert(LOOP || GMAX == 0, "workgroups that take one chunk write leaves");
     __shared__ ChunkLds<D, R, VL> sh;
     constexpr int JT = ChunkShape<D>::JT;
-    // page-table entries of the first chunk: in bounds whatever kv_len is
-    // (row b, entries < pt_stride), so they are read alongside kv_lens rather
-    // than after it; later chunks' entries are read one chunk ahead
+    const int kv_len_b = kv_lens[blockIdx.z];          // read once, kept in a register
+    const int pos_max = tile_ctx_len<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
+                                           kv_len_b, pt_stride, max_kv_len).pos_max;
+    const int glog = (GMAX > 0 && !cu_q && pos_max >= 0) ? node_level<GMAX>(pos_max / CHUNK + 1) : 0;
+    const int gs = 1 << glog;
     int phys_next[JT];
     {
         TileCtx x0;
         x0.pt_row = (int64_t)blockIdx.z * pt_stride;
-        load_phys<D>(x0, blockIdx.y, page_table, pt_stride, phys_next, threadIdx.x);
+        load_phys<D>(x0, blockIdx.y * gs, page_table, pt_stride, phys_next, threadIdx.x);
     }
-    const int pos_max = tile_ctx<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
-                                       kv_lens, pt_stride, max_kv_len).pos_max;
 #pragma clang loop unroll(disable)
-    for (int c = blockIdx.y; c * CHUNK <= pos_max; c += gridDim.y) {
-        // the tile context, q fragments, row maps and lane-derived addresses
-        // are re-derived per chunk (cache hits and a few ALU operations)
-        // rather than held live across chunks, which would spill
-        asm volatile("" ::: "memory");
+    for (int node = blockIdx.y; node * gs * CHUNK <= pos_max; node += gridDim.y) {
+        ChunkOut<R> slot[GMAX + 1];
+        unsigned count = 0;
+#pragma clang loop unroll(disable)
+        for (int i = 0; i < gs; ++i) {
+            const int c = node * gs + i;
+            if (c * CHUNK > pos_max) break;
+            // the tile context, q fragments, row maps and lane-derived
+            // addresses are re-derived per chunk (a few ALU operations and
+            // cache hits) rather than held live across chunks, which would spill
+            asm volatile("" ::: "memory");
+            int t = threadIdx.x;
+            if constexpr (LOOP) asm volatile("" : "+v"(t));
+            const TileCtx x = tile_ctx_len<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv,
+                                                 cu_q, kv_len_b, pt_stride, max_kv_len);
+            int phys[JT];
+#pragma unroll
+            for (int u = 0; u < JT; ++u) phys[u] = phys_next[u];
+            if constexpr (LOOP) {
+                // page-table entries of the next chunk this workgroup takes
+                const int c_next = (i + 1 < gs) ? c + 1 : (node + (int)gridDim.y) * gs;
+                if (c_next * CHUNK <= pos_max)
+                    load_phys<D>(x, c_next, page_table, pt_stride, phys_next, t);
+            }
+            ChunkOut<R> carry = chunk_compute<D, G, R, VL>(x, c, phys, page_table, q, kc, vc,
+                                                           pt_stride, Hq, Hkv, scale_log2, sh, t);
+            // binary increment: equal-size subtrees merge, the older one on the left
+            bool live = true;
+#pragma unroll
+            for (int s = 0; s <= GMAX; ++s) {
+                if (live) {
+                    if (count & (1u << s)) {
+                        carry = combine_out<R>(slot[s], carry);
+                    } else {
+                        slot[s] = carry;
+                        live = false;
+                    }
+                }
+            }
+            ++count;
+            if constexpr (LOOP) __syncthreads();           // LDS free for the next chunk
+        }
+        // the node: remaining subtrees, smallest (rightmost) first
+        ChunkOut<R> r = slot[0];
+        bool have = false;
+#pragma unroll
+        for (int s = 0; s <= GMAX; ++s) {
+            if (count & (1u << s)) {
+                if (!have) { r = slot[s]; have = true; }
+                else r = combine_out<R>(slot[s], r);
+            }
+        }
         int t = threadIdx.x;
         if constexpr (LOOP) asm volatile("" : "+v"(t));
         const int lane = t & 63, wave = t >> 6, ag = lane >> 4;
-        const TileCtx x = tile_ctx<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
-                                         kv_lens, pt_stride, max_kv_len);
-        int phys[JT];
-#pragma unroll
-        for (int u = 0; u < JT; ++u) phys[u] = phys_next[u];
-        if (LOOP && (c + (int)gridDim.y) * CHUNK <= pos_max)
-            load_phys<D>(x, c + gridDim.y, page_table, pt_stride, phys_next, t);
-        const ChunkOut<R> r = chunk_compute<D, G, R, VL>(x, c, phys, page_table, q, kc, vc,
-                                                         pt_stride, Hq, Hkv, scale_log2, sh, t);
-        const int j0 = c * CHUNK;
-        // partials of the rows that see at least one key of this chunk
+        const TileCtx x = tile_ctx_len<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
+                                             kv_len_b, pt_stride, max_kv_len);
+        const int j0 = node * gs * CHUNK;
+        // partials of the rows that see at least one key of this node
 #pragma unroll
         for (int rt = 0; rt < R; ++rt)
 #pragma unroll
@@ -108,23 +182,22 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
                 const RowInfo ri = row_info<G, R>(16 * rt + 4 * ag + e, x.b, x.g, x.qt, x.q_len,
                                                   x.q_start, x.kv_len);
                 if (ri.token < 0 || ri.pos < j0) continue;
-                const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)n_chunks + c;
-                ws_o[slot * D + 16 * wave + (lane & 15)] = r.o[rt][e];
+                const int64_t slot_i = (ri.token * (int64_t)n_chunks + node) * Hq + ri.head;
+                ws_o[slot_i * D + 16 * wave + (lane & 15)] = r.o[rt][e];
             }
         if (t < 256 * R && (t & 15) == 0) {
             const RowInfo ri = row_info<G, R>(t >> 4, x.b, x.g, x.qt, x.q_len, x.q_start, x.kv_len);
             if (ri.token >= 0 && ri.pos >= j0) {
-                const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)n_chunks + c;
-                ws_ml[slot] = make_float2(r.ml_m, r.l);
+                const int64_t slot_i = (ri.token * (int64_t)n_chunks + node) * Hq + ri.head;
+                ws_ml[slot_i] = make_float2(r.ml_m, r.l);
             }
         }
         if constexpr (!LOOP) break;
-        __syncthreads();                    // LDS free for the next chunk
     }
 }
 
 // One wave per (token, head) row; lane owns features lane (+ 64).
-template <int D>
+template <int D, int GMAX>
 __global__ __launch_bounds__(NT) void attn_merge_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ kv_lens, int64_t B,
     int64_t n_tokens, int Hq, int n_chunks, int max_kv_len,
@@ -160,11 +233,17 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
         for (int i = 0; i < NO; ++i) orow[lane + 64 * i] = 0;
         return;
     }
-    int n = pos / CHUNK + 1;
-    if (n > n_chunks) n = n_chunks;
+    // the row's pos / CHUNK + 1 chunks arrive as nodes of the level the chunk
+    // kernel chose for it (leaves for prefill rows)
+    int n_leaf = pos / CHUNK + 1;
+    if (n_leaf > n_chunks) n_leaf = n_chunks;
+    const int glog = (GMAX > 0 && !cu_q) ? node_level<GMAX>(n_leaf) : 0;
+    const int n = ((n_leaf - 1) >> glog) + 1;
 
-    const float* po = ws_o + row * (int64_t)n_chunks * D;
-    const float2* pml = ws_ml + row * (int64_t)n_chunks;
+    // node c of the row: slot (token * n_chunks + c) * Hq + head
+    const int64_t slot0 = token * (int64_t)n_chunks * Hq + (row - token * Hq);
+    const float* po = ws_o + slot0 * D;
+    const float2* pml = ws_ml + slot0;
 
     Partial slot[STACK];
     unsigned count = 0;
@@ -177,10 +256,10 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
         for (int k = 0; k < GRP; ++k) {
             const int c = c0 + k;
             if (c < n) {
-                const float2 ml = pml[c];
+                const float2 ml = pml[(int64_t)c * Hq];
                 dst[k].m = ml.x; dst[k].l = ml.y;
 #pragma unroll
-                for (int i = 0; i < NO; ++i) dst[k].o[i] = po[(int64_t)c * D + lane + 64 * i];
+                for (int i = 0; i < NO; ++i) dst[k].o[i] = po[(int64_t)c * Hq * D + lane + 64 * i];
             }
         }
     };
@@ -226,11 +305,11 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
     }
 }
 
-// workgroups per (query tile, KV head) when they loop over chunks: a sequence
-// of n chunks is covered in ceil(n / CHUNK_LANES) rounds
-constexpr int CHUNK_LANES = 16;
+#ifndef BINV_DECODE_GMAX
+#define BINV_DECODE_GMAX 1
+#endif
 
-template <int D, int G, int R>
+template <int D, int G, int R, bool LOOP, int GMAX>
 hipError_t launch_dgr(const AttnArgs& a, hipStream_t s) {
     constexpr int TQ = ROWS * R / G;
     const int n_chunks = (int)((a.max_kv_len + CHUNK - 1) / CHUNK);
@@ -238,31 +317,31 @@ hipError_t launch_dgr(const AttnArgs& a, hipStream_t s) {
     const int64_t Rows = a.n_tokens * a.Hq;
     float* ws_o = a.ws;
     float2* ws_ml = reinterpret_cast<float2*>(a.ws + Rows * n_chunks * a.D);
-    // decode workgroups (R = 1) loop over their sequence's chunks; prefill
-    // tiles already fill the machine with one chunk per workgroup
-    constexpr bool LOOP = (R == 1);
     dim3 grid1((unsigned)(nqt * a.Hkv),
                (unsigned)(LOOP && n_chunks > CHUNK_LANES ? CHUNK_LANES : n_chunks), (unsigned)a.B);
-    hipLaunchKernelGGL((attn_chunk_kernel<D, G, R, LOOP>), grid1, dim3(ChunkShape<D>::NTH), 0, s,
-                       (const bf16_t*)a.q, a.cu_q, (const bf16_t*)a.k_cache,
+    hipLaunchKernelGGL((attn_chunk_kernel<D, G, R, LOOP, GMAX>), grid1, dim3(ChunkShape<D>::NTH),
+                       0, s, (const bf16_t*)a.q, a.cu_q, (const bf16_t*)a.k_cache,
                        (const bf16_t*)a.v_cache, a.page_table, a.pt_stride, a.kv_lens, ws_o,
                        ws_ml, a.Hq, a.Hkv, n_chunks, (int)a.max_kv_len, a.scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid2((unsigned)((Rows + 3) / 4));
-    hipLaunchKernelGGL((attn_merge_kernel<D>), grid2, dim3(NT), 0, s, a.cu_q, a.kv_lens, a.B,
+    hipLaunchKernelGGL((attn_merge_kernel<D, GMAX>), grid2, dim3(NT), 0, s, a.cu_q, a.kv_lens, a.B,
                        a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len, (const float*)ws_o,
                        (const float2*)ws_ml, (bf16_t*)a.out);
     return hipGetLastError();
 }
 
-// decode: one token per sequence, one row tile; prefill: two row tiles at D = 128
+// decode: one token per sequence, one row tile, looping workgroups, nodes up
+// to level BINV_DECODE_GMAX; prefill: leaves, one chunk per workgroup, two
+// row tiles at D = 128 (one, looping, at D = 64)
 template <int D, int G>
 hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
-    if constexpr (D == 128) {
-        if (a.cu_q) return launch_dgr<D, G, 2>(a, s);
+    if (a.cu_q) {
+        if constexpr (D == 128) return launch_dgr<D, G, 2, false, 0>(a, s);
+        return launch_dgr<D, G, 1, true, 0>(a, s);
     }
-    return launch_dgr<D, G, 1>(a, s);
+    return launch_dgr<D, G, 1, true, BINV_DECODE_GMAX>(a, s);
 }
 
 template <int D>

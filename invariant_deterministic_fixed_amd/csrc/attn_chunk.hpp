@@ -73,14 +73,14 @@ struct TileCtx {
     int n_pages;
 };
 
+// kv_len_b = kv_lens[b] as read by the caller
 template <int G, int R>
-__device__ __forceinline__ TileCtx tile_ctx(int b, int g, int qt, const int32_t* cu_q,
-                                            const int32_t* kv_lens, int64_t pt_stride,
-                                            int max_kv_len) {
+__device__ __forceinline__ TileCtx tile_ctx_len(int b, int g, int qt, const int32_t* cu_q,
+                                                int kv_len_b, int64_t pt_stride, int max_kv_len) {
     constexpr int TQ = ROWS * R / G;
     TileCtx x;
     x.b = b; x.g = g; x.qt = qt;
-    x.kv_len = min(kv_lens[b], max_kv_len);
+    x.kv_len = min(kv_len_b, max_kv_len);
     if (cu_q) {
         x.q_start = cu_q[b];
         x.q_len = cu_q[b + 1] - cu_q[b];
@@ -94,6 +94,13 @@ __device__ __forceinline__ TileCtx tile_ctx(int b, int g, int qt, const int32_t*
     x.pt_row = (int64_t)b * pt_stride;
     x.n_pages = (x.kv_len + PAGE - 1) / PAGE;
     return x;
+}
+
+template <int G, int R>
+__device__ __forceinline__ TileCtx tile_ctx(int b, int g, int qt, const int32_t* cu_q,
+                                            const int32_t* kv_lens, int64_t pt_stride,
+                                            int max_kv_len) {
+    return tile_ctx_len<G, R>(b, g, qt, cu_q, kv_lens[b], pt_stride, max_kv_len);
 }
 
 template <int D, int R, bool VL>
@@ -351,16 +358,46 @@ struct Partial {
     float o[2];
 };
 
-// left-to-right combine of two partials (m in the log2 domain)
+// left-to-right combine of two partials (m in the log2 domain):
+//   m = max(ma, mb); fa = 2^(ma - m); fb = 2^(mb - m);
+//   l = fa la + fb lb; o = fa oa + fb ob   (one fmaf each, product fb x first)
+// Every combine of the merge tree, wherever it runs, is this function.
+__device__ __forceinline__ void combine_scale(float ma, float mb, float& m, float& fa, float& fb) {
+    m = fmaxf(ma, mb);
+    fa = exp2f(ma - m);
+    fb = exp2f(mb - m);
+}
+__device__ __forceinline__ float combine_val(float fa, float a, float fb, float b) {
+    return fmaf(fa, a, fb * b);
+}
+
 template <int NO>
 __device__ __forceinline__ Partial combine(const Partial& a, const Partial& b) {
     Partial r;
-    r.m = fmaxf(a.m, b.m);
-    const float fa = exp2f(a.m - r.m);
-    const float fb = exp2f(b.m - r.m);
-    r.l = fmaf(fa, a.l, fb * b.l);
+    float fa, fb;
+    combine_scale(a.m, b.m, r.m, fa, fb);
+    r.l = combine_val(fa, a.l, fb, b.l);
 #pragma unroll
-    for (int i = 0; i < NO; ++i) r.o[i] = fmaf(fa, a.o[i], fb * b.o[i]);
+    for (int i = 0; i < NO; ++i) r.o[i] = combine_val(fa, a.o[i], fb, b.o[i]);
+    return r;
+}
+
+// the same combine on chunk results as a workgroup holds them: per lane the
+// o and m of its rows, per l-thread the row's l and max
+template <int R>
+__device__ __forceinline__ ChunkOut<R> combine_out(const ChunkOut<R>& a, const ChunkOut<R>& b) {
+    ChunkOut<R> r;
+#pragma unroll
+    for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float fa, fb;
+            combine_scale(a.m[rt][e], b.m[rt][e], r.m[rt][e], fa, fb);
+            r.o[rt][e] = combine_val(fa, a.o[rt][e], fb, b.o[rt][e]);
+        }
+    float fa, fb;
+    combine_scale(a.ml_m, b.ml_m, r.ml_m, fa, fb);
+    r.l = combine_val(fa, a.l, fb, b.l);
     return r;
 }
 
