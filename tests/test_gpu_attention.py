@@ -187,6 +187,31 @@ def test_prefill_chunked_and_decode_bitwise_equal():
     assert row_rel_err(f64(one_shot[rows]), ref).max() <= TOL_BF16
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (4, 4, 64)])
+def test_decode_tree_levels_equal_prefill_leaves(Hq, Hkv, D):
+    # Decode hands a row's partials to the merge kernel as nodes of one or two
+    # chunks depending on its chunk count (1..16: leaves; 17..32: pairs; 33 and
+    # 34: leaves again); prefill always hands over leaves.  Every decode
+    # position must equal the one-shot prefill of the same position bit for bit.
+    L = 34 * 256 - 100
+    scale = 1 / math.sqrt(D)
+    k, v = synth.random_kv(L, Hkv, D, 91, DEV)
+    cache, _ = make_cache([L], Hkv, D, 92, seqs=[(k, v)])
+    q = synth.normal((L, Hq, D), 1.0, 93, DEV)
+    one_shot = _prefill(cache, q, [0, L], [L], L, L, scale)
+    rng = np.random.default_rng(94)
+    edges = [0, 1, 255, 256, 4095, 4096, 4351, 4352, 4607, 8191, 8192, 8447, 8448, L - 1]
+    rows = np.unique(np.concatenate([edges, rng.integers(0, L, 200)])).astype(np.int64)
+    pt = cache.page_table[:1].expand(len(rows), -1).contiguous()
+    kv_lens = torch.as_tensor(rows + 1, dtype=torch.int32, device=DEV)
+    qr = q[torch.as_tensor(rows, device=DEV)].contiguous()
+    dec = binv.attn_decode(qr, cache.k_cache, cache.v_cache, pt, kv_lens, L, scale)
+    assert_bitwise_equal(dec, one_shot[torch.as_tensor(rows, device=DEV)], "decode vs prefill")
+    sample = [0, 4096, 8447, L - 1]
+    ref = oracle.attention(f64(q[sample]), sample, f64(k), f64(v), scale)
+    assert row_rel_err(f64(one_shot[sample]), ref).max() <= TOL_BF16
+
+
 def test_prefill_tile_positions_do_not_change_bits():
     # the same tokens prefilled at different offsets inside the 16-row tiles
     Hq, Hkv, D, L = 32, 8, 128, 777
