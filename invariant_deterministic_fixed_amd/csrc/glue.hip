@@ -142,26 +142,28 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ sr
 // One workgroup per row.  Each value maps to an order-preserving 32-bit key
 // (NaN -> 0, below every other key; -0 and +0 one key).  Let T be the key of
 // the K-th largest entry: the result is every entry with key > T plus the
-// lowest-index entries with key == T, which is what both paths below select.
-//   fast path (two reads of the row):
-//     1. histogram of the keys' top byte (LDS increments: integer counts, so
-//        the totals do not depend on the order in which lanes add) -> the
-//        bucket b holding T and how many entries above it are winners;
-//     2. one pass in index order (1024-element tiles, ballots and wave prefix
-//        counts) keeps the entries above bucket b and gathers bucket b's
-//        entries, still in index order, into LDS;
-//     3. radix passes over bytes 2, 1, 0 of the gathered keys pin down T, and
-//        an index-ordered pass over them takes the keys > T and the first
-//        keys == T;
-//   fallback (a row with fewer than K non-NaN entries, or more than
-//   TOPK_CAND entries in bucket b): the same radix select over bytes 3..0 and
-//   the index-ordered collection, both reading the row.
-// The <= 32 winners are then sorted by (value desc, index asc).
+// lowest-index entries with key == T, which is what every path below selects.
+// Counting uses integer LDS increments and slots are reserved with integer LDS
+// atomics, so neither counts nor the selected set depend on the order in which
+// lanes and waves arrive; where order matters (equal keys) it is the index.
+//   1. histogram of the keys' top 11 bits (sign, exponent, two mantissa bits;
+//      a bucket is a quarter octave) -> the bucket b holding T and how many
+//      entries above it are winners;
+//   2. one pass over the row: entries above bucket b go to the winner slots,
+//      bucket b's entries to an LDS candidate list (unordered);
+//   3. two 8-bit radix passes and a final one over the candidates pin down T;
+//      candidates > T are winners; those == T are listed and the `need`
+//      lowest indices among them (ranked by index) complete the K;
+//   crowded bucket (more than TOPK_CAND entries in b): the radix passes and
+//   the pass that lists > T and == T read the row instead;
+//   more than TOPK_EQ_MAX entries equal to T, or fewer than K non-NaN entries:
+//   one index-ordered pass over the row (ballots and wave prefix counts) takes
+//   the keys > T and the first keys == T, stopping once all are placed.
+// The <= 32 winners are then ranked by (value desc, index asc).
 constexpr int TOPK_MAX = 32;
 constexpr int TOPK_NT = 1024;
 constexpr int TOPK_NW = TOPK_NT / 64;
 constexpr int TOPK_CAND = 4096;
-constexpr int TOPK_E = 8;            // entries per thread per tile in the gathering pass
 
 __device__ __forceinline__ uint32_t order_key(float v) {
     uint32_t b = __float_as_uint(v);
@@ -174,70 +176,122 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
 
+constexpr int TOPK_EQ_MAX = 256;     // entries equal to the K-th key ranked by index in LDS
+
+constexpr int TOPK_HB = 11;           // bits of the first digit (sign, exponent, 2 mantissa bits)
+
 struct TopkShared {
-    uint32_t hist[256];
+    uint32_t hist[1 << TOPK_HB];
     uint32_t s_prefix, s_need;
     uint32_t w_a[TOPK_NW], w_b[TOPK_NW];
-    uint32_t w_ea[TOPK_E][TOPK_NW], w_eb[TOPK_E][TOPK_NW];
+    uint32_t n_gt, n_cand, n_eq;         // slot counters (LDS integer atomics)
+    int eq_i[TOPK_EQ_MAX];
     float sel_v[TOPK_MAX];
     int sel_i[TOPK_MAX];
     float cand_v[TOPK_CAND];
     int cand_i[TOPK_CAND];
 };
 
-// Radix select over `m` values read by get(j): keys with (key & mask) == prefix
-// are refined byte by byte, shifts `shift`, shift - 8, ..., `last`.  Returns
-// false if fewer than `need` such keys exist.  Otherwise prefix holds the
-// bytes fixed so far of the need-th largest key (all of T when last = 0) and
-// need how many entries with that prefix are still to be taken.  Every thread
-// returns the same values.
-template <class Get>
-__device__ bool radix_select(TopkShared& sh, Get get, int64_t m, int shift, int last,
+// Radix select over `m` values: keys with (key & mask) == prefix are refined
+// digit by digit, BITS bits at shifts `shift`, shift - BITS, ..., down to
+// `last` (a digit may overlap bits already fixed: they agree with prefix).
+// Returns false if fewer than `need` such keys exist.  Otherwise prefix holds
+// the bits fixed so far of the need-th largest key (all of T when last = 0)
+// and need how many entries with that prefix are still to be taken.  Every
+// thread returns the same values.  get4(i) returns values 4i .. 4i+3 (NaN past
+// m); get4_fast(i) the same without bounds checks, used (when fast_ok) for
+// tiles wholly inside.  E reads of four per thread per tile, the next tile's
+// reads issued before the current tile is counted (integer LDS atomics: the
+// order of the increments does not matter).
+template <int E, int BITS, class Get4, class Get4Fast>
+__device__ bool radix_select(TopkShared& sh, Get4 get4, Get4Fast get4_fast, bool fast_ok,
+                             int64_t m, int shift, int last,
                              uint32_t& prefix, uint32_t& mask, uint32_t& need) {
-    const int t = threadIdx.x;
-    for (; shift >= last; shift -= 8) {
-        if (t < 256) sh.hist[t] = 0u;
+    constexpr int NB = 1 << BITS;
+    constexpr int PER = NB >= TOPK_NT ? NB / TOPK_NT : 1;   // bins per thread
+    constexpr int NACT = NB / PER;                          // threads that own bins
+    static_assert(NACT % 64 == 0 && NACT <= TOPK_NT, "whole waves own the bins");
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t m4 = (m + 3) / 4;
+    constexpr int64_t TILE = (int64_t)E * TOPK_NT;
+    for (; shift >= last; shift -= BITS) {
+        for (int b = t; b < NB; b += TOPK_NT) sh.hist[b] = 0u;
         __syncthreads();
-        for (int64_t j0 = 0; j0 < m; j0 += (int64_t)TOPK_E * TOPK_NT) {
-            float v[TOPK_E];
+        f32x4 v[E];
+        auto load = [&](int64_t i0) {
+            if (fast_ok && 4 * (i0 + TILE) <= m) {       // whole tile inside: plain reads
 #pragma unroll
-            for (int e = 0; e < TOPK_E; ++e) {
-                const int64_t j = j0 + e * TOPK_NT + t;
-                v[e] = j < m ? get(j) : __uint_as_float(0x7fc00000u);
-            }
+                for (int e = 0; e < E; ++e) v[e] = get4_fast(i0 + e * TOPK_NT + t);
+            } else {
 #pragma unroll
-            for (int e = 0; e < TOPK_E; ++e) {
-                const uint32_t key = order_key(v[e]);
-                if (key != 0u && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+                for (int e = 0; e < E; ++e) {
+                    const int64_t i = i0 + e * TOPK_NT + t;
+                    v[e] = i < m4 ? get4(i) : f32x4{NAN, NAN, NAN, NAN};
+                }
             }
+        };
+        load(0);
+        for (int64_t i0 = 0; i0 < m4; i0 += TILE) {
+            f32x4 cur[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) cur[e] = v[e];
+            if (i0 + TILE < m4) load(i0 + TILE);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t key = order_key(cur[e][q]);
+                    if (key != 0u && (key & mask) == prefix)
+                        atomicAdd(&sh.hist[(key >> shift) & (NB - 1)], 1u);
+                }
         }
         __syncthreads();
-        if (t == 0) {
-            uint32_t cum = 0u, chosen = 0u, nd = need;
-            bool found = false;
-            for (int bkt = 255; bkt >= 0; --bkt) {
-                const uint32_t h = sh.hist[bkt];
-                if (cum + h >= need) { chosen = (uint32_t)bkt; nd = need - cum; found = true; break; }
-                cum += h;
+        // bucket of the need-th largest key: thread t < NACT owns bins
+        // [t PER, t PER + PER); suffix sums over the owners (a shift scan
+        // inside each wave, then the wave totals above)
+        uint32_t own[PER], sum = 0u, suf = 0u;
+        if (t < NACT) {
+#pragma unroll
+            for (int k = 0; k < PER; ++k) { own[k] = sh.hist[t * PER + k]; sum += own[k]; }
+            suf = sum;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t y = __shfl_down(suf, d);
+                if (lane + d < 64) suf += y;
             }
-            sh.s_prefix = found ? (prefix | (chosen << shift)) : 0xffffffffu;
-            sh.s_need = found ? nd : 0u;
+            if (lane == 0) sh.w_a[wave] = suf;               // wave total
+        }
+        if (t == 0) { sh.s_prefix = 0xffffffffu; sh.s_need = 0u; }
+        __syncthreads();
+        if (t < NACT) {
+            uint32_t above = suf - sum;                      // owners above t inside the wave
+            for (int w = wave + 1; w < NACT / 64; ++w) above += sh.w_a[w];
+#pragma unroll
+            for (int k = PER - 1; k >= 0; --k) {
+                if (above < need && need <= above + own[k]) {
+                    sh.s_prefix = prefix | ((uint32_t)(t * PER + k) << shift);
+                    sh.s_need = need - above;
+                }
+                above += own[k];
+            }
         }
         __syncthreads();
         if (sh.s_prefix == 0xffffffffu) return false;
         prefix = sh.s_prefix;
         need = sh.s_need;
-        mask |= 255u << shift;
+        mask |= (uint32_t)(NB - 1) << shift;
+        __syncthreads();                                     // s_prefix / w_a read by all
     }
     return true;
 }
 
 // One index-ordered pass over m values: entries whose key satisfies gt() go
 // to sel slots gt_base + (their rank), the first n_eq entries satisfying eq()
-// go to slots eq_base + rank.  Returns nothing; sel is complete afterwards.
+// go to slots eq_base + rank; the pass ends once n_gt_all entries above and
+// n_eq equal ones have been seen.  sel is complete afterwards.
 template <class Get, class Gt, class Eq>
 __device__ void collect(TopkShared& sh, Get get, int64_t m, Gt gt_of, Eq eq_of, uint32_t gt_base,
-                        uint32_t eq_base, uint32_t n_eq) {
+                        uint32_t eq_base, uint32_t n_eq, uint32_t n_gt_all) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t run_gt = 0u, run_eq = 0u;
@@ -265,6 +319,76 @@ __device__ void collect(TopkShared& sh, Get get, int64_t m, Gt gt_of, Eq eq_of, 
         run_gt += tot_gt;
         run_eq += tot_eq;
         __syncthreads();
+        if (run_gt >= n_gt_all && run_eq >= n_eq) break;     // every winner placed
+    }
+}
+
+// One pass over the m values 4i .. 4i+3 = get4(i) (get4_fast for tiles wholly
+// inside when fast_ok): entries whose key satisfies is_gt / is_eq are handed
+// to put() with their rank among the flagged lanes of their ballot and the
+// base of the slots their wave reserved for that ballot with one LDS atomic
+// on *n_gt / *n_eq (slot order is not index order).
+template <int E, class Get4, class Get4Fast, class Put, class IsGt, class IsEq>
+__device__ void row_pass(Get4 get4, Get4Fast get4_fast, bool fast_ok, int64_t m, Put put,
+                         IsGt is_gt, IsEq is_eq, uint32_t* n_gt, uint32_t* n_eq) {
+    const int t = threadIdx.x, lane = t & 63;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    constexpr int64_t TILE = (int64_t)E * TOPK_NT;
+    const int64_t m4 = (m + 3) / 4;
+    f32x4 v[E];
+    auto load = [&](int64_t i0) {
+        if (fast_ok && 4 * (i0 + TILE) <= m) {            // whole tile inside: plain reads
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = get4_fast(i0 + e * TOPK_NT + t);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int64_t i = i0 + e * TOPK_NT + t;
+                v[e] = i < m4 ? get4(i) : f32x4{NAN, NAN, NAN, NAN};   // NaN: never flagged
+            }
+        }
+    };
+    load(0);
+    for (int64_t i0 = 0; i0 < m4; i0 += TILE) {
+        f32x4 cur[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) cur[e] = v[e];
+        if (i0 + TILE < m4) load(i0 + TILE);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t key = order_key(cur[e][q]);
+                const bool gt = key != 0u && is_gt(key);
+                const bool eq = key != 0u && is_eq(key);
+                const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
+                if (bgt | beq) {
+                    uint32_t base_gt = 0u, base_eq = 0u;
+                    if (lane == 0) {
+                        if (bgt) base_gt = atomicAdd(n_gt, (uint32_t)__popcll(bgt));
+                        if (beq) base_eq = atomicAdd(n_eq, (uint32_t)__popcll(beq));
+                    }
+                    base_gt = (uint32_t)__builtin_amdgcn_readfirstlane((int)base_gt);
+                    base_eq = (uint32_t)__builtin_amdgcn_readfirstlane((int)base_eq);
+                    put(key, cur[e][q], 4 * (i0 + e * TOPK_NT + t) + q, gt, eq, base_gt, base_eq,
+                        (uint32_t)__popcll(bgt & below), (uint32_t)__popcll(beq & below));
+                }
+            }
+    }
+}
+
+// Of the n_eq_all entries listed in eq_i (all equal to the K-th key), the
+// `need` lowest indices go to sel slots base .. base + need - 1 in index order.
+__device__ void rank_equal(TopkShared& sh, const float* row, uint32_t n_eq_all, uint32_t base,
+                           uint32_t need) {
+    for (uint32_t a = threadIdx.x; a < n_eq_all; a += TOPK_NT) {
+        const int ia = sh.eq_i[a];
+        uint32_t rank = 0u;
+        for (uint32_t b2 = 0; b2 < n_eq_all; ++b2) rank += sh.eq_i[b2] < ia ? 1u : 0u;
+        if (rank < need && base + rank < TOPK_MAX) {
+            sh.sel_v[base + rank] = row[ia];
+            sh.sel_i[base + rank] = ia;
+        }
     }
 }
 
@@ -277,134 +401,129 @@ __global__ __launch_bounds__(TOPK_NT) void topk_kernel(const float* __restrict__
     const float* row = x + r * ldx;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     auto from_row = [&](int64_t j) { return row[j]; };
+    // values 4i .. 4i+3 of the row, NaN past n; one 16-byte read when the row
+    // is 16-byte aligned and the four are inside it
+    const bool row_vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0u;
+    auto row4 = [&](int64_t i) -> f32x4 {
+        const int64_t j = 4 * i;
+        f32x4 r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = j + q < n ? row[j + q] : NAN;
+        return r;
+    };
+    auto row4_vec = [&](int64_t i) -> f32x4 { return *reinterpret_cast<const f32x4*>(row + 4 * i); };
     if (t < TOPK_MAX) { sh.sel_v[t] = -INFINITY; sh.sel_i[t] = -1; }
 
-    // ---- 1. top byte
+    // ---- 1. the first TOPK_HB bits of the K-th key (one pass over the row)
     uint32_t prefix = 0u, mask = 0u, need = (uint32_t)K;
-    bool fast = radix_select(sh, from_row, n, 24, 24, prefix, mask, need);
-    const uint32_t top = prefix >> 24, gt1 = (uint32_t)K - need;
+    const bool ok1 = radix_select<4, TOPK_HB>(sh, row4, row4_vec, row_vec, n, 32 - TOPK_HB,
+                                              32 - TOPK_HB, prefix, mask, need);
+    const uint32_t top = prefix >> (32 - TOPK_HB), gt1 = (uint32_t)K - need;
 
-    // ---- 2. winners above the bucket, the bucket's entries gathered in index
-    // order; tiles of E x 1024 entries, entry j0 + e * 1024 + t read by thread t
-    // (all E loads in flight at once), ranked in (e, t) = index order
+    // ---- 2. one pass over the row: entries above the bucket go to sel slots
+    // [0, gt1), the bucket's entries to the candidate list.  Each wave reserves
+    // slots for the flagged lanes of one ballot with one LDS atomic, so slot
+    // order is not index order; nothing below depends on it except the choice
+    // among entries equal to the K-th key, which is made by index (step 3).
+    if (t == 0) { sh.n_gt = 0u; sh.n_cand = 0u; sh.n_eq = 0u; }
+    __syncthreads();
     uint32_t n_cand = 0u;
-    if (fast) {
-        constexpr int E = TOPK_E;
-        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        uint32_t run_gt = 0u, run_c = 0u;
-        for (int64_t j0 = 0; j0 < n; j0 += (int64_t)E * TOPK_NT) {
-            float v[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int64_t j = j0 + e * TOPK_NT + t;
-                v[e] = j < n ? row[j] : __uint_as_float(0x7fc00000u);   // NaN: never flagged
-            }
-            uint64_t bgt[E], bcd[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const uint32_t key = order_key(v[e]);
-                bgt[e] = __ballot(key != 0u && (key >> 24) > top);
-                bcd[e] = __ballot(key != 0u && (key >> 24) == top);
-                if (lane == 0) { sh.w_ea[e][wave] = __popcll(bgt[e]); sh.w_eb[e][wave] = __popcll(bcd[e]); }
-            }
-            __syncthreads();
-            uint32_t off_gt = run_gt, off_c = run_c;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                uint32_t pre_gt = 0u, pre_c = 0u, tot_gt = 0u, tot_c = 0u;
-                for (int w = 0; w < TOPK_NW; ++w) {
-                    if (w < wave) { pre_gt += sh.w_ea[e][w]; pre_c += sh.w_eb[e][w]; }
-                    tot_gt += sh.w_ea[e][w]; tot_c += sh.w_eb[e][w];
-                }
-                const int64_t j = j0 + e * TOPK_NT + t;
-                if ((bgt[e] >> lane) & 1ull) {
-                    const uint32_t slot = off_gt + pre_gt + __popcll(bgt[e] & below);
-                    if (slot < TOPK_MAX) { sh.sel_v[slot] = v[e]; sh.sel_i[slot] = (int)j; }
-                }
-                if ((bcd[e] >> lane) & 1ull) {
-                    const uint32_t c = off_c + pre_c + __popcll(bcd[e] & below);
-                    if (c < (uint32_t)TOPK_CAND) { sh.cand_v[c] = v[e]; sh.cand_i[c] = (int)j; }
-                }
-                off_gt += tot_gt;
-                off_c += tot_c;
-            }
-            run_gt = off_gt;
-            run_c = off_c;
-            __syncthreads();
-        }
-        n_cand = run_c;
-        fast = n_cand <= (uint32_t)TOPK_CAND;
+    if (ok1) {
+        row_pass<4>(row4, row4_vec, row_vec, n, [&](uint32_t key, float v, int64_t j, bool take_gt,
+                                                     bool take_cd, uint32_t base_gt, uint32_t base_cd,
+                                                     uint32_t r_gt, uint32_t r_cd) {
+            if (take_gt && base_gt + r_gt < TOPK_MAX) { sh.sel_v[base_gt + r_gt] = v; sh.sel_i[base_gt + r_gt] = (int)j; }
+            if (take_cd && base_cd + r_cd < (uint32_t)TOPK_CAND) { sh.cand_v[base_cd + r_cd] = v; sh.cand_i[base_cd + r_cd] = (int)j; }
+        }, [&](uint32_t key) { return (key >> (32 - TOPK_HB)) > top; },
+           [&](uint32_t key) { return (key >> (32 - TOPK_HB)) == top; }, &sh.n_gt, &sh.n_cand);
+        __syncthreads();
+        n_cand = sh.n_cand;
     }
 
-    if (fast) {
-        // ---- 3. bytes 2..0 over the gathered entries, then take them in index order
-        auto from_cand = [&](int64_t c) { return sh.cand_v[c]; };
-        radix_select(sh, from_cand, (int64_t)n_cand, 16, 0, prefix, mask, need);  // T: >= need entries
-        const uint32_t T = prefix;
+    // ---- 3. the remaining bits of T, the K-th key; take every entry above T
+    // and, of those equal to T, the `need` lowest indices
+    bool ordered = true;          // fall back to one index-ordered pass over the row
+    bool found = ok1;
+    uint32_t T = 0u;
+    if (ok1 && n_cand <= (uint32_t)TOPK_CAND) {
+        auto cand4 = [&](int64_t i) -> f32x4 {
+            f32x4 r;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) r[q] = 4 * i + q < (int64_t)n_cand ? sh.cand_v[4 * i + q] : NAN;
+            return r;
+        };
+        // bits 20..5 in two 8-bit digits, then bits 7..0 (7..5 already fixed)
+        radix_select<1, 8>(sh, cand4, cand4, false, (int64_t)n_cand, 13, 5, prefix, mask, need);
+        radix_select<1, 8>(sh, cand4, cand4, false, (int64_t)n_cand, 0, 0, prefix, mask, need);
+        T = prefix;
         // (the gt1 winners above the bucket are in sel slots [0, gt1) already)
-        {
-            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-            uint32_t run_gt = 0u, run_eq = 0u;
-            for (int64_t c0 = 0; c0 < (int64_t)n_cand; c0 += TOPK_NT) {
-                const int64_t c = c0 + t;
-                const float v = c < (int64_t)n_cand ? sh.cand_v[c] : 0.0f;
-                const uint32_t key = c < (int64_t)n_cand ? order_key(v) : 0u;
-                const bool gt = key > T, eq = key == T && key != 0u;
-                const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
-                __syncthreads();                          // w_a / w_b of the last tile read
-                if (lane == 0) { sh.w_a[wave] = __popcll(bgt); sh.w_b[wave] = __popcll(beq); }
-                __syncthreads();
-                uint32_t off_gt = run_gt, off_eq = run_eq, tot_gt = 0u, tot_eq = 0u;
-                for (int w = 0; w < TOPK_NW; ++w) {
-                    if (w < wave) { off_gt += sh.w_a[w]; off_eq += sh.w_b[w]; }
-                    tot_gt += sh.w_a[w]; tot_eq += sh.w_b[w];
-                }
-                if (gt) {
-                    const uint32_t slot = gt1 + off_gt + __popcll(bgt & below);
-                    if (slot < TOPK_MAX) { sh.sel_v[slot] = v; sh.sel_i[slot] = sh.cand_i[c]; }
-                }
-                if (eq) {
-                    const uint32_t k = off_eq + __popcll(beq & below);
-                    const uint32_t slot = (uint32_t)K - need + k;
-                    if (k < need && slot < TOPK_MAX) { sh.sel_v[slot] = v; sh.sel_i[slot] = sh.cand_i[c]; }
-                }
-                run_gt += tot_gt;
-                run_eq += tot_eq;
+        for (int64_t c = t; c < (int64_t)n_cand; c += TOPK_NT) {
+            const uint32_t key = order_key(sh.cand_v[c]);
+            if (key > T) {
+                const uint32_t slot = atomicAdd(&sh.n_gt, 1u);      // continues after the gt1 slots
+                if (slot < TOPK_MAX) { sh.sel_v[slot] = sh.cand_v[c]; sh.sel_i[slot] = sh.cand_i[c]; }
+            } else if (key == T) {
+                const uint32_t k = atomicAdd(&sh.n_eq, 1u);
+                if (k < (uint32_t)TOPK_EQ_MAX) sh.eq_i[k] = sh.cand_i[c];
             }
         }
-    } else {
-        // ---- fallback: full radix select and collection over the row
+        __syncthreads();
+        if (sh.n_eq <= (uint32_t)TOPK_EQ_MAX) {
+            rank_equal(sh, row, sh.n_eq, (uint32_t)K - need, need);
+            ordered = false;
+        }
+        // else: many exact ties at the K-th key; T and need are final
+    } else if (ok1) {
+        // a crowded first bucket: the remaining digits over the row, then one
+        // pass over the row for the entries above T and those equal to it
+        radix_select<4, 8>(sh, row4, row4_vec, row_vec, n, 13, 5, prefix, mask, need);
+        radix_select<4, 8>(sh, row4, row4_vec, row_vec, n, 0, 0, prefix, mask, need);
+        T = prefix;
+        if (t == 0) { sh.n_gt = 0u; sh.n_eq = 0u; }
+        __syncthreads();
+        row_pass<4>(row4, row4_vec, row_vec, n, [&](uint32_t key, float v, int64_t j, bool take_gt,
+                                                     bool take_eq, uint32_t base_gt, uint32_t base_eq,
+                                                     uint32_t r_gt, uint32_t r_eq) {
+            if (take_gt && base_gt + r_gt < TOPK_MAX) { sh.sel_v[base_gt + r_gt] = v; sh.sel_i[base_gt + r_gt] = (int)j; }
+            if (take_eq && base_eq + r_eq < (uint32_t)TOPK_EQ_MAX) sh.eq_i[base_eq + r_eq] = (int)j;
+        }, [&](uint32_t key) { return key > T; }, [&](uint32_t key) { return key == T; },
+           &sh.n_gt, &sh.n_eq);
+        __syncthreads();
+        if (sh.n_eq <= (uint32_t)TOPK_EQ_MAX) {
+            rank_equal(sh, row, sh.n_eq, (uint32_t)K - need, need);
+            ordered = false;
+        }
+    }
+    if (ordered) {
+        // one index-ordered pass over the row: entries above T, then the
+        // first `need` equal to T (a row with fewer than K valid entries:
+        // every valid entry)
+        __syncthreads();
         if (t < TOPK_MAX) { sh.sel_v[t] = -INFINITY; sh.sel_i[t] = -1; }
-        prefix = 0u; mask = 0u; need = (uint32_t)K;
-        const bool found = radix_select(sh, from_row, n, 24, 0, prefix, mask, need);
-        // a row with fewer than K valid entries: every valid entry is selected
-        const uint32_t T = found ? prefix : 1u;
+        const uint32_t Tc = found ? T : 1u;
         const uint32_t n_eq = found ? need : (uint32_t)K;
         const uint32_t eq_base = found ? (uint32_t)K - need : 0u;
-        collect(sh, from_row, n, [&](uint32_t k) { return found && k > T; },
-                [&](uint32_t k) { return found ? k == T : k >= T; }, 0u, eq_base, n_eq);
+        collect(sh, from_row, n, [&](uint32_t k) { return found && k > Tc; },
+                [&](uint32_t k) { return found ? k == Tc : k >= Tc; }, 0u, eq_base, n_eq,
+                (uint32_t)K - n_eq);
     }
     __syncthreads();
 
-    // ---- 4. order the winners
-    if (t == 0) {
-        float v[TOPK_MAX];
-        int id[TOPK_MAX];
-        for (int k = 0; k < K; ++k) { v[k] = sh.sel_v[k]; id[k] = sh.sel_i[k]; }
-        // insertion sort; a missing entry (id -1) sorts after every real one
-        for (int a = 1; a < K; ++a) {
-            const float va = v[a];
-            const int ia = id[a];
-            int b = a;
-            while (b > 0 && ia >= 0 && (id[b - 1] < 0 || better(va, ia, v[b - 1], id[b - 1]))) {
-                v[b] = v[b - 1]; id[b] = id[b - 1]; --b;
-            }
-            v[b] = va; id[b] = ia;
-        }
+    // ---- 4. order the winners: thread k < K ranks entry k against all K (real
+    // entries by value descending, index ascending -- ids are distinct, so the
+    // ranks are a permutation; missing entries (id -1) after them in slot order)
+    if (t < K) {
+        const float v = sh.sel_v[t];
+        const int id = sh.sel_i[t];
+        int rank = 0;
         for (int k = 0; k < K; ++k) {
-            ids[r * K + k] = id[k];
-            vals[r * K + k] = id[k] < 0 ? -INFINITY : v[k];
+            const float vk = sh.sel_v[k];
+            const int ik = sh.sel_i[k];
+            const bool before = (id < 0) ? (ik >= 0 || k < t) : (ik >= 0 && better(vk, ik, v, id));
+            rank += before ? 1 : 0;
         }
+        ids[r * K + rank] = id;
+        vals[r * K + rank] = id < 0 ? -INFINITY : v;
     }
 }
 

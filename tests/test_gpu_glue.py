@@ -78,7 +78,7 @@ def test_gather_rows_bit_copy():
 
 
 def test_topk_exact_with_ties_and_nan():
-    x = synth.normal((7, 128256), 3.0, 8, DEV, dtype=torch.float32)
+    x = synth.normal((9, 128256), 3.0, 8, DEV, dtype=torch.float32)
     x[1, 100:140] = 50.0                       # a block of ties above everything else
     x[2, 5] = float("nan")
     x[3, :] = -1.0                             # every entry tied
@@ -89,9 +89,16 @@ def test_topk_exact_with_ties_and_nan():
     # the 20th place falls inside a tie: 10 entries at 100, 30 tied at 99
     x[6, 1000:1010] = 100.0
     x[6, 5000:5030] = 99.0
+    # 15 clear winners, then the 20th place inside a tie of scattered entries:
+    # 100 of them (picked by index among the gathered entries) and 300 (more
+    # than that path ranks; the row falls back to the full radix passes)
+    perm = np.random.default_rng(9).permutation(128256)
+    for r, n_tie in [(7, 100), (8, 300)]:
+        x[r, torch.as_tensor(perm[:15], device=DEV)] = 200.0
+        x[r, torch.as_tensor(perm[15:15 + n_tie], device=DEV)] = 150.0
     ids, vals = binv.topk(x, 20)
     xc = x.cpu().numpy()
-    for r in range(7):
+    for r in range(9):
         row = np.where(np.isnan(xc[r]), -np.inf, xc[r])
         want_ids, want_vals = od.topk(row, 20)
         np.testing.assert_array_equal(ids[r].cpu().numpy(), want_ids)
@@ -99,6 +106,35 @@ def test_topk_exact_with_ties_and_nan():
     assert ids[1].tolist() == list(range(100, 120))
     assert ids[3].tolist() == list(range(20))
     assert ids[6].tolist() == list(range(1000, 1010)) + list(range(5000, 5010))
+    for r, n_tie in [(7, 100), (8, 300)]:
+        assert ids[r].tolist() == sorted(perm[:15].tolist()) + sorted(perm[15:15 + n_tie].tolist())[:5]
+
+
+@pytest.mark.parametrize("n,ldx", [(128256, 128256), (50001, 50003), (4099, 4101)])
+def test_topk_matches_oracle_across_paths(n, ldx):
+    # rows that take each path of the kernel: a thin first bucket (normal
+    # logits), a crowded one (uniform values; many share the top 11 key bits),
+    # a crowded one with a few exact ties at the 20th place, and rows whose
+    # starts are not 16-byte aligned (odd ldx) or whose length is not a
+    # multiple of 4
+    g = torch.Generator(device=DEV).manual_seed(n)
+    x = torch.empty((6, ldx), device=DEV)
+    x[0] = torch.randn(ldx, generator=g, device=DEV) * 3.0
+    x[1] = torch.randn(ldx, generator=g, device=DEV) * 2.0
+    x[2] = torch.rand(ldx, generator=g, device=DEV) * 2 - 1
+    x[3] = torch.rand(ldx, generator=g, device=DEV) * 2 - 1
+    x[3, 7::97] = 0.99990234375                # every 97th entry: exact ties at the top
+    x[4] = torch.rand(ldx, generator=g, device=DEV) * 2 - 1
+    x[4, n // 3] = 5.0
+    x[5] = -torch.rand(ldx, generator=g, device=DEV)          # all negative
+    flat = x.reshape(-1)[: 5 * ldx + n]
+    xs = torch.as_strided(flat, (6, n), (ldx, 1))
+    ids, vals = binv.topk(xs, 20)
+    xc = xs.cpu().numpy()
+    for r in range(6):
+        want_ids, want_vals = od.topk(xc[r].astype(np.float64), 20)
+        np.testing.assert_array_equal(ids[r].cpu().numpy(), want_ids, err_msg=f"row {r}")
+        np.testing.assert_array_equal(vals[r].cpu().numpy(), want_vals.astype(np.float32))
 
 
 def test_topk_signed_zero_and_short_rows():
