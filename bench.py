@@ -434,6 +434,36 @@ def sweep(dev="cuda:0"):
              tuned_tokens_per_s=round(res["tuned"], 1),
              locked_one_tokens_per_s=round(res["locked"], 1) if "locked" in res else None,
              slowdown_vs_tuned=round(res["tuned"] / res["invariant"], 3))
+    del w
+    torch.cuda.empty_cache()
+
+    # fp32-activation mitigation: six RMSNorm -> GEMM blocks at d = 4096 with
+    # bf16 or fp32 activations, invariant or tuned kernels; the target row's
+    # output drift over batch sizes 1 / 64 / 256 / 1024 and the chain's time
+    from invariant_deterministic_fixed_amd import fp32act
+    d, layers = 4096, 6
+    ws = [synth.normal((d, d), 1.0 / 64, 300 + l, dev) for l in range(layers)]
+    ws3 = [fp32act.stack3(x) for x in ws]
+    gamma = torch.ones(d, dtype=torch.bfloat16, device=dev)
+    target = synth.normal((1, d), 1.0, 299, dev)
+    r = np.random.default_rng(298)
+    for mode in ("bf16", "fp32"):
+        for tuned in (False, True):
+            outs, ms = {}, {}
+            for B in (1, 64, 256, 1024):
+                X = synth.normal((B, d), 1.0, 400 + B, dev)
+                p = int(r.integers(0, B))
+                X[p] = target[0]
+                outs[B] = fp32act.chain(X, ws, gamma, mode, tuned, weights3=ws3)[p].double().cpu()
+                ms[B] = _cold_ms([lambda: fp32act.chain(X, ws, gamma, mode, tuned, weights3=ws3)],
+                                 reps=10)
+            base = outs[1]
+            drift = max(float((outs[B] - base).abs().max()) for B in outs) / float(base.abs().max())
+            moved = max(int((outs[B] != base).sum()) for B in outs)
+            emit(sweep="fp32act_chain", activations=mode,
+                 kernels="tuned" if tuned else "invariant", d=d, layers=layers,
+                 drift_rel=drift, elements_moved=moved,
+                 ms_B1=round(ms[1], 4), ms_B64=round(ms[64], 4), ms_B1024=round(ms[1024], 4))
 
 
 def main():

@@ -259,6 +259,20 @@ int binv_residual_add(float* h, int64_t ldh, const void* x, int64_t ldx, int64_t
 int binv_gather_rows(const void* src, int dt, int64_t lds, const int32_t* idx, int64_t R,
                      void* dst, int64_t ldd, int64_t cols, void* stream);
 
+/* Three-way bf16 split of fp32 activations, for the fp32-activation mitigation
+ * (devpress.csdn.net explainer of "Defeating Nondeterminism in LLM Inference",
+ * sections 2 and 6: weights stay bf16, activations fp32).  For x fp32 [M, ldx]:
+ *   out[i, k] = hi = bf16(x[i, k]),  out[i, K + k] = mid = bf16(x[i, k] - hi),
+ *   out[i, 2K + k] = lo = bf16(x[i, k] - hi - mid)     (round to nearest even)
+ * out bf16 [M, ld_out >= 3K].  hi + mid + lo == x exactly for finite x whose
+ * parts stay normal, so binv_gemm_bf16 of out against the weights stacked three
+ * times ([W; W; W], 3K x N) with fp32 output contracts the fp32 activations
+ * with exact products and one fp32 accumulator per element.  Elementwise, so
+ * batch-invariant as it stands.  K, ldx, ld_out multiples of 4; x 16-byte and
+ * out 8-byte aligned; M <= 65535.  The caller owns both buffers. */
+int binv_split_bf16x3(const float* x, int64_t ldx, int64_t M, int64_t K, void* out,
+                      int64_t ld_out, void* stream);
+
 /* Exact top-K (K <= 32) of each fp32 row of x [R, ldx] over its first n entries:
  * ids int32 [R, K] and vals fp32 [R, K], sorted by value descending, equal values
  * by index ascending; NaN is never selected (a row with fewer than K non-NaN

@@ -55,6 +55,7 @@ def _declare(lib):
         "binv_residual_add": (ci, [vp, i64, vp, i64, i64, i64, vp]),
         "binv_gather_rows": (ci, [vp, ci, i64, vp, i64, vp, i64, i64, vp]),
         "binv_topk": (ci, [vp, i64, i64, i64, ci, vp, vp, vp]),
+        "binv_split_bf16x3": (ci, [vp, i64, i64, i64, vp, i64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -274,6 +275,20 @@ def gather_rows(src, idx, out=None):
     _, ldd = _rows(out)
     _check(lib().binv_gather_rows(_ptr(src), _dt(src), lds, _ptr(idx), R, _ptr(out), ldd,
                                   src.shape[1], _stream(src)), "binv_gather_rows")
+    return out
+
+
+def split_bf16x3(x, out=None):
+    """fp32 [M, K] -> bf16 [M, 3K] = [hi | mid | lo] with hi + mid + lo == x."""
+    _dev(x, out)
+    assert x.dtype == torch.float32
+    M, ldx = _rows(x)
+    K = x.shape[1]
+    if out is None:
+        out = torch.empty((M, 3 * K), dtype=torch.bfloat16, device=x.device)
+    _, ldo = _rows(out)
+    _check(lib().binv_split_bf16x3(_ptr(x), ldx, M, K, _ptr(out), ldo, _stream(x)),
+           "binv_split_bf16x3")
     return out
 
 

@@ -276,6 +276,18 @@ int binv_gather_rows(const void* src, int dt, int64_t lds, const int32_t* idx, i
                                          (hipStream_t)stream));
 }
 
+int binv_split_bf16x3(const float* x, int64_t ldx, int64_t M, int64_t K, void* out,
+                      int64_t ld_out, void* stream) {
+    if (M < 0 || K < 0) return BINV_ERR_INVALID_ARG;
+    if (M == 0 || K == 0) return BINV_OK;
+    if (!x || !out || ldx < K || ld_out < 3 * K) return BINV_ERR_INVALID_ARG;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(out) & 7u) || ldx % 4 || ld_out % 4)
+        return BINV_ERR_INVALID_ARG;
+    if (K % 4 != 0) return BINV_ERR_UNSUPPORTED;
+    if (M > 65535 || 3 * K > I32MAX) return BINV_ERR_UNSUPPORTED;
+    return status_of(binv::launch_split3(x, ldx, M, (int)K, out, ld_out, (hipStream_t)stream));
+}
+
 int binv_topk(const float* x, int64_t ldx, int64_t R, int64_t n, int K, int32_t* ids,
               float* vals, void* stream) {
     if (R < 0 || n < 0 || K < 1) return BINV_ERR_INVALID_ARG;

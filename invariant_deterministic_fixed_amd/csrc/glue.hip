@@ -136,6 +136,47 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ sr
         *reinterpret_cast<uint32_t*>(d + j) = *reinterpret_cast<const uint32_t*>(s + j);
 }
 
+// ------------------------------------------------------------------ fp32 split
+// Three bf16 parts of an fp32 activation, for contracting fp32 activations
+// against bf16 weights on bf16 matrix cores (the fp32-activation mitigation
+// the devpress.csdn.net explainer names in sections 2 and 6: weights stay
+// bf16, activations fp32).  hi = bf16(x), mid = bf16(x - hi), lo = bf16(x -
+// hi - mid), each rounded to nearest even; both differences are exact in
+// fp32 (x - hi keeps at most 16 significant bits, x - hi - mid at most 8), so
+// hi + mid + lo = x whenever the parts stay in the normal range.  Row i of
+// out holds [hi(x[i, :]) | mid(...) | lo(...)], K elements each.  Four
+// elements (16 bytes in, three 8-byte pieces out) per lane.
+__global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ x, int64_t ldx,
+                                                     int K, bf16_t* __restrict__ out,
+                                                     int64_t ldo) {
+    const int64_t row = blockIdx.y;
+    const int k = 4 * (blockIdx.x * 256 + threadIdx.x);
+    if (k >= K) return;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(x + row * ldx + k);
+    u32x2 hi, mid, lo;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t ph[2], pm[2], pl[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float xv = v[2 * h + i];
+            const uint32_t bh = f32_to_bf16(xv);
+            const float r1 = xv - bf16_to_f32(bh);
+            const uint32_t bm = f32_to_bf16(r1);
+            const float r2 = r1 - bf16_to_f32(bm);
+            const uint32_t bl = f32_to_bf16(r2);
+            ph[i] = bh; pm[i] = bm; pl[i] = bl;
+        }
+        hi[h] = ph[0] | (ph[1] << 16);
+        mid[h] = pm[0] | (pm[1] << 16);
+        lo[h] = pl[0] | (pl[1] << 16);
+    }
+    bf16_t* o = out + row * ldo + k;
+    *reinterpret_cast<u32x2*>(o) = hi;
+    *reinterpret_cast<u32x2*>(o + K) = mid;
+    *reinterpret_cast<u32x2*>(o + 2 * K) = lo;
+}
+
 // ------------------------------------------------------------------ top-k
 // Exact top-K of one fp32 row: the K largest values, sorted by value
 // descending and, among equal values, by index ascending; NaN never selected.
@@ -569,6 +610,14 @@ hipError_t launch_gather(const void* src, int64_t lds, const int32_t* idx, int64
     if (R == 0) return hipSuccess;
     hipLaunchKernelGGL(gather_kernel, dim3((unsigned)R), dim3(256), 0, s, (const char*)src, lds,
                        idx, (char*)dst, ldd, row_bytes);
+    return hipGetLastError();
+}
+
+hipError_t launch_split3(const float* x, int64_t ldx, int64_t M, int K, void* out, int64_t ldo,
+                         hipStream_t s) {
+    if (M == 0 || K == 0) return hipSuccess;
+    hipLaunchKernelGGL(split3_kernel, dim3((unsigned)((K / 4 + 255) / 256), (unsigned)M), dim3(256),
+                       0, s, x, ldx, K, (bf16_t*)out, ldo);
     return hipGetLastError();
 }
 

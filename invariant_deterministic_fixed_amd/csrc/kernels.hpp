@@ -59,5 +59,7 @@ hipError_t launch_gather(const void* src, int64_t lds, const int32_t* idx, int64
                          int64_t ldd, int row_bytes, hipStream_t s);
 hipError_t launch_topk(const float* x, int64_t ldx, int64_t R, int64_t n, int K, int32_t* ids,
                        float* vals, hipStream_t s);
+hipError_t launch_split3(const float* x, int64_t ldx, int64_t M, int K, void* out, int64_t ldo,
+                         hipStream_t s);
 
 }  // namespace binv

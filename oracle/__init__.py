@@ -83,6 +83,20 @@ def round_bf16(x):
     return y
 
 
+def split_bf16x3(x):
+    """The three bf16 parts of fp32 values, for contracting fp32 activations on
+    bf16 matrix cores (fp32-activation mitigation: devpress.csdn.net explainer of
+    "Defeating Nondeterminism in LLM Inference", sections 2 and 6 -- weights stay
+    bf16, activations fp32).  hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi
+    - mid), nearest-even; the differences are formed in fp64, where they are
+    exact.  Returns (hi, mid, lo) as fp64 arrays."""
+    x = _f64(x)
+    hi = round_bf16(x)
+    mid = round_bf16(x - hi)
+    lo = round_bf16(x - hi - mid)
+    return hi, mid, lo
+
+
 def rmsnorm(x, gamma, eps):
     """y = x / sqrt(mean(x^2) + eps) * gamma, row by row.  x [M, d], gamma [d]."""
     x = _f64(x)

@@ -195,3 +195,13 @@ def test_topk_validation():
     assert f(FAKE, 8, 2, 16, 4, FAKE, FAKE, L) == INVALID                   # ldx < n
     assert f(FAKE, 16, 2, 16, 4, L, FAKE, L) == INVALID                     # null ids
     assert f(FAKE, 16, -1, 16, 4, FAKE, FAKE, L) == INVALID
+
+
+def test_split_bf16x3_validation():
+    f = _lib().binv_split_bf16x3
+    assert f(L, 8, 0, 8, L, 24, L) == OK                                    # M = 0
+    assert f(L, 8, 2, 8, FAKE, 24, L) == INVALID                            # null x
+    assert f(FAKE, 8, 2, 8, FAKE, 16, L) == INVALID                         # ld_out < 3K
+    assert f(FAKE + 4, 8, 2, 8, FAKE, 24, L) == INVALID                     # misaligned x
+    assert f(FAKE, 8, 2, 6, FAKE, 24, L) == UNSUPPORTED                     # K % 4
+    assert f(FAKE, 8, -1, 8, FAKE, 24, L) == INVALID

@@ -1,0 +1,79 @@
+"""The fp32-activation mitigation (weights bf16, activations fp32) against the
+bf16 path: the split kernel against the oracle's split, bitwise; then a chain
+of RMSNorm -> GEMM blocks run at several batch sizes with the target row at a
+random position among random neighbours, with the invariant kernels and with
+the shape-tuned comparators.  Measured: how far the target's output moves with
+the batch (drift) and how far it is from the fp64 chain (oracle error)."""
+import numpy as np
+import pytest
+import torch
+
+import invariant_deterministic_fixed_amd as binv
+import oracle
+from invariant_deterministic_fixed_amd import fp32act, synth
+from helpers import f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def test_split_kernel_matches_oracle_split_bitwise():
+    g = torch.Generator(device=DEV).manual_seed(21)
+    x = torch.randn((37, 1028), generator=g, device=DEV) * torch.exp(
+        torch.randn((37, 1028), generator=g, device=DEV) * 5)
+    x[0, :4] = torch.tensor([0.0, -0.0, 1 + 2.0 ** -23, -(1 + 2.0 ** -8 + 2.0 ** -16)], device=DEV)
+    out = binv.split_bf16x3(x)
+    hi, mid, lo = oracle.split_bf16x3(x.double().cpu().numpy())
+    K = x.shape[1]
+    got = out.float().double().cpu().numpy()
+    np.testing.assert_array_equal(got[:, :K], hi)
+    np.testing.assert_array_equal(got[:, K:2 * K], mid)
+    np.testing.assert_array_equal(got[:, 2 * K:], lo)
+    np.testing.assert_array_equal(got[:, :K] + got[:, K:2 * K] + got[:, 2 * K:], x.double().cpu().numpy())
+
+
+def _oracle_chain(x, weights, eps):
+    h = f64(x)
+    ones = np.ones(h.shape[1])
+    for w in weights:
+        h = oracle.gemm(oracle.rmsnorm(h, ones, eps), f64(w))
+    return h
+
+
+def test_fp32_activations_narrow_batch_drift_and_oracle_error():
+    # d = 4096 so the comparators' choices move with the batch: split-K 16 / 16 /
+    # 8 / 2 ways for 1 / 64 / 256 / 1024 rows, RMSNorm 1024 or 256 lanes per row
+    d, layers, eps = 4096, 6, 1e-6
+    batches = [1, 64, 256, 1024]
+    ws = [synth.normal((d, d), 1.0 / 64, 300 + l, DEV) for l in range(layers)]     # bf16
+    ws3 = [fp32act.stack3(w) for w in ws]
+    gamma = torch.ones(d, dtype=torch.bfloat16, device=DEV)
+    target = synth.normal((1, d), 1.0, 299, DEV)                                    # bf16 values
+    rng = np.random.default_rng(298)
+    ref64 = _oracle_chain(target, ws, eps)[0]
+    rows = {}
+    for mode in ["bf16", "fp32"]:
+        for tuned in [False, True]:
+            outs = {}
+            for B in batches:
+                X = synth.normal((B, d), 1.0, 400 + B, DEV)
+                p = int(rng.integers(0, B))
+                X[p] = target[0]
+                Y = fp32act.chain(X, ws, gamma, mode, tuned, eps, weights3=ws3)
+                outs[B] = Y[p].double().cpu().numpy()
+            base = outs[1]
+            scale = np.abs(base).max()
+            drift = max(np.abs(outs[B] - base).max() for B in batches) / scale
+            moved = max(int(np.sum(outs[B] != base)) for B in batches)
+            err = np.abs(base - ref64).max() / np.abs(ref64).max()
+            rows[(mode, tuned)] = (drift, moved, err)
+            print(f"{mode} activations, {'tuned' if tuned else 'invariant'} kernels: "
+                  f"drift over B={batches} {drift:.3e} ({moved} of {d} elements move); "
+                  f"error vs fp64 chain {err:.3e}")
+    # invariant kernels: no drift with either activation type
+    assert rows[("bf16", False)][0] == 0.0 and rows[("fp32", False)][0] == 0.0
+    # tuned kernels drift (positive control); fp32 activations narrow it a lot
+    assert rows[("bf16", True)][0] > 0.0
+    assert rows[("fp32", True)][0] * 20 < rows[("bf16", True)][0]
+    # and fp32 activations stay much closer to the fp64 chain
+    assert rows[("fp32", False)][2] * 20 < rows[("bf16", False)][2]

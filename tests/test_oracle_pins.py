@@ -42,6 +42,31 @@ def test_round_bf16_matches_torch_on_fp32_values():
     np.testing.assert_array_equal(got, want)
 
 
+# ------------------------------------------------------------------ fp32 -> three bf16 parts
+def test_split_bf16x3_reconstructs_fp32_exactly():
+    # fp32 has a 24-bit significand and each bf16 part carries 8 bits, so the
+    # three parts must add back to x exactly (parts in the normal range); a
+    # dropped part, a sign slip in a difference or a truncating rounding fails
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn(50000, generator=g) * torch.exp(torch.randn(50000, generator=g) * 6)
+    x = torch.cat([x, torch.tensor([0.0, -0.0, 1.0, -1.0, 3.0e38, -1e-30, 1 + 2.0 ** -23])])
+    xd = x.double().numpy()
+    hi, mid, lo = oracle.split_bf16x3(xd)
+    np.testing.assert_array_equal(hi + mid + lo, xd)
+    for part in (hi, mid, lo):                                 # each part is a bf16 value
+        np.testing.assert_array_equal(oracle.round_bf16(part), part)
+    nz = hi != 0
+    assert np.all(np.abs(mid[nz]) <= np.abs(hi[nz]) * 2.0 ** -8)   # |mid| <= half an ulp of hi
+    # by hand: 1 + 2^-23 -> hi = 1, and the residual 2^-23 is itself a bf16 value
+    h1, m1, l1 = oracle.split_bf16x3(np.array([1 + 2.0 ** -23]))
+    assert (h1[0], m1[0], l1[0]) == (1.0, 2.0 ** -23, 0.0)
+    # 1 + 2^-8 + 2^-16 + 2^-23 lies above the midpoint 1 + 2^-8, so hi = 1 + 2^-7;
+    # the residual -2^-8 + 2^-16 + 2^-23 rounds (spacing 2^-16 there) to
+    # mid = -2^-8 + 2^-16, leaving lo = 2^-23
+    h2, m2, l2 = oracle.split_bf16x3(np.array([1 + 2.0 ** -8 + 2.0 ** -16 + 2.0 ** -23]))
+    assert (h2[0], m2[0], l2[0]) == (1.0 + 2.0 ** -7, -(2.0 ** -8) + 2.0 ** -16, 2.0 ** -23)
+
+
 # ------------------------------------------------------------------ RMSNorm
 def test_rmsnorm_hand_worked_golden():
     for row in read_golden("rmsnorm_hand_worked.txt"):
