@@ -11,21 +11,23 @@
 // depth, prefill and decode producing bit-identical intermediates).
 //
 // Kernel 1 (chunk): one workgroup = one sequence b, one KV head g, one tile of
-// 16 query rows (16/G tokens x the G = Hq/Hkv query heads of g), one chunk c
-// = keys [256c, 256c+256).  Decode tiles hold one token; prefill tiles hold up
-// to 16/G consecutive new tokens of one sequence.  For every row it writes the
-// fp32 partial (m, l, o[D]) of the keys of chunk c that the row may see
-// (key j <= the row's position):
+// 16R query rows (16R/G tokens x the G = Hq/Hkv query heads of g); for each
+// chunk c = keys [256c, 256c+256) it takes, every row's partial (m, l, o[D])
+// of the keys of chunk c that the row may see (key j <= the row's position):
 //     s_j = (q . k_j) * scale * log2(e)      (scores kept in the log2 domain)
 //     m   = max_j s_j
 //     p_j = bf16(exp2(s_j - m))              (0 for keys the row may not see)
 //     l   = sum_j p_j                        (fixed order, below)
 //     o   = sum_j p_j v_j                    (matrix cores, keys ascending)
-// Kernel 2 (merge): one wave per (token, head) row merges the row's
-// n = pos/256 + 1 partials with a binary counter, which reproduces exactly the
-// left-aligned binary tree over 512 leaves whose padding leaves are the
-// identity (a padding leaf only ever meets a real subtree, and merging with the
-// identity returns the real subtree bit for bit).  out = bf16(o / l).
+// Decode tiles hold one token and hand over nodes of the merge tree (subtrees
+// of one or two consecutive chunks, merged in the workgroup); prefill tiles
+// hold up to 16R/G consecutive new tokens of one sequence and hand over leaves.
+// Kernel 2 (merge): one wave per (token, head) row merges the row's nodes with
+// a binary counter, which reproduces exactly the left-aligned binary tree over
+// 512 leaves whose padding leaves are the identity (a padding leaf only ever
+// meets a real subtree, and merging with the identity returns the real subtree
+// bit for bit) -- at whatever level the nodes were handed over.
+// out = bf16(o / l).
 //
 // Why the bits of a row do not depend on the batch: every per-row quantity is
 // computed by the same instruction sequence whatever else is in the tile --
