@@ -198,6 +198,209 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     }
 }
 
+// Prefill at D = 128: one workgroup = one sequence, one KV head, a block of
+// 128 query rows (128/G new tokens x the G query heads), one chunk.  Each of
+// the eight waves owns one 16-row tile outright -- its q.k over all 256 keys,
+// row max, p, l and p.v for all 128 features -- so rows need no cross-wave
+// reduction; the chunk's K and V pages are copied HBM -> LDS once (global_load_lds)
+// and read by all eight tiles, which then share one load of the chunk where
+// the chunk kernel's two-tile workgroups share it among 32 rows.  Every
+// per-element operation is the chunk kernel's, in the same order: q.k as
+// v_mfma_f32_16x16x32_bf16 over features 32ks + 8(lane>>4) .. +8, ks
+// ascending; scale, mask, exact max; p = bf16(exp2(s - m)); l = sixteen
+// sequential 16-key sums combined as the pairwise tree ((s0+s1)+(s2+s3)) +
+// ... (what the chunk kernel's xor butterfly forms); p.v over keys 32ks +
+// 8(lane>>4) .. +8, ks ascending, V slots at or past kv_len read as zero --
+// so a row's partial has the same bits as from the chunk kernel, and prefill
+// stays bit-equal to decode.
+// LDS: K [16 pages][16 keys][128] with 16-byte chunk c of key k at c ^ (k & 15);
+// V [16 pages][128 features][16 slots] with the 16-byte half h of feature d
+// at h ^ ((d >> 3) & 1); once every tile has its scores, the K area holds each
+// tile's p [16 rows][256 keys] (8 KB per wave, the chunk kernel's swizzle).
+constexpr int PF_WAVES = 8;
+constexpr int PF_ROWS = 16 * PF_WAVES;
+
+template <int G>
+__global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
+    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    const int32_t* __restrict__ page_table, int64_t pt_stride,
+    const int32_t* __restrict__ kv_lens, float* __restrict__ ws_o,
+    float2* __restrict__ ws_ml, int Hq, int Hkv, int n_chunks, int max_kv_len,
+    float scale_log2) {
+    constexpr int D = 128, KS = D / 32, NKT = CHUNK / 16;
+    __shared__ __attribute__((aligned(1024))) char kbuf[16 * PAGE * D * 2];   // K, then p
+    __shared__ __attribute__((aligned(1024))) char vbuf[16 * D * PAGE * 2];
+    __shared__ float mrow[PF_WAVES][16];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int ar = lane & 15, ag = lane >> 4;
+    const int g = blockIdx.x % Hkv, qb = blockIdx.x / Hkv, c = blockIdx.y, b = blockIdx.z;
+    const TileCtx x = tile_ctx<G, PF_WAVES>(b, g, qb, cu_q, kv_lens, pt_stride, max_kv_len);
+    const int j0 = c * CHUNK;
+    if (j0 > x.pos_max) return;                       // no row of the block sees this chunk
+    const int kv_len = x.kv_len;
+
+    // ---- K and V pages 2 wave, 2 wave + 1 of the chunk -> LDS; pages past the
+    // sequence copy page 0 of the cache (their keys are masked, their V slots
+    // read as zero)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int pl = 2 * wave + u;
+        const int pidx = 16 * c + pl;
+        const bool ok = pidx < x.n_pages && pidx < pt_stride;
+        const int64_t ph = ok ? (int64_t)page_table[x.pt_row + pidx] : 0;
+        const char* ksrc = reinterpret_cast<const char*>(kc + (ph * Hkv + g) * (PAGE * D));
+        const char* vsrc = reinterpret_cast<const char*>(vc + (ph * Hkv + g) * (D * PAGE));
+#pragma unroll
+        for (int part = 0; part < 4; ++part) {
+            // LDS position part*1024 + 16 lane: key 4 part + lane / 16, chunk lane & 15
+            const int key = 4 * part + (lane >> 4), pos = lane & 15;
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(ksrc + key * (D * 2) + ((pos ^ key) << 4)),
+                (__attribute__((address_space(3))) void*)(kbuf + pl * (PAGE * D * 2) + part * 1024),
+                16, 0, 0);
+            // LDS position part*1024 + 16 lane: feature 32 part + lane / 2, half lane & 1
+            const int d = 32 * part + (lane >> 1), h = lane & 1;
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(vsrc + d * (PAGE * 2) + ((h ^ ((d >> 3) & 1)) << 4)),
+                (__attribute__((address_space(3))) void*)(vbuf + pl * (D * PAGE * 2) + part * 1024),
+                16, 0, 0);
+        }
+    }
+
+    // ---- q fragments of this wave's tile: row 16 wave + (lane&15), features
+    // 32ks + 8(lane>>4) .. +8
+    u32x4 qf[KS];
+    {
+        const RowInfo a_row = row_info<G, PF_WAVES>(16 * wave + ar, b, g, qb, x.q_len, x.q_start, kv_len);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[ks] = u32x4{0u, 0u, 0u, 0u};
+            if (a_row.token >= 0) qf[ks] = ld16(q + (a_row.token * Hq + a_row.head) * D + 32 * ks + 8 * ag);
+        }
+    }
+    int rpos[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        rpos[e] = row_info<G, PF_WAVES>(16 * wave + 4 * ag + e, b, g, qb, x.q_len, x.q_start, kv_len).pos;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                                  // K and V of the chunk in LDS
+
+    // ---- S = Q K^T: key tile kt holds keys 16 kt .. 16 kt + 15 of the chunk
+    f32x4 sc[NKT];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+        sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const char* krow = kbuf + (16 * kt + ar) * (D * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + (((4 * ks + ag) ^ ar) << 4));
+            sc[kt] = mfma16x16x32(qf[ks], kf, sc[kt]);
+        }
+    }
+    // scale, mask (key <= the row's position), row max over the 256 keys
+    float mx[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        mx[e] = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+            const bool valid = j0 + 16 * kt + ar <= rpos[e];
+            const float v = valid ? sc[kt][e] * scale_log2 : -INFINITY;
+            sc[kt][e] = v;
+            mx[e] = fmaxf(mx[e], v);
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], off));
+    }
+    if (ar == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mrow[wave][4 * ag + e] = mx[e];
+    }
+    __syncthreads();                                  // every tile done with K: its area takes p
+
+    // ---- p = bf16(exp2(s - m)) into this tile's 8 KB of the K area
+    char* pt = kbuf + wave * (16 * CHUNK * 2);
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+        const int key = 16 * kt + ar;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = sc[kt][e];
+            const float p = (v == -INFINITY) ? 0.0f : exp2f(v - mx[e]);
+            *reinterpret_cast<bf16_t*>(pt + p_off(4 * ag + e, key >> 3) + 2 * (key & 7)) =
+                (bf16_t)f32_to_bf16(p);
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile's p, read below by its own wave
+
+    // ---- l of row ar: segments 4(lane>>4) .. +3 summed key by key, then the
+    // pairwise tree over the 16 segment sums
+    float lrow;
+    {
+        float seg[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int sg = 4 * ag + k;
+            const u32x4 p0 = *reinterpret_cast<const u32x4*>(pt + p_off(ar, 2 * sg));
+            const u32x4 p1 = *reinterpret_cast<const u32x4*>(pt + p_off(ar, 2 * sg + 1));
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { acc += lo_bf16(p0[i]); acc += hi_bf16(p0[i]); }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { acc += lo_bf16(p1[i]); acc += hi_bf16(p1[i]); }
+            seg[k] = acc;
+        }
+        float c4 = (seg[0] + seg[1]) + (seg[2] + seg[3]);
+        c4 += __shfl_xor(c4, 16);
+        c4 += __shfl_xor(c4, 32);
+        lrow = c4;
+    }
+
+    // ---- O = P V: feature tile f holds features 16 f .. 16 f + 15; keys
+    // ascending in k-blocks of 32 per (tile, f)
+    u32x4 pa[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+        pa[ks] = *reinterpret_cast<const u32x4*>(pt + p_off(ar, 4 * ks + ag));
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int f = 0; f < D / 16; ++f) {
+        o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int d = 16 * f + ar;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int pl = 2 * ks + (ag >> 1), h = ag & 1;
+            u32x4 v = *reinterpret_cast<const u32x4*>(vbuf + pl * (D * PAGE * 2) + d * (PAGE * 2) +
+                                                      ((h ^ ((d >> 3) & 1)) << 4));
+            const int nvalid = kv_len - ((16 * c + pl) * PAGE + 8 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (2 * i + 1 >= nvalid) v[i] &= (2 * i < nvalid) ? 0x0000ffffu : 0u;
+            }
+            o[f] = mfma16x16x32(pa[ks], v, o[f]);
+        }
+    }
+
+    // ---- partials of the rows that see at least one key of this chunk:
+    // slot (token * n_chunks + c) * Hq + head
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const RowInfo ri = row_info<G, PF_WAVES>(16 * wave + 4 * ag + e, b, g, qb, x.q_len, x.q_start, kv_len);
+        if (ri.token < 0 || ri.pos < j0) continue;
+        const int64_t slot_i = (ri.token * (int64_t)n_chunks + c) * Hq + ri.head;
+#pragma unroll
+        for (int f = 0; f < D / 16; ++f) ws_o[slot_i * D + 16 * f + ar] = o[f][e];
+    }
+    if (ag == 0) {
+        const RowInfo ri = row_info<G, PF_WAVES>(16 * wave + ar, b, g, qb, x.q_len, x.q_start, kv_len);
+        if (ri.token >= 0 && ri.pos >= j0) {
+            const int64_t slot_i = (ri.token * (int64_t)n_chunks + c) * Hq + ri.head;
+            ws_ml[slot_i] = make_float2(mrow[wave][ar], lrow);
+        }
+    }
+}
+
 // One wave per (token, head) row; lane owns features lane (+ 64).
 template <int D, int GMAX>
 __global__ __launch_bounds__(NT) void attn_merge_kernel(
@@ -337,10 +540,32 @@ hipError_t launch_dgr(const AttnArgs& a, hipStream_t s) {
 // decode: one token per sequence, one row tile, looping workgroups, nodes up
 // to level BINV_DECODE_GMAX; prefill: leaves, one chunk per workgroup, two
 // row tiles at D = 128 (one, looping, at D = 64)
+template <int G>
+hipError_t launch_prefill128(const AttnArgs& a, hipStream_t s) {
+    constexpr int TQ = PF_ROWS / G;
+    const int n_chunks = (int)((a.max_kv_len + CHUNK - 1) / CHUNK);
+    const int64_t nqb = (a.max_q_len + TQ - 1) / TQ;
+    const int64_t Rows = a.n_tokens * a.Hq;
+    float* ws_o = a.ws;
+    float2* ws_ml = reinterpret_cast<float2*>(a.ws + Rows * n_chunks * a.D);
+    dim3 grid1((unsigned)(nqb * a.Hkv), (unsigned)n_chunks, (unsigned)a.B);
+    hipLaunchKernelGGL((attn_prefill_kernel<G>), grid1, dim3(64 * PF_WAVES), 0, s,
+                       (const bf16_t*)a.q, a.cu_q, (const bf16_t*)a.k_cache,
+                       (const bf16_t*)a.v_cache, a.page_table, a.pt_stride, a.kv_lens, ws_o,
+                       ws_ml, a.Hq, a.Hkv, n_chunks, (int)a.max_kv_len, a.scale_log2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid2((unsigned)((Rows + 3) / 4));
+    hipLaunchKernelGGL((attn_merge_kernel<128, 0>), grid2, dim3(NT), 0, s, a.cu_q, a.kv_lens, a.B,
+                       a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len, (const float*)ws_o,
+                       (const float2*)ws_ml, (bf16_t*)a.out);
+    return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
     if (a.cu_q) {
-        if constexpr (D == 128) return launch_dgr<D, G, 2, false, 0>(a, s);
+        if constexpr (D == 128) return launch_prefill128<G>(a, s);
         return launch_dgr<D, G, 1, true, 0>(a, s);
     }
     return launch_dgr<D, G, 1, true, BINV_DECODE_GMAX>(a, s);

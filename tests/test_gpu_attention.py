@@ -212,6 +212,32 @@ def test_decode_tree_levels_equal_prefill_leaves(Hq, Hkv, D):
     assert row_rel_err(f64(one_shot[sample]), ref).max() <= TOL_BF16
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (32, 2)])
+def test_prefill_head_groups_parity_and_decode_bitwise(Hq, Hkv):
+    # D = 128 prefill blocks hold 128 / G tokens: G = 1, 8 and 16 besides the
+    # G = 4 of the other tests; ragged batch with cached prefixes
+    D = 128
+    lens = [300, 17, 1000, 600]
+    qlens = [300, 5, 133, 1]
+    cache, seqs = make_cache(lens, Hkv, D, 71 + Hq)
+    T = sum(qlens)
+    q = synth.normal((T, Hq, D), 1.0, 72 + Hq, DEV)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    scale = 1 / math.sqrt(D)
+    out = _prefill(cache, q, cu, lens, max(qlens), max(lens), scale)
+    for b, (k, v) in enumerate(seqs):
+        pos = [lens[b] - qlens[b] + i for i in range(qlens[b])]
+        ref = oracle.attention(f64(q[cu[b]:cu[b + 1]]), pos, f64(k), f64(v), scale)
+        assert row_rel_err(f64(out[cu[b]:cu[b + 1]]), ref).max() <= TOL_BF16, b
+    # every prefill row equals the decode of the same position, bit for bit
+    b_of = np.repeat(np.arange(len(lens)), qlens)
+    pos_of = np.concatenate([[lens[b] - qlens[b] + i for i in range(qlens[b])] for b in range(len(lens))])
+    pt = cache.page_table[torch.as_tensor(b_of, device=DEV)].contiguous()
+    kv = torch.as_tensor(pos_of + 1, dtype=torch.int32, device=DEV)
+    dec = binv.attn_decode(q, cache.k_cache, cache.v_cache, pt, kv, max(lens), scale)
+    assert_bitwise_equal(dec, out, "decode vs prefill")
+
+
 def test_prefill_tile_positions_do_not_change_bits():
     # the same tokens prefilled at different offsets inside the 16-row tiles
     Hq, Hkv, D, L = 32, 8, 128, 777
