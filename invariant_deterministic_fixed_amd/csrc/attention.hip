@@ -538,8 +538,8 @@ hipError_t launch_dgr(const AttnArgs& a, hipStream_t s) {
 }
 
 // decode: one token per sequence, one row tile, looping workgroups, nodes up
-// to level BINV_DECODE_GMAX; prefill: leaves, one chunk per workgroup, two
-// row tiles at D = 128 (one, looping, at D = 64)
+// to level BINV_DECODE_GMAX; prefill: leaves (the 128-row block kernel at
+// D = 128 for calls with long new-token runs, else one row tile, looping)
 template <int G>
 hipError_t launch_prefill128(const AttnArgs& a, hipStream_t s) {
     constexpr int TQ = PF_ROWS / G;
@@ -562,10 +562,17 @@ hipError_t launch_prefill128(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Prefill calls at D = 128 whose longest new-token run fills at least half a
+// 128-row block take the block kernel; calls of a few new tokens per sequence
+// (the decode steps of a mixed-batch engine) take the looping chunk kernel,
+// which spends one 16-row tile, not eight, per (sequence, KV head, chunk).
+// Every row's partial has the same bits from either kernel (the per-element
+// arithmetic is the same), so the choice never reaches the output.
 template <int D, int G>
 hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
     if (a.cu_q) {
-        if constexpr (D == 128) return launch_prefill128<G>(a, s);
+        if constexpr (D == 128)
+            if (a.max_q_len * G >= PF_ROWS / 2) return launch_prefill128<G>(a, s);
         return launch_dgr<D, G, 1, true, 0>(a, s);
     }
     return launch_dgr<D, G, 1, true, BINV_DECODE_GMAX>(a, s);
