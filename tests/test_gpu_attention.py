@@ -238,6 +238,45 @@ def test_prefill_head_groups_parity_and_decode_bitwise(Hq, Hkv):
     assert_bitwise_equal(dec, out, "decode vs prefill")
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (32, 2)])
+def test_prefill_short_and_long_query_runs_bitwise_equal(Hq, Hkv):
+    # At D = 128 a prefill call whose longest new-token run fills less than
+    # half a 128-row block (an engine's decode steps, a few-token tail) runs
+    # on the looping one-tile chunk kernel, a longer one on the block kernel.
+    # The last rows of a long-run call must equal the same rows from short-run
+    # calls (one token each, and the longest run just below the threshold).
+    D = 128
+    G = Hq // Hkv
+    lens = [300, 17, 1000, 600, 4100]
+    cache, seqs = make_cache(lens, Hkv, D, 81 + Hq)
+    scale = 1 / math.sqrt(D)
+    long_q = [160, 5, 333, 1, 260]
+    T = sum(long_q)
+    q = synth.normal((T, Hq, D), 1.0, 82 + Hq, DEV)
+    cu = np.concatenate([[0], np.cumsum(long_q)]).astype(np.int32)
+    assert max(long_q) * G >= 64
+    out_long = _prefill(cache, q, cu, lens, max(long_q), max(lens), scale)
+    # one token per sequence: each sequence's last position
+    last = torch.as_tensor(cu[1:] - 1, dtype=torch.long, device=DEV)
+    q1 = q[last].contiguous()
+    out_one = _prefill(cache, q1, np.arange(len(lens) + 1, dtype=np.int32), lens, 1,
+                       max(lens), scale)
+    assert_bitwise_equal(out_one, out_long[last], "one-token prefill vs block prefill")
+    # the longest run just below the threshold: the last k tokens of each sequence
+    k_run = max(1, (64 - 1) // G)
+    assert k_run * G < 64
+    short_q = [min(k_run, n) for n in long_q]
+    idx = np.concatenate([np.arange(cu[b + 1] - short_q[b], cu[b + 1]) for b in range(len(lens))])
+    idx_t = torch.as_tensor(idx, dtype=torch.long, device=DEV)
+    cu_s = np.concatenate([[0], np.cumsum(short_q)]).astype(np.int32)
+    out_short = _prefill(cache, q[idx_t].contiguous(), cu_s, lens, max(short_q), max(lens), scale)
+    assert_bitwise_equal(out_short, out_long[idx_t], "short-run prefill vs block prefill")
+    # and the oracle on the one-token rows
+    for b, (kk, vv) in enumerate(seqs):
+        ref = oracle.attention(f64(q1[b:b + 1]), [lens[b] - 1], f64(kk), f64(vv), scale)
+        assert row_rel_err(f64(out_one[b:b + 1]), ref).max() <= TOL_BF16, b
+
+
 def test_prefill_tile_positions_do_not_change_bits():
     # the same tokens prefilled at different offsets inside the 16-row tiles
     Hq, Hkv, D, L = 32, 8, 128, 777
