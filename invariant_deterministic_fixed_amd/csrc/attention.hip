@@ -101,8 +101,10 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     const int32_t* __restrict__ page_table, int64_t pt_stride,
     const int32_t* __restrict__ kv_lens, float* __restrict__ ws_o,
     float2* __restrict__ ws_ml, int Hq, int Hkv, int n_chunks, int max_kv_len,
-    float scale_log2) {
+    float scale_log2, int q_skip) {
     constexpr bool VL = (R == 1);           // V through LDS for single-tile (decode) workgroups
+    // prefill: sequences with q_skip or more new tokens belong to the block kernel
+    if (cu_q && cu_q[blockIdx.z + 1] - cu_q[blockIdx.z] >= q_skip) return;
     static_assert(LOOP || GMAX == 0, "workgroups that take one chunk write leaves");
     __shared__ ChunkLds<D, R, VL> sh;
     constexpr int JT = ChunkShape<D>::JT;
@@ -227,8 +229,10 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     const int32_t* __restrict__ page_table, int64_t pt_stride,
     const int32_t* __restrict__ kv_lens, float* __restrict__ ws_o,
     float2* __restrict__ ws_ml, int Hq, int Hkv, int n_chunks, int max_kv_len,
-    float scale_log2) {
+    float scale_log2, int q_min) {
     constexpr int D = 128, KS = D / 32, NKT = CHUNK / 16;
+    // sequences with fewer than q_min new tokens belong to the chunk kernel
+    if (cu_q[blockIdx.z + 1] - cu_q[blockIdx.z] < q_min) return;
     __shared__ __attribute__((aligned(1024))) char kbuf[16 * PAGE * D * 2];   // K, then p
     __shared__ __attribute__((aligned(1024))) char vbuf[16 * D * PAGE * 2];
     __shared__ float mrow[PF_WAVES][16];
@@ -514,11 +518,11 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
 #define BINV_DECODE_GMAX 1
 #endif
 
+// chunk kernel over query tiles [0, nqt) of every sequence; prefill sequences
+// with q_skip or more new tokens are left to the block kernel
 template <int D, int G, int R, bool LOOP, int GMAX>
-hipError_t launch_dgr(const AttnArgs& a, hipStream_t s) {
-    constexpr int TQ = ROWS * R / G;
+hipError_t launch_chunk(const AttnArgs& a, hipStream_t s, int64_t nqt, int q_skip) {
     const int n_chunks = (int)((a.max_kv_len + CHUNK - 1) / CHUNK);
-    const int64_t nqt = a.cu_q ? (a.max_q_len + TQ - 1) / TQ : 1;
     const int64_t Rows = a.n_tokens * a.Hq;
     float* ws_o = a.ws;
     float2* ws_ml = reinterpret_cast<float2*>(a.ws + Rows * n_chunks * a.D);
@@ -527,22 +531,40 @@ hipError_t launch_dgr(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((attn_chunk_kernel<D, G, R, LOOP, GMAX>), grid1, dim3(ChunkShape<D>::NTH),
                        0, s, (const bf16_t*)a.q, a.cu_q, (const bf16_t*)a.k_cache,
                        (const bf16_t*)a.v_cache, a.page_table, a.pt_stride, a.kv_lens, ws_o,
-                       ws_ml, a.Hq, a.Hkv, n_chunks, (int)a.max_kv_len, a.scale_log2);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dim3 grid2((unsigned)((Rows + 3) / 4));
-    hipLaunchKernelGGL((attn_merge_kernel<D, GMAX>), grid2, dim3(NT), 0, s, a.cu_q, a.kv_lens, a.B,
-                       a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len, (const float*)ws_o,
-                       (const float2*)ws_ml, (bf16_t*)a.out);
+                       ws_ml, a.Hq, a.Hkv, n_chunks, (int)a.max_kv_len, a.scale_log2, q_skip);
     return hipGetLastError();
 }
 
-// decode: one token per sequence, one row tile, looping workgroups, nodes up
-// to level BINV_DECODE_GMAX; prefill: leaves (the 128-row block kernel at
-// D = 128 for calls with long new-token runs, else one row tile, looping)
+template <int D, int GMAX>
+hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
+    const int n_chunks = (int)((a.max_kv_len + CHUNK - 1) / CHUNK);
+    const int64_t Rows = a.n_tokens * a.Hq;
+    const float* ws_o = a.ws;
+    const float2* ws_ml = reinterpret_cast<const float2*>(a.ws + Rows * n_chunks * a.D);
+    dim3 grid2((unsigned)((Rows + 3) / 4));
+    hipLaunchKernelGGL((attn_merge_kernel<D, GMAX>), grid2, dim3(NT), 0, s, a.cu_q, a.kv_lens, a.B,
+                       a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len, ws_o, ws_ml,
+                       (bf16_t*)a.out);
+    return hipGetLastError();
+}
+
+template <int D, int G, int R, bool LOOP, int GMAX>
+hipError_t launch_dgr(const AttnArgs& a, hipStream_t s) {
+    constexpr int TQ = ROWS * R / G;
+    const int64_t nqt = a.cu_q ? (a.max_q_len + TQ - 1) / TQ : 1;
+    hipError_t e = launch_chunk<D, G, R, LOOP, GMAX>(a, s, nqt, 0x7fffffff);
+    if (e != hipSuccess) return e;
+    return launch_merge<D, GMAX>(a, s);
+}
+
+// Prefill at D = 128 with long new-token runs: sequences with at least
+// Q_SPLIT = 64 / G new tokens (half a 128-row block) go to the block kernel,
+// the others (e.g. the decode rows of a mixed engine step) to the looping
+// one-tile chunk kernel, whose grid then needs only the query tiles of fewer
+// than Q_SPLIT tokens; both write leaves, merged by one merge launch.
 template <int G>
 hipError_t launch_prefill128(const AttnArgs& a, hipStream_t s) {
-    constexpr int TQ = PF_ROWS / G;
+    constexpr int TQ = PF_ROWS / G, Q_SPLIT = (PF_ROWS / 2 + G - 1) / G, TQ1 = ROWS / G;
     const int n_chunks = (int)((a.max_kv_len + CHUNK - 1) / CHUNK);
     const int64_t nqb = (a.max_q_len + TQ - 1) / TQ;
     const int64_t Rows = a.n_tokens * a.Hq;
@@ -552,22 +574,23 @@ hipError_t launch_prefill128(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((attn_prefill_kernel<G>), grid1, dim3(64 * PF_WAVES), 0, s,
                        (const bf16_t*)a.q, a.cu_q, (const bf16_t*)a.k_cache,
                        (const bf16_t*)a.v_cache, a.page_table, a.pt_stride, a.kv_lens, ws_o,
-                       ws_ml, a.Hq, a.Hkv, n_chunks, (int)a.max_kv_len, a.scale_log2);
+                       ws_ml, a.Hq, a.Hkv, n_chunks, (int)a.max_kv_len, a.scale_log2, Q_SPLIT);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid2((unsigned)((Rows + 3) / 4));
-    hipLaunchKernelGGL((attn_merge_kernel<128, 0>), grid2, dim3(NT), 0, s, a.cu_q, a.kv_lens, a.B,
-                       a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len, (const float*)ws_o,
-                       (const float2*)ws_ml, (bf16_t*)a.out);
-    return hipGetLastError();
+    // max_q_len only bounds the runs: any sequence may be short
+    const int64_t nqt = (Q_SPLIT - 1 + TQ1 - 1) / TQ1;
+    e = launch_chunk<128, G, 1, true, 0>(a, s, nqt, Q_SPLIT);
+    if (e != hipSuccess) return e;
+    return launch_merge<128, 0>(a, s);
 }
 
 // Prefill calls at D = 128 whose longest new-token run fills at least half a
-// 128-row block take the block kernel; calls of a few new tokens per sequence
-// (the decode steps of a mixed-batch engine) take the looping chunk kernel,
-// which spends one 16-row tile, not eight, per (sequence, KV head, chunk).
-// Every row's partial has the same bits from either kernel (the per-element
-// arithmetic is the same), so the choice never reaches the output.
+// 128-row block take the block kernel for their long runs; calls of a few new
+// tokens per sequence (the decode steps of a mixed-batch engine) take the
+// looping chunk kernel alone, which spends one 16-row tile, not eight, per
+// (sequence, KV head, chunk).  Every row's partial has the same bits from
+// either kernel (the per-element arithmetic is the same), so the choice never
+// reaches the output.
 template <int D, int G>
 hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
     if (a.cu_q) {

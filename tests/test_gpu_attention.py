@@ -271,6 +271,13 @@ def test_prefill_short_and_long_query_runs_bitwise_equal(Hq, Hkv):
     cu_s = np.concatenate([[0], np.cumsum(short_q)]).astype(np.int32)
     out_short = _prefill(cache, q[idx_t].contiguous(), cu_s, lens, max(short_q), max(lens), scale)
     assert_bitwise_equal(out_short, out_long[idx_t], "short-run prefill vs block prefill")
+    # a call whose max_q_len overstates its runs (one sequence, 5 new tokens,
+    # bound 200): the short run is still computed, by the chunk kernel
+    b4 = 4
+    rows5 = torch.arange(int(cu[b4 + 1]) - 5, int(cu[b4 + 1]), device=DEV)
+    cache4, _ = make_cache([lens[b4]], Hkv, D, 0, seqs=[seqs[b4]])
+    out5 = _prefill(cache4, q[rows5].contiguous(), [0, 5], [lens[b4]], 200, max(lens), scale)
+    assert_bitwise_equal(out5, out_long[rows5], "overstated max_q_len")
     # and the oracle on the one-token rows
     for b, (kk, vv) in enumerate(seqs):
         ref = oracle.attention(f64(q1[b:b + 1]), [lens[b] - 1], f64(kk), f64(vv), scale)
