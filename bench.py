@@ -397,6 +397,26 @@ def sweep(dev="cuda:0"):
     del c, q, out, ws
     torch.cuda.empty_cache()
 
+    # mixed engine step through the prefill entry point: one sequence runs a
+    # prompt chunk, the others one decode token each, every context ctx long
+    for (B, run_len, ctx) in [(64, 1, 1024), (64, 512, 1024), (256, 256, 2048), (16, 2048, 4096)]:
+        qlens = [run_len] + [1] * (B - 1)
+        c = paged([ctx] * B, synth.seed_for(4) + 7)
+        T = sum(qlens)
+        q = synth.normal((T, HQ, HD), 1.0, 17, dev)
+        out = torch.empty_like(q)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32, device=dev)
+        kvl = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+        ws = torch.empty(binv.attn_workspace_bytes(T, HQ, HD, ctx), dtype=torch.uint8, device=dev)
+        t = _cold_ms([lambda: binv.attn_prefill(q, cu, c.k_cache, c.v_cache, c.page_table, kvl,
+                                                run_len, ctx, 1.0 / math.sqrt(HD), out=out,
+                                                workspace=ws)], reps=5)
+        kv_bytes = B * ctx * HKV * HD * 2 * 2
+        emit(sweep="prefill_mixed", B=B, run=run_len, context=ctx, us=round(t * 1e3, 1),
+             kv_GBps=round(kv_bytes / t / 1e6, 1))
+        del c, q, out, ws
+        torch.cuda.empty_cache()
+
     # 8B-class decoder: decode tokens/s at batch B with 1024-token contexts, all
     # invariant, all tuned, and one locked request among tuned neighbours
     cfg = dec.CONFIG5
