@@ -138,9 +138,12 @@ int binv_gemm_bf16(const void* A, int64_t lda,
  *   and the partials are merged by a binary tree padded to a fixed depth of 9
  *   (tom-jerr.github.io "Batch-Invariant Kernel", section Flash Attention,
  *   fixed-size Split-KV with a chunk-count-independent tree merge).
- *   Decode and prefill run the same chunk and merge code, so a token's output
- *   bits are the same on either path.  An output element that is exactly zero
- *   is written as +0.
+ *   Decode and prefill compute every chunk partial with the same per-element
+ *   arithmetic, whichever kernel a call's shape selects (prefill sequences
+ *   with long new-token runs share one load of each chunk among 128 rows),
+ *   and merge with the same tree, so a token's output bits are the same on
+ *   either path and in any call.  An output element that is exactly zero is
+ *   written as +0.
  *
  * Workspace: fp32 partials, caller-owned, at least
  *   binv_attn_workspace_bytes(n_query_tokens, Hq, D, max_kv_len) bytes.
