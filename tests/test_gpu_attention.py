@@ -278,6 +278,13 @@ def test_prefill_short_and_long_query_runs_bitwise_equal(Hq, Hkv):
     cache4, _ = make_cache([lens[b4]], Hkv, D, 0, seqs=[seqs[b4]])
     out5 = _prefill(cache4, q[rows5].contiguous(), [0, 5], [lens[b4]], 200, max(lens), scale)
     assert_bitwise_equal(out5, out_long[rows5], "overstated max_q_len")
+    # sequences with no new tokens in a long-run call: the others' rows unchanged
+    zq = [long_q[0], 0, long_q[2], 0, long_q[4]]
+    keep = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in (0, 2, 4)])
+    keep_t = torch.as_tensor(keep, dtype=torch.long, device=DEV)
+    cu_z = np.concatenate([[0], np.cumsum(zq)]).astype(np.int32)
+    out_z = _prefill(cache, q[keep_t].contiguous(), cu_z, lens, max(zq), max(lens), scale)
+    assert_bitwise_equal(out_z, out_long[keep_t], "zero-length runs in a mixed call")
     # and the oracle on the one-token rows
     for b, (kk, vv) in enumerate(seqs):
         ref = oracle.attention(f64(q1[b:b + 1]), [lens[b] - 1], f64(kk), f64(vv), scale)
