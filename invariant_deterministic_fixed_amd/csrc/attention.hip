@@ -89,8 +89,11 @@ __device__ __forceinline__ int node_level(int n) {
 // writes and re-reads fewer partials.  gridDim.y is capped at CHUNK_LANES, so
 // a grid sized for the longest allowed sequence does not spend a workgroup
 // per empty node slot of every short sequence.
-// Prefill (cu_q given; R = 2 at D = 128): leaves (L = 0); without looping
-// gridDim.y = the chunk count and a workgroup takes chunk y alone.
+// Prefill (cu_q given; R = 1, looping): leaves (L = 0), for the sequences of
+// a call with fewer than q_skip new tokens (all of them at D = 64, and at
+// D = 128 when no run can fill half a 128-row block); longer runs at D = 128
+// go to attn_prefill_kernel.  Without looping gridDim.y = the chunk count and
+// a workgroup takes chunk y alone.
 //
 // Partials: slot (token * n_chunks + node) * Hq + head of ws_o [.., D] and
 // ws_ml [..] (the G heads of one tile are adjacent).
@@ -205,8 +208,8 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
 // the eight waves owns one 16-row tile outright -- its q.k over all 256 keys,
 // row max, p, l and p.v for all 128 features -- so rows need no cross-wave
 // reduction; the chunk's K and V pages are copied HBM -> LDS once (global_load_lds)
-// and read by all eight tiles, which then share one load of the chunk where
-// the chunk kernel's two-tile workgroups share it among 32 rows.  Every
+// and read by all eight tiles, so 128 rows share one load of the chunk where
+// a chunk-kernel workgroup shares it among 16.  Every
 // per-element operation is the chunk kernel's, in the same order: q.k as
 // v_mfma_f32_16x16x32_bf16 over features 32ks + 8(lane>>4) .. +8, ks
 // ascending; scale, mask, exact max; p = bf16(exp2(s - m)); l = sixteen

@@ -1,10 +1,12 @@
 // attn_chunk.hpp -- per-chunk attention arithmetic shared by the invariant
-// decode / prefill kernels (attention.hip) and the shape-tuned comparator
-// (attention_tuned.hip).  Sharing it is what makes a row's partial for a
-// chunk the same bits on every path.
+// chunk kernel (attention.hip: decode, and prefill runs too short for the
+// 128-row block kernel) and the shape-tuned comparator (attention_tuned.hip).
+// Sharing it is what makes a row's partial for a chunk the same bits on every
+// path; the block kernel repeats the same per-element operations in the same
+// order.
 //
-// A workgroup handles R tiles of 16 query rows (R = 1 for decode, 2 for
-// prefill) against one 256-key chunk.  Nothing a row computes depends on R or
+// A workgroup handles R tiles of 16 query rows (R = 1 in every current launch)
+// against one 256-key chunk.  Nothing a row computes depends on R or
 // on the row's slot: the q.k and p.v products are per-element MFMA chains over
 // fixed k-blocks, the max is exact, and l is summed in one fixed order; R only
 // decides how many rows share one load of the chunk's K and V.
