@@ -459,29 +459,28 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
 
     Partial slot[STACK];
     unsigned count = 0;
-    // leaves are loaded four at a time, the next four in flight while the
-    // current four are pushed into the binary counter in leaf order
+    // nodes are loaded GRP at a time into two buffers used in turn: while one
+    // group is pushed into the binary counter, in node order, the next group's
+    // loads are in flight (no register copy between the buffers, so no wait
+    // for data that is not yet needed).  Loads past the row's last node read
+    // that last node again and are not pushed.
     constexpr int GRP = 4;
-    Partial cur[GRP], nxt[GRP];
+    Partial ba[GRP], bb[GRP];
     auto load_group = [&](Partial (&dst)[GRP], int c0) {
 #pragma unroll
         for (int k = 0; k < GRP; ++k) {
-            const int c = c0 + k;
-            if (c < n) {
-                const float2 ml = pml[(int64_t)c * Hq];
-                dst[k].m = ml.x; dst[k].l = ml.y;
+            const int c = min(c0 + k, n - 1);
+            const float2 ml = pml[(int64_t)c * Hq];
+            dst[k].m = ml.x; dst[k].l = ml.y;
 #pragma unroll
-                for (int i = 0; i < NO; ++i) dst[k].o[i] = po[(int64_t)c * Hq * D + lane + 64 * i];
-            }
+            for (int i = 0; i < NO; ++i) dst[k].o[i] = po[(int64_t)c * Hq * D + lane + 64 * i];
         }
     };
-    load_group(cur, 0);
-    for (int c0 = 0; c0 < n; c0 += GRP) {
-        if (c0 + GRP < n) load_group(nxt, c0 + GRP);
+    auto push_group = [&](const Partial (&src)[GRP], int c0) {
 #pragma unroll
         for (int k = 0; k < GRP; ++k) {
             if (c0 + k >= n) break;
-            Partial carry = cur[k];
+            Partial carry = src[k];
             // binary increment: equal-size subtrees merge, the older one on the left
             bool live = true;
 #pragma unroll
@@ -497,8 +496,14 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
             }
             ++count;
         }
-#pragma unroll
-        for (int k = 0; k < GRP; ++k) cur[k] = nxt[k];
+    };
+    load_group(ba, 0);
+    for (int c0 = 0; c0 < n; c0 += 2 * GRP) {
+        if (c0 + GRP < n) load_group(bb, c0 + GRP);
+        push_group(ba, c0);
+        if (c0 + GRP >= n) break;
+        if (c0 + 2 * GRP < n) load_group(ba, c0 + 2 * GRP);
+        push_group(bb, c0 + GRP);
     }
     // remaining subtrees, smallest (rightmost) first: root = s_hi (+) (... (+) s_lo)
     Partial res;
