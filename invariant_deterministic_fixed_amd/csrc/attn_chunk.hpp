@@ -177,9 +177,38 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
         phys[u] = page_ok[u] ? (int64_t)phys_in[u] : 0;
     }
 
+    // ---- Q fragments (A operand) of each row tile: row 16 rt + (lane&15),
+    // features 32ks + 8(lane>>4) .. +8; issued first, so that waiting for them
+    // (padding rows keep zeros) leaves the K and V loads in flight
+    u32x4 qf[R][KS];
+#pragma unroll
+    for (int rt = 0; rt < R; ++rt) {
+        const RowInfo a_row = row_info<G, R>(16 * rt + ar, x.b, g, x.qt, x.q_len, x.q_start, kv_len);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
+            if (a_row.token >= 0)
+                qf[rt][ks] = ld16(q + (a_row.token * Hq + a_row.head) * D + 32 * ks + 8 * ag);
+        }
+    }
+    // ---- K fragments (B operand of q.k): page 16c + JT*wave + u, key slot lane&15,
+    // features 32ks + 8(lane>>4) .. +8
+    u32x4 kf[JT][KS];
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
+        const bf16_t* kp = kc + ((phys[u] * Hkv + g) * PAGE + (lane & 15)) * D + 8 * ag;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kf[u][ks] = page_ok[u] ? ld16(kp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    if (t < ROWS * R) sh.row_pos[t] = row_info<G, R>(t, x.b, g, x.qt, x.q_len, x.q_start, kv_len).pos;
+
     // ---- V page blocks of the same JT pages -> LDS (4 KB at D = 128, 2 KB at
-    // D = 64, 1 KB per instruction).  Pages past the sequence end copy page 0
-    // of the cache; all their slots are >= kv_len and are zeroed when read.
+    // D = 64, 1 KB per instruction), issued after the q and K loads: loads
+    // retire in issue order, so q.k waits for q and K only while V is still in
+    // flight.  Pages past the sequence end copy page 0 of the cache; all their
+    // slots are >= kv_len and are zeroed when read.
     if constexpr (VL) {
 #pragma unroll
         for (int u = 0; u < JT; ++u) {
@@ -193,32 +222,6 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
                     16, 0, 0);
         }
     }
-
-    // ---- K fragments (B operand of q.k): page 16c + JT*wave + u, key slot lane&15,
-    // features 32ks + 8(lane>>4) .. +8
-    u32x4 kf[JT][KS];
-#pragma unroll
-    for (int u = 0; u < JT; ++u) {
-        const bf16_t* kp = kc + ((phys[u] * Hkv + g) * PAGE + (lane & 15)) * D + 8 * ag;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            kf[u][ks] = page_ok[u] ? ld16(kp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
-    }
-
-    // ---- Q fragments (A operand) of each row tile: row 16 rt + (lane&15),
-    // features 32ks + 8(lane>>4) .. +8
-    u32x4 qf[R][KS];
-#pragma unroll
-    for (int rt = 0; rt < R; ++rt) {
-        const RowInfo a_row = row_info<G, R>(16 * rt + ar, x.b, g, x.qt, x.q_len, x.q_start, kv_len);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
-            if (a_row.token >= 0)
-                qf[rt][ks] = ld16(q + (a_row.token * Hq + a_row.head) * D + 32 * ks + 8 * ag);
-        }
-    }
-    if (t < ROWS * R) sh.row_pos[t] = row_info<G, R>(t, x.b, g, x.qt, x.q_len, x.q_start, kv_len).pos;
 
     // ---- S = Q K^T on the matrix cores
     f32x4 s[R][JT];
@@ -245,8 +248,7 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
                           : u32x4{0u, 0u, 0u, 0u};
         }
     }
-    if constexpr (VL) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // V copies landed
-    __syncthreads();   // row_pos (and with VL every wave's V pages) visible
+    __syncthreads();   // row_pos visible
 
     // lane holds rows 16 rt + 4*(lane>>4) + e, key j0 + 16*(JT*wave + u) + (lane&15)
     const int key_lane = j0 + 16 * JT * wave + (lane & 15);
@@ -300,7 +302,8 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
                     (bf16_t)f32_to_bf16(p);
             }
         }
-    __syncthreads();
+    if constexpr (VL) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's V copies landed
+    __syncthreads();   // p, and with VL every wave's V pages, visible
 
     // ---- l (threads 0 .. 256R-1): thread t sums keys 16(t&15) .. +15 of row t>>4
     // in key order, then a 4-level xor butterfly over the 16 segment sums of the row
