@@ -24,6 +24,15 @@ constexpr int STACK = 10;          // binary counter slots: enough for 1023 leav
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Workgroup barrier for LDS data only: this wave's LDS accesses done, then
+// s_barrier.  Unlike __syncthreads() it does not wait for global loads, so a
+// V copy requested before it stays in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // P tile in LDS: [16 R rows][256 keys] bf16, rows of 512 bytes = 32 chunks of
 // 16 bytes; chunk ch of row r is stored at position ch ^ (r & 31).
 __device__ __forceinline__ int p_off(int r, int ch) { return (r << 9) + ((ch ^ (r & 31)) << 4); }
@@ -112,7 +121,6 @@ struct ChunkLds {
     __attribute__((aligned(1024))) char v[VL ? 16 * D * PAGE * 2 : 16];
     __attribute__((aligned(16))) char p[ROWS * R * CHUNK * 2];
     float red_max[ChunkShape<D>::NW][ROWS * R];
-    int row_pos[ROWS * R];
 };
 
 // Result of one chunk for the workgroup's 16R rows:
@@ -178,18 +186,18 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
     }
 
     // ---- Q fragments (A operand) of each row tile: row 16 rt + (lane&15),
-    // features 32ks + 8(lane>>4) .. +8; issued first, so that waiting for them
-    // (padding rows keep zeros) leaves the K and V loads in flight
+    // features 32ks + 8(lane>>4) .. +8.  A padding row (no token) reads the
+    // tile's first token instead of branching around its load: every key is
+    // masked for it (position -1), so its scores, p and partial are never
+    // used, and no row's result depends on another row's q.
     u32x4 qf[R][KS];
 #pragma unroll
     for (int rt = 0; rt < R; ++rt) {
         const RowInfo a_row = row_info<G, R>(16 * rt + ar, x.b, g, x.qt, x.q_len, x.q_start, kv_len);
+        const int64_t tok = a_row.token >= 0 ? a_row.token : x.q_start;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
-            if (a_row.token >= 0)
-                qf[rt][ks] = ld16(q + (a_row.token * Hq + a_row.head) * D + 32 * ks + 8 * ag);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+            qf[rt][ks] = ld16(q + (tok * Hq + a_row.head) * D + 32 * ks + 8 * ag);
     }
     // ---- K fragments (B operand of q.k): page 16c + JT*wave + u, key slot lane&15,
     // features 32ks + 8(lane>>4) .. +8
@@ -202,13 +210,29 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
             kf[u][ks] = page_ok[u] ? ld16(kp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
     }
 
-    if (t < ROWS * R) sh.row_pos[t] = row_info<G, R>(t, x.b, g, x.qt, x.q_len, x.q_start, kv_len).pos;
 
+    // ---- S = Q K^T on the matrix cores
+    f32x4 s[R][JT];
+#pragma unroll
+    for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+        for (int u = 0; u < JT; ++u) {
+            s[rt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) s[rt][u] = mfma16x16x32(qf[rt][ks], kf[u][ks], s[rt][u]);
+        }
+    if constexpr (VL) {
+#pragma unroll
+        for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+            for (int u = 0; u < JT; ++u) asm volatile("" : "+v"(s[rt][u]) : : "memory");
+    }
     // ---- V page blocks of the same JT pages -> LDS (4 KB at D = 128, 2 KB at
-    // D = 64, 1 KB per instruction), issued after the q and K loads: loads
-    // retire in issue order, so q.k waits for q and K only while V is still in
-    // flight.  Pages past the sequence end copy page 0 of the cache; all their
-    // slots are >= kv_len and are zeroed when read.
+    // D = 64, 1 KB per instruction), requested once the q.k products are
+    // issued (the fence ties the scores to this point), so that q.k waits for
+    // q and K only and V arrives while the scores are masked, reduced and
+    // turned into p.  Pages past the sequence end copy page 0 of the cache;
+    // all their slots are >= kv_len and are zeroed when read.
     if constexpr (VL) {
 #pragma unroll
         for (int u = 0; u < JT; ++u) {
@@ -223,16 +247,6 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
         }
     }
 
-    // ---- S = Q K^T on the matrix cores
-    f32x4 s[R][JT];
-#pragma unroll
-    for (int rt = 0; rt < R; ++rt)
-#pragma unroll
-        for (int u = 0; u < JT; ++u) {
-            s[rt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) s[rt][u] = mfma16x16x32(qf[rt][ks], kf[u][ks], s[rt][u]);
-        }
     // ---- without VL: V fragments straight into registers, issued once the
     // q.k products are queued: feature d = 16 wave + (lane&15), keys
     // 32ks + 8(lane>>4) .. +8 = page 16c + 2ks + (ag>>1), slots 8(ag&1) .. +8
@@ -248,7 +262,6 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
                           : u32x4{0u, 0u, 0u, 0u};
         }
     }
-    __syncthreads();   // row_pos visible
 
     // lane holds rows 16 rt + 4*(lane>>4) + e, key j0 + 16*(JT*wave + u) + (lane&15)
     const int key_lane = j0 + 16 * JT * wave + (lane & 15);
@@ -258,7 +271,8 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
         float mx[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int rpos = sh.row_pos[16 * rt + 4 * ag + e];
+            const int rpos = row_info<G, R>(16 * rt + 4 * ag + e, x.b, g, x.qt, x.q_len,
+                                            x.q_start, kv_len).pos;
             mx[e] = -INFINITY;
 #pragma unroll
             for (int u = 0; u < JT; ++u) {
@@ -275,7 +289,7 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
             for (int e = 0; e < 4; ++e) sh.red_max[wave][16 * rt + 4 * ag + e] = mx[e];
         }
     }
-    __syncthreads();
+    lds_barrier();     // every wave's row maxima visible (V may still be in flight)
 #pragma unroll
     for (int rt = 0; rt < R; ++rt)
 #pragma unroll
