@@ -125,8 +125,10 @@ int binv_gemm_bf16(const void* A, int64_t lda,
  *   Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8, 16}.
  *
  * Only the first ceil(kv_lens[b] / 16) page-table entries of a sequence are
- * read, and slots at or past kv_lens[b] are never used (they may hold any
- * bits, NaN included).
+ * used as page indices (later entries of the row, within its pt_stride, may
+ * be read ahead but never dereferenced; they may hold any value), and slots
+ * at or past kv_lens[b] are never used (they may hold any bits, NaN
+ * included).
  *
  * Attention computed (devpress.csdn.net explainer, section 3.3: two
  * reductions over the KV length; fixed-size split example):

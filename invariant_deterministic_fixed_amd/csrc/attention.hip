@@ -117,10 +117,18 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     const int glog = (GMAX > 0 && !cu_q && pos_max >= 0) ? node_level<GMAX>(pos_max / CHUNK + 1) : 0;
     const int gs = 1 << glog;
     int phys_next[JT];
+    // K of the workgroup's current chunk: the first chunk's requested here,
+    // every later one by the chunk before it
+    u32x4 kf[JT][ChunkShape<D>::KS];
     {
         TileCtx x0;
         x0.pt_row = (int64_t)blockIdx.z * pt_stride;
         load_phys<D>(x0, blockIdx.y * gs, page_table, pt_stride, phys_next, threadIdx.x);
+        if (blockIdx.y * gs * CHUNK <= pos_max) {
+            const TileCtx x1 = tile_ctx_len<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv,
+                                                  cu_q, kv_len_b, pt_stride, max_kv_len);
+            load_k<D>(x1, blockIdx.y * gs, phys_next, kc, pt_stride, Hkv, kf, threadIdx.x);
+        }
     }
 #pragma clang loop unroll(disable)
     for (int node = blockIdx.y; node * gs * CHUNK <= pos_max; node += gridDim.y) {
@@ -141,14 +149,19 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
             int phys[JT];
 #pragma unroll
             for (int u = 0; u < JT; ++u) phys[u] = phys_next[u];
+            // the next chunk this workgroup takes: its page-table entries now,
+            // its K once this chunk's V is requested
+            int c_nx = -1;
             if constexpr (LOOP) {
-                // page-table entries of the next chunk this workgroup takes
                 const int c_next = (i + 1 < gs) ? c + 1 : (node + (int)gridDim.y) * gs;
-                if (c_next * CHUNK <= pos_max)
+                if (c_next * CHUNK <= pos_max) {
                     load_phys<D>(x, c_next, page_table, pt_stride, phys_next, t);
+                    c_nx = c_next;
+                }
             }
-            ChunkOut<R> carry = chunk_compute<D, G, R, VL>(x, c, phys, page_table, q, kc, vc,
-                                                           pt_stride, Hq, Hkv, scale_log2, sh, t);
+            ChunkOut<R> carry = chunk_compute<D, G, R, VL, LOOP>(
+                x, c, phys, page_table, q, kc, vc, pt_stride, Hq, Hkv, scale_log2, sh, t, kf, c_nx,
+                phys_next);
             // binary increment: equal-size subtrees merge, the older one on the left
             bool live = true;
 #pragma unroll

@@ -60,8 +60,10 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_spl
         __syncthreads();                           // LDS of the previous chunk is free
         int phys[ChunkShape<D>::JT];
         load_phys<D>(x, c, page_table, pt_stride, phys, t);
+        u32x4 kf[ChunkShape<D>::JT][ChunkShape<D>::KS];
         const ChunkOut<1> r = chunk_compute<D, G, 1, true>(x, c, phys, page_table, q, kc, vc,
-                                                           pt_stride, Hq, Hkv, scale_log2, sh, t);
+                                                           pt_stride, Hq, Hkv, scale_log2, sh, t,
+                                                           kf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             if (r.m[0][e] == -INFINITY) continue;

@@ -136,8 +136,7 @@ struct ChunkOut {
 };
 
 // Page-table entries of the JT pages this wave reads in chunk c (independent
-// of kv_len, so they can be fetched up front; only x.pt_row is used); 0 past
-// the table's row.
+// of kv_len, so they can be fetched up front; only x.pt_row is used).
 // t = threadIdx.x, passed in so that a caller looping over chunks can keep
 // the lane-derived arithmetic inside its loop.
 template <int D>
@@ -148,8 +147,31 @@ __device__ __forceinline__ void load_phys(const TileCtx& x, int c,
     const int wave = t >> 6;
 #pragma unroll
     for (int u = 0; u < JT; ++u) {
+        // an index past the row reads the row's last entry (no branch around
+        // the load, so nothing waits for it before its use); every user
+        // replaces entries at or past the sequence's page count by page 0
+        const int pidx = min(16 * c + JT * wave + u, (int)pt_stride - 1);
+        phys[u] = page_table[x.pt_row + pidx];
+    }
+}
+
+// K fragments (B operand of q.k) of chunk c: page 16c + JT*wave + u, key slot
+// lane&15, features 32ks + 8(lane>>4) .. +8.  Pages past the sequence's last
+// one read page 0 of the cache instead (no branch around the loads): all
+// their keys are past every row's position and masked.
+template <int D>
+__device__ __forceinline__ void load_k(const TileCtx& x, int c, const int (&phys_in)[ChunkShape<D>::JT],
+                                       const bf16_t* __restrict__ kc, int64_t pt_stride, int Hkv,
+                                       u32x4 (&kf)[ChunkShape<D>::JT][ChunkShape<D>::KS], int t) {
+    constexpr int JT = ChunkShape<D>::JT, KS = ChunkShape<D>::KS;
+    const int lane = t & 63, wave = t >> 6, ag = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
         const int pidx = 16 * c + JT * wave + u;
-        phys[u] = (pidx < pt_stride) ? page_table[x.pt_row + pidx] : 0;
+        const int64_t ph = (pidx < x.n_pages && pidx < pt_stride) ? (int64_t)phys_in[u] : 0;
+        const bf16_t* kp = kc + ((ph * Hkv + x.g) * PAGE + (lane & 15)) * D + 8 * ag;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[u][ks] = ld16(kp + 32 * ks);
     }
 }
 
@@ -160,12 +182,18 @@ __device__ __forceinline__ void load_phys(const TileCtx& x, int c,
 // or straight from memory into registers after q.k (prefill, where 16R rows
 // share each V fragment and LDS is better spent on more workgroups per CU).
 // Either way every lane feeds the same V values into the same p.v chain.
-template <int D, int G, int R, bool VL>
+// KPRE: kf already holds chunk c's K (requested by the previous chunk); once
+// this chunk's V is requested, chunk c_nx's K (c_nx >= 0) is requested into
+// kf, to arrive while this chunk's softmax and p.v run.  Without KPRE chunk
+// c's K is requested here.
+template <int D, int G, int R, bool VL, bool KPRE = false>
 __device__ __forceinline__ ChunkOut<R> chunk_compute(
     const TileCtx& x, int c, const int (&phys_in)[ChunkShape<D>::JT],
     const int32_t* __restrict__ page_table, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, int64_t pt_stride,
-    int Hq, int Hkv, float scale_log2, ChunkLds<D, R, VL>& sh, int t) {
+    int Hq, int Hkv, float scale_log2, ChunkLds<D, R, VL>& sh, int t,
+    u32x4 (&kf)[ChunkShape<D>::JT][ChunkShape<D>::KS], int c_nx = -1,
+    const int (&phys_nx)[ChunkShape<D>::JT] = {}) {
     using S = ChunkShape<D>;
     constexpr int NW = S::NW, JT = S::JT, KS = S::KS;
     static_assert(S::NTH >= 256 * R, "one thread per (row, 16-key segment) for l");
@@ -199,16 +227,8 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
         for (int ks = 0; ks < KS; ++ks)
             qf[rt][ks] = ld16(q + (tok * Hq + a_row.head) * D + 32 * ks + 8 * ag);
     }
-    // ---- K fragments (B operand of q.k): page 16c + JT*wave + u, key slot lane&15,
-    // features 32ks + 8(lane>>4) .. +8
-    u32x4 kf[JT][KS];
-#pragma unroll
-    for (int u = 0; u < JT; ++u) {
-        const bf16_t* kp = kc + ((phys[u] * Hkv + g) * PAGE + (lane & 15)) * D + 8 * ag;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            kf[u][ks] = page_ok[u] ? ld16(kp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
-    }
+    // ---- K fragments (B operand of q.k)
+    if constexpr (!KPRE) load_k<D>(x, c, phys_in, kc, pt_stride, Hkv, kf, t);
 
 
     // ---- S = Q K^T on the matrix cores
@@ -245,6 +265,14 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
                     (__attribute__((address_space(3))) void*)(sh.v + pl * (D * PAGE * 2) + part * 1024),
                     16, 0, 0);
         }
+    }
+    // ---- the next chunk's K, requested after this chunk's V (loads retire in
+    // issue order: the wait for V below leaves these JT*KS loads in flight)
+    constexpr int KPRE_LOADS = KPRE ? JT * KS : 0;
+    const bool kpre = KPRE && c_nx >= 0;
+    if constexpr (KPRE) {
+        asm volatile("" ::: "memory");
+        if (kpre) load_k<D>(x, c_nx, phys_nx, kc, pt_stride, Hkv, kf, t);
     }
 
     // ---- without VL: V fragments straight into registers, issued once the
@@ -316,8 +344,13 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
                     (bf16_t)f32_to_bf16(p);
             }
         }
-    if constexpr (VL) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's V copies landed
-    __syncthreads();   // p, and with VL every wave's V pages, visible
+    if constexpr (VL) {                                // this wave's V copies landed
+        if (kpre)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(KPRE_LOADS) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    lds_barrier();     // p, and with VL every wave's V pages, visible
 
     // ---- l (threads 0 .. 256R-1): thread t sums keys 16(t&15) .. +15 of row t>>4
     // in key order, then a 4-level xor butterfly over the 16 segment sums of the row
