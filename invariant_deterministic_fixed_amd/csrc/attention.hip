@@ -249,9 +249,20 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     constexpr int D = 128, KS = D / 32, NKT = CHUNK / 16;
     // sequences with fewer than q_min new tokens belong to the chunk kernel
     if (cu_q[blockIdx.z + 1] - cu_q[blockIdx.z] < q_min) return;
-    __shared__ __attribute__((aligned(1024))) char kbuf[16 * PAGE * D * 2];   // K, then p
-    __shared__ __attribute__((aligned(1024))) char vbuf[16 * D * PAGE * 2];
-    __shared__ float mrow[PF_WAVES][16];
+    // one object, so that the compiler can tell the V copy's destination from
+    // the q and K areas read while it is in flight
+    struct PfLds {
+        __attribute__((aligned(1024))) char k[16 * PAGE * D * 2];   // K, then p
+        __attribute__((aligned(1024))) char v[16 * D * PAGE * 2];
+        // q of the block's 128 rows [row][D], 16-byte chunk c of row r at
+        // c ^ (r & 15); once a wave has read its 16 rows, their first 64 bytes
+        // hold its row maxima
+        __attribute__((aligned(1024))) char q[PF_ROWS * D * 2];
+    };
+    __shared__ PfLds sh;
+    char* const kbuf = sh.k;
+    char* const vbuf = sh.v;
+    char* const qbuf = sh.q;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int ar = lane & 15, ag = lane >> 4;
     const int g = blockIdx.x % Hkv, qb = blockIdx.x / Hkv, c = blockIdx.y, b = blockIdx.z;
@@ -260,51 +271,85 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     if (j0 > x.pos_max) return;                       // no row of the block sees this chunk
     const int kv_len = x.kv_len;
 
-    // ---- K and V pages 2 wave, 2 wave + 1 of the chunk -> LDS; pages past the
-    // sequence copy page 0 of the cache (their keys are masked, their V slots
-    // read as zero)
+    // ---- HBM -> LDS by global_load_lds, in the order the block needs them:
+    // this wave's 16 q rows (a row without a token copies the block's first
+    // token: every key is masked for it), then K and then V pages 2 wave,
+    // 2 wave + 1 of the chunk (pages past the sequence copy page 0 of the
+    // cache: their keys are masked, their V slots read as zero).  Copies
+    // retire in issue order, so q.k waits for q and K while V is in flight.
+    {
+        const char* qsrc[4];
+#pragma unroll
+        for (int part = 0; part < 4; ++part) {
+            // LDS position part*1024 + 16 lane: row 4 part + lane / 16 of the wave's
+            // tile, chunk lane & 15 holding feature chunk (lane & 15) ^ row
+            const int rr = 4 * part + (lane >> 4);
+            const RowInfo ri = row_info<G, PF_WAVES>(16 * wave + rr, b, g, qb, x.q_len, x.q_start, kv_len);
+            const int64_t tok = ri.token >= 0 ? ri.token : x.q_start;
+            qsrc[part] = reinterpret_cast<const char*>(q + (tok * Hq + ri.head) * D) +
+                         (((lane & 15) ^ rr) << 4);
+        }
+#pragma unroll
+        for (int part = 0; part < 4; ++part)
+            __builtin_amdgcn_global_load_lds(
+                (const void*)qsrc[part],
+                (__attribute__((address_space(3))) void*)(qbuf + wave * (16 * D * 2) + part * 1024),
+                16, 0, 0);
+    }
+    const char* ksrc[2];
+    const char* vsrc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int pidx = 16 * c + 2 * wave + u;
+        const bool ok = pidx < x.n_pages && pidx < pt_stride;
+        const int64_t ph = ok ? (int64_t)page_table[x.pt_row + pidx] : 0;
+        ksrc[u] = reinterpret_cast<const char*>(kc + (ph * Hkv + g) * (PAGE * D));
+        vsrc[u] = reinterpret_cast<const char*>(vc + (ph * Hkv + g) * (D * PAGE));
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int pl = 2 * wave + u;
-        const int pidx = 16 * c + pl;
-        const bool ok = pidx < x.n_pages && pidx < pt_stride;
-        const int64_t ph = ok ? (int64_t)page_table[x.pt_row + pidx] : 0;
-        const char* ksrc = reinterpret_cast<const char*>(kc + (ph * Hkv + g) * (PAGE * D));
-        const char* vsrc = reinterpret_cast<const char*>(vc + (ph * Hkv + g) * (D * PAGE));
 #pragma unroll
         for (int part = 0; part < 4; ++part) {
             // LDS position part*1024 + 16 lane: key 4 part + lane / 16, chunk lane & 15
             const int key = 4 * part + (lane >> 4), pos = lane & 15;
             __builtin_amdgcn_global_load_lds(
-                (const void*)(ksrc + key * (D * 2) + ((pos ^ key) << 4)),
+                (const void*)(ksrc[u] + key * (D * 2) + ((pos ^ key) << 4)),
                 (__attribute__((address_space(3))) void*)(kbuf + pl * (PAGE * D * 2) + part * 1024),
                 16, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int pl = 2 * wave + u;
+#pragma unroll
+        for (int part = 0; part < 4; ++part) {
             // LDS position part*1024 + 16 lane: feature 32 part + lane / 2, half lane & 1
             const int d = 32 * part + (lane >> 1), h = lane & 1;
             __builtin_amdgcn_global_load_lds(
-                (const void*)(vsrc + d * (PAGE * 2) + ((h ^ ((d >> 3) & 1)) << 4)),
+                (const void*)(vsrc[u] + d * (PAGE * 2) + ((h ^ ((d >> 3) & 1)) << 4)),
                 (__attribute__((address_space(3))) void*)(vbuf + pl * (D * PAGE * 2) + part * 1024),
                 16, 0, 0);
         }
     }
 
-    // ---- q fragments of this wave's tile: row 16 wave + (lane&15), features
-    // 32ks + 8(lane>>4) .. +8
-    u32x4 qf[KS];
-    {
-        const RowInfo a_row = row_info<G, PF_WAVES>(16 * wave + ar, b, g, qb, x.q_len, x.q_start, kv_len);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qf[ks] = u32x4{0u, 0u, 0u, 0u};
-            if (a_row.token >= 0) qf[ks] = ld16(q + (a_row.token * Hq + a_row.head) * D + 32 * ks + 8 * ag);
-        }
-    }
     int rpos[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         rpos[e] = row_info<G, PF_WAVES>(16 * wave + 4 * ag + e, b, g, qb, x.q_len, x.q_start, kv_len).pos;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();                                  // K and V of the chunk in LDS
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // this wave's q and K copies landed
+    lds_barrier();                                    // every wave's: q and K of the block in LDS
+
+    // ---- q fragments of this wave's tile: row 16 wave + (lane&15), features
+    // 32ks + 8(lane>>4) .. +8
+    u32x4 qf[KS];
+    {
+        const char* qrow = qbuf + (16 * wave + ar) * (D * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = *reinterpret_cast<const u32x4*>(qrow + (((4 * ks + ag) ^ ar) << 4));
+    }
+    float* mrow = reinterpret_cast<float*>(qbuf + wave * (16 * D * 2));   // after the reads above
 
     // ---- S = Q K^T: key tile kt holds keys 16 kt .. 16 kt + 15 of the chunk
     f32x4 sc[NKT];
@@ -335,9 +380,9 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     }
     if (ar == 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mrow[wave][4 * ag + e] = mx[e];
+        for (int e = 0; e < 4; ++e) mrow[4 * ag + e] = mx[e];
     }
-    __syncthreads();                                  // every tile done with K: its area takes p
+    lds_barrier();                                    // every tile done with K: its area takes p
 
     // ---- p = bf16(exp2(s - m)) into this tile's 8 KB of the K area
     char* pt = kbuf + wave * (16 * CHUNK * 2);
@@ -376,6 +421,9 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
         c4 += __shfl_xor(c4, 32);
         lrow = c4;
     }
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's V copies landed
+    lds_barrier();                                    // every wave's: V of the chunk in LDS
 
     // ---- O = P V: feature tile f holds features 16 f .. 16 f + 15; keys
     // ascending in k-blocks of 32 per (tile, f)
@@ -416,7 +464,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
         const RowInfo ri = row_info<G, PF_WAVES>(16 * wave + ar, b, g, qb, x.q_len, x.q_start, kv_len);
         if (ri.token >= 0 && ri.pos >= j0) {
             const int64_t slot_i = (ri.token * (int64_t)n_chunks + c) * Hq + ri.head;
-            ws_ml[slot_i] = make_float2(mrow[wave][ar], lrow);
+            ws_ml[slot_i] = make_float2(mrow[ar], lrow);
         }
     }
 }
