@@ -128,6 +128,11 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
             const TileCtx x1 = tile_ctx_len<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv,
                                                   cu_q, kv_len_b, pt_stride, max_kv_len);
             load_k<D>(x1, blockIdx.y * gs, phys_next, kc, pt_stride, Hkv, kf, threadIdx.x);
+            // the tile's q, the same for every chunk, staged in LDS once
+            if constexpr (LOOP) {
+                stage_q<D, G, R, VL>(x1, q, Hq, sh, threadIdx.x);
+                lds_barrier();
+            }
         }
     }
 #pragma clang loop unroll(disable)

@@ -121,6 +121,9 @@ struct ChunkLds {
     __attribute__((aligned(1024))) char v[VL ? 16 * D * PAGE * 2 : 16];
     __attribute__((aligned(16))) char p[ROWS * R * CHUNK * 2];
     float red_max[ChunkShape<D>::NW][ROWS * R];
+    // q fragments of the tile for a workgroup that loops over chunks (its rows
+    // do not change): [row tile][k-step][lane] 16 bytes each
+    __attribute__((aligned(16))) char qf[R * ChunkShape<D>::KS * 64 * 16];
 };
 
 // Result of one chunk for the workgroup's 16R rows:
@@ -175,6 +178,26 @@ __device__ __forceinline__ void load_k(const TileCtx& x, int c, const int (&phys
     }
 }
 
+// q fragments of the workgroup's tile -> sh.qf (wave 0 loads and writes them;
+// the caller's barrier makes them visible).  A padding row reads the tile's
+// first token: every key is masked for it.
+template <int D, int G, int R, bool VL>
+__device__ __forceinline__ void stage_q(const TileCtx& x, const bf16_t* __restrict__ q, int Hq,
+                                        ChunkLds<D, R, VL>& sh, int t) {
+    constexpr int KS = ChunkShape<D>::KS;
+    const int lane = t & 63, ar = lane & 15, ag = lane >> 4;
+    if (t >= 64) return;
+#pragma unroll
+    for (int rt = 0; rt < R; ++rt) {
+        const RowInfo a_row = row_info<G, R>(16 * rt + ar, x.b, x.g, x.qt, x.q_len, x.q_start, x.kv_len);
+        const int64_t tok = a_row.token >= 0 ? a_row.token : x.q_start;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            *reinterpret_cast<u32x4*>(sh.qf + ((rt * KS + ks) * 64 + lane) * 16) =
+                ld16(q + (tok * Hq + a_row.head) * D + 32 * ks + 8 * ag);
+    }
+}
+
 // The per-chunk arithmetic shared by decode, prefill and the comparator: keys
 // [256c, 256c+256) of the tile's sequence, each row limited to keys <= its
 // position.  LDS may be reused only after a __syncthreads().  t = threadIdx.x.
@@ -219,13 +242,22 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
     // masked for it (position -1), so its scores, p and partial are never
     // used, and no row's result depends on another row's q.
     u32x4 qf[R][KS];
+    if constexpr (KPRE) {
+        // a looping workgroup's q, staged in LDS once (stage_q)
 #pragma unroll
-    for (int rt = 0; rt < R; ++rt) {
-        const RowInfo a_row = row_info<G, R>(16 * rt + ar, x.b, g, x.qt, x.q_len, x.q_start, kv_len);
-        const int64_t tok = a_row.token >= 0 ? a_row.token : x.q_start;
+        for (int rt = 0; rt < R; ++rt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qf[rt][ks] = ld16(q + (tok * Hq + a_row.head) * D + 32 * ks + 8 * ag);
+            for (int ks = 0; ks < KS; ++ks)
+                qf[rt][ks] = *reinterpret_cast<const u32x4*>(sh.qf + ((rt * KS + ks) * 64 + lane) * 16);
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < R; ++rt) {
+            const RowInfo a_row = row_info<G, R>(16 * rt + ar, x.b, g, x.qt, x.q_len, x.q_start, kv_len);
+            const int64_t tok = a_row.token >= 0 ? a_row.token : x.q_start;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[rt][ks] = ld16(q + (tok * Hq + a_row.head) * D + 32 * ks + 8 * ag);
+        }
     }
     // ---- K fragments (B operand of q.k)
     if constexpr (!KPRE) load_k<D>(x, c, phys_in, kc, pt_stride, Hkv, kf, t);
