@@ -55,7 +55,7 @@ using namespace attn;
 
 // workgroups per (query tile, KV head) of a decode sequence; they loop over
 // the sequence's nodes
-constexpr int CHUNK_LANES = 16;
+constexpr int CHUNK_LANES = 32;
 
 // Level of the merge tree at which a decode row's partials are handed from
 // the chunk kernel to the merge kernel, from the row's chunk count n: the
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
 }
 
 #ifndef BINV_DECODE_GMAX
-#define BINV_DECODE_GMAX 1
+#define BINV_DECODE_GMAX 2
 #endif
 
 // chunk kernel over query tiles [0, nqt) of every sequence; prefill sequences

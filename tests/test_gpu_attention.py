@@ -189,10 +189,10 @@ def test_prefill_chunked_and_decode_bitwise_equal():
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (4, 4, 64)])
 def test_decode_tree_levels_equal_prefill_leaves(Hq, Hkv, D):
-    # Decode hands a row's partials to the merge kernel as nodes of one or two
-    # chunks depending on its chunk count (1..16: leaves; 17..32: pairs; 33 and
-    # 34: leaves again); prefill always hands over leaves.  Every decode
-    # position must equal the one-shot prefill of the same position bit for bit.
+    # Decode hands a row's partials to the merge kernel as nodes of one, two or
+    # four chunks depending on its chunk count; prefill always hands over
+    # leaves.  Every decode position must equal the one-shot prefill of the
+    # same position bit for bit.
     L = 34 * 256 - 100
     scale = 1 / math.sqrt(D)
     k, v = synth.random_kv(L, Hkv, D, 91, DEV)
@@ -210,6 +210,33 @@ def test_decode_tree_levels_equal_prefill_leaves(Hq, Hkv, D):
     sample = [0, 4096, 8447, L - 1]
     ref = oracle.attention(f64(q[sample]), sample, f64(k), f64(v), scale)
     assert row_rel_err(f64(one_shot[sample]), ref).max() <= TOL_BF16
+
+
+def test_decode_long_rows_every_node_level_equal_leaves():
+    # Rows of 1 .. 130 chunks: decode hands them over as leaves, pairs or
+    # nodes of four chunks (the level follows the row's chunk count); the
+    # same rows as one-token prefill sequences are merged from leaves.  Both
+    # must give the same bits; a few rows against the oracle.
+    Hq, Hkv, D = 32, 8, 128
+    L = 130 * 256 - 100
+    scale = 1 / math.sqrt(D)
+    k, v = synth.random_kv(L, Hkv, D, 95, DEV)
+    cache, _ = make_cache([L], Hkv, D, 96, seqs=[(k, v)])
+    rng = np.random.default_rng(97)
+    edges = [0, 255, 256] + [256 * n + d for n in (16, 32, 48, 64, 96, 112, 128) for d in (-1, 0)]
+    rows = np.unique(np.concatenate([edges, rng.integers(0, L, 100), [L - 1]])).astype(np.int64)
+    n = len(rows)
+    qr = synth.normal((n, Hq, D), 1.0, 98, DEV)
+    pt = cache.page_table[:1].expand(n, -1).contiguous()
+    kv_lens = torch.as_tensor(rows + 1, dtype=torch.int32, device=DEV)
+    dec = binv.attn_decode(qr, cache.k_cache, cache.v_cache, pt, kv_lens, L, scale)
+    leaves = binv.attn_prefill(qr, torch.arange(n + 1, dtype=torch.int32, device=DEV),
+                               cache.k_cache, cache.v_cache, pt, kv_lens, 1, L, scale)
+    assert_bitwise_equal(dec, leaves, "decode nodes vs prefill leaves")
+    for i in [0, int(np.searchsorted(rows, 256 * 97)), n - 1]:
+        p = int(rows[i])
+        ref = oracle.attention(f64(qr[i:i + 1]), [p], f64(k), f64(v), scale)
+        assert row_rel_err(f64(dec[i:i + 1]), ref).max() <= TOL_BF16, p
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (32, 2)])
