@@ -474,15 +474,42 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     }
 }
 
-// One wave per (token, head) row; lane owns features lane (+ 64).
-template <int D, int GMAX>
+// A node as the merge holds it: per lane VPL consecutive features of one row.
+template <int VPL>
+struct MergeNode {
+    float m, l;
+    float o[VPL];
+};
+template <int VPL>
+__device__ __forceinline__ MergeNode<VPL> combine_node(const MergeNode<VPL>& a,
+                                                       const MergeNode<VPL>& b) {
+    MergeNode<VPL> r;
+    float fa, fb;
+    combine_scale(a.m, b.m, r.m, fa, fb);
+    r.l = combine_val(fa, a.l, fb, b.l);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) r.o[i] = combine_val(fa, a.o[i], fb, b.o[i]);
+    return r;
+}
+
+constexpr int MERGE_VPL = 4;
+
+// D / VPL lanes per (token, head) row, each owning VPL = 4 consecutive
+// features: one 16-byte load per node and lane (single-feature lanes took
+// 4 % longer on a 4096-token prefill), 64 VPL / D rows per wave.  SK
+// binary-counter slots hold any row of at most 2^SK - 1 nodes.
+template <int D, int GMAX, int SK>
 __global__ __launch_bounds__(NT) void attn_merge_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ kv_lens, int64_t B,
     int64_t n_tokens, int Hq, int n_chunks, int max_kv_len,
     const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, bf16_t* __restrict__ out) {
-    constexpr int NO = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+    constexpr int VPL = MERGE_VPL, LPR = D / VPL, RPW = 64 / LPR;
+    static_assert(D % VPL == 0 && 64 % LPR == 0, "");
+    typedef float Vec __attribute__((ext_vector_type(VPL)));
+    typedef uint32_t Packed __attribute__((ext_vector_type(VPL / 2)));
+    using Node = MergeNode<VPL>;
+    const int lane = threadIdx.x & 63, sub = lane % LPR;
+    const int64_t row = ((int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6)) * RPW + lane / LPR;
     if (row >= n_tokens * Hq) return;
     const int64_t token = row / Hq;
 
@@ -505,10 +532,9 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
         if (kv_len > max_kv_len) kv_len = max_kv_len;
         pos = kv_len - 1;
     }
-    bf16_t* orow = out + row * D;
+    bf16_t* orow = out + row * D + VPL * sub;
     if (pos < 0) {
-#pragma unroll
-        for (int i = 0; i < NO; ++i) orow[lane + 64 * i] = 0;
+        *reinterpret_cast<Packed*>(orow) = Packed(0u);
         return;
     }
     // the row's pos / CHUNK + 1 chunks arrive as nodes of the level the chunk
@@ -520,10 +546,10 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
 
     // node c of the row: slot (token * n_chunks + c) * Hq + head
     const int64_t slot0 = token * (int64_t)n_chunks * Hq + (row - token * Hq);
-    const float* po = ws_o + slot0 * D;
+    const float* po = ws_o + slot0 * D + VPL * sub;
     const float2* pml = ws_ml + slot0;
 
-    Partial slot[STACK];
+    Node slot[SK];
     unsigned count = 0;
     // nodes are loaded GRP at a time into two buffers used in turn: while one
     // group is pushed into the binary counter, in node order, the next group's
@@ -531,29 +557,30 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
     // for data that is not yet needed).  Loads past the row's last node read
     // that last node again and are not pushed.
     constexpr int GRP = 4;
-    Partial ba[GRP], bb[GRP];
-    auto load_group = [&](Partial (&dst)[GRP], int c0) {
+    Node ba[GRP], bb[GRP];
+    auto load_group = [&](Node (&dst)[GRP], int c0) {
 #pragma unroll
         for (int k = 0; k < GRP; ++k) {
             const int c = min(c0 + k, n - 1);
             const float2 ml = pml[(int64_t)c * Hq];
             dst[k].m = ml.x; dst[k].l = ml.y;
+            const Vec v = *reinterpret_cast<const Vec*>(po + (int64_t)c * Hq * D);
 #pragma unroll
-            for (int i = 0; i < NO; ++i) dst[k].o[i] = po[(int64_t)c * Hq * D + lane + 64 * i];
+            for (int i = 0; i < VPL; ++i) dst[k].o[i] = v[i];
         }
     };
-    auto push_group = [&](const Partial (&src)[GRP], int c0) {
+    auto push_group = [&](const Node (&src)[GRP], int c0) {
 #pragma unroll
         for (int k = 0; k < GRP; ++k) {
             if (c0 + k >= n) break;
-            Partial carry = src[k];
+            Node carry = src[k];
             // binary increment: equal-size subtrees merge, the older one on the left
             bool live = true;
 #pragma unroll
-            for (int s = 0; s < STACK; ++s) {
+            for (int s = 0; s < SK; ++s) {
                 if (live) {
                     if (count & (1u << s)) {
-                        carry = combine<NO>(slot[s], carry);
+                        carry = combine_node<VPL>(slot[s], carry);
                     } else {
                         slot[s] = carry;
                         live = false;
@@ -572,20 +599,20 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
         push_group(bb, c0 + GRP);
     }
     // remaining subtrees, smallest (rightmost) first: root = s_hi (+) (... (+) s_lo)
-    Partial res;
+    Node res;
     bool have = false;
 #pragma unroll
-    for (int k = 0; k < STACK; ++k) {
+    for (int k = 0; k < SK; ++k) {
         if (count & (1u << k)) {
             if (!have) { res = slot[k]; have = true; }
-            else res = combine<NO>(slot[k], res);
+            else res = combine_node<VPL>(slot[k], res);
         }
     }
+    Packed w;
 #pragma unroll
-    for (int i = 0; i < NO; ++i) {
-        const float v = res.o[i] / res.l + 0.0f;       // + 0.0f turns -0 into +0
-        orow[lane + 64 * i] = (bf16_t)f32_to_bf16(v);
-    }
+    for (int i = 0; i < VPL / 2; ++i)        // + 0.0f turns -0 into +0
+        w[i] = pack_bf16x2(res.o[2 * i] / res.l + 0.0f, res.o[2 * i + 1] / res.l + 0.0f);
+    *reinterpret_cast<Packed*>(orow) = w;
 }
 
 #ifndef BINV_DECODE_GMAX
@@ -615,10 +642,22 @@ hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
     const int64_t Rows = a.n_tokens * a.Hq;
     const float* ws_o = a.ws;
     const float2* ws_ml = reinterpret_cast<const float2*>(a.ws + Rows * n_chunks * a.D);
-    dim3 grid2((unsigned)((Rows + 3) / 4));
-    hipLaunchKernelGGL((attn_merge_kernel<D, GMAX>), grid2, dim3(NT), 0, s, a.cu_q, a.kv_lens, a.B,
-                       a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len, ws_o, ws_ml,
-                       (bf16_t*)a.out);
+    constexpr int RPB = (NT / 64) * (64 * MERGE_VPL / D);      // rows per workgroup
+    dim3 grid2((unsigned)((Rows + RPB - 1) / RPB));
+    // binary-counter depth for the most nodes a row can have (a row's nodes
+    // never outnumber its leaves; unused slots would never be touched)
+    if (n_chunks <= 31)
+        hipLaunchKernelGGL((attn_merge_kernel<D, GMAX, 5>), grid2, dim3(NT), 0, s, a.cu_q,
+                           a.kv_lens, a.B, a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len, ws_o,
+                           ws_ml, (bf16_t*)a.out);
+    else if (n_chunks <= 255)
+        hipLaunchKernelGGL((attn_merge_kernel<D, GMAX, 8>), grid2, dim3(NT), 0, s, a.cu_q,
+                           a.kv_lens, a.B, a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len, ws_o,
+                           ws_ml, (bf16_t*)a.out);
+    else
+        hipLaunchKernelGGL((attn_merge_kernel<D, GMAX, STACK>), grid2, dim3(NT), 0, s, a.cu_q,
+                           a.kv_lens, a.B, a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len, ws_o,
+                           ws_ml, (bf16_t*)a.out);
     return hipGetLastError();
 }
 

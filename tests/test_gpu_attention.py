@@ -187,12 +187,14 @@ def test_prefill_chunked_and_decode_bitwise_equal():
     assert row_rel_err(f64(one_shot[rows]), ref).max() <= TOL_BF16
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (4, 4, 64)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (4, 4, 64), (3, 3, 128), (5, 5, 64)])
 def test_decode_tree_levels_equal_prefill_leaves(Hq, Hkv, D):
     # Decode hands a row's partials to the merge kernel as nodes of one, two or
     # four chunks depending on its chunk count; prefill always hands over
     # leaves.  Every decode position must equal the one-shot prefill of the
-    # same position bit for bit.
+    # same position bit for bit.  The merge puts 2 (D = 128) or 4 (D = 64)
+    # (token, head) rows in one wave: with an odd head count those rows belong
+    # to different tokens with different node counts.
     L = 34 * 256 - 100
     scale = 1 / math.sqrt(D)
     k, v = synth.random_kv(L, Hkv, D, 91, DEV)
