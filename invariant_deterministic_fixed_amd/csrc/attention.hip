@@ -368,17 +368,29 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
             sc[kt] = mfma16x16x32(qf[ks], kf, sc[kt]);
         }
     }
-    // scale, mask (key <= the row's position), row max over the 256 keys
+    // scale, mask (key <= the row's position), row max over the 256 keys.
+    // Below the diagonal every key of the chunk is valid for every row of the
+    // wave and the mask is skipped (a wave-uniform branch, same values).
     float mx[4];
+    const bool all_seen = __all(j0 + CHUNK - 1 <= min(min(rpos[0], rpos[1]), min(rpos[2], rpos[3])));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         mx[e] = -INFINITY;
+        if (all_seen) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
-            const bool valid = j0 + 16 * kt + ar <= rpos[e];
-            const float v = valid ? sc[kt][e] * scale_log2 : -INFINITY;
-            sc[kt][e] = v;
-            mx[e] = fmaxf(mx[e], v);
+            for (int kt = 0; kt < NKT; ++kt) {
+                const float v = sc[kt][e] * scale_log2;
+                sc[kt][e] = v;
+                mx[e] = fmaxf(mx[e], v);
+            }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                const bool valid = j0 + 16 * kt + ar <= rpos[e];
+                const float v = valid ? sc[kt][e] * scale_log2 : -INFINITY;
+                sc[kt][e] = v;
+                mx[e] = fmaxf(mx[e], v);
+            }
         }
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], off));
@@ -436,24 +448,32 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
         pa[ks] = *reinterpret_cast<const u32x4*>(pt + p_off(ar, 4 * ks + ag));
+    // V slots at or past kv_len exist only in the sequence's last chunk; in
+    // every other chunk the zeroing is skipped (block-uniform branch)
     f32x4 o[D / 16];
+    auto pv = [&](auto masked) {
 #pragma unroll
-    for (int f = 0; f < D / 16; ++f) {
-        o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int d = 16 * f + ar;
+        for (int f = 0; f < D / 16; ++f) {
+            o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int d = 16 * f + ar;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int pl = 2 * ks + (ag >> 1), h = ag & 1;
-            u32x4 v = *reinterpret_cast<const u32x4*>(vbuf + pl * (D * PAGE * 2) + d * (PAGE * 2) +
-                                                      ((h ^ ((d >> 3) & 1)) << 4));
-            const int nvalid = kv_len - ((16 * c + pl) * PAGE + 8 * h);
+            for (int ks = 0; ks < 8; ++ks) {
+                const int pl = 2 * ks + (ag >> 1), h = ag & 1;
+                u32x4 v = *reinterpret_cast<const u32x4*>(vbuf + pl * (D * PAGE * 2) + d * (PAGE * 2) +
+                                                          ((h ^ ((d >> 3) & 1)) << 4));
+                if constexpr (decltype(masked)::value) {
+                    const int nvalid = kv_len - ((16 * c + pl) * PAGE + 8 * h);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (2 * i + 1 >= nvalid) v[i] &= (2 * i < nvalid) ? 0x0000ffffu : 0u;
+                    for (int i = 0; i < 4; ++i) {
+                        if (2 * i + 1 >= nvalid) v[i] &= (2 * i < nvalid) ? 0x0000ffffu : 0u;
+                    }
+                }
+                o[f] = mfma16x16x32(pa[ks], v, o[f]);
             }
-            o[f] = mfma16x16x32(pa[ks], v, o[f]);
         }
-    }
+    };
+    if (j0 + CHUNK > kv_len) pv(std::true_type{});
+    else pv(std::false_type{});
 
     // ---- partials of the rows that see at least one key of this chunk:
     // slot (token * n_chunks + c) * Hq + head
