@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import invariant_deterministic_fixed_amd as binv
+import invariant_deterministic_fixed_amd.binding as bd
 import oracle
 from invariant_deterministic_fixed_amd import synth
 from helpers import TOL_BF16, assert_bitwise_equal, f64, row_rel_err
@@ -239,6 +240,36 @@ def test_decode_long_rows_every_node_level_equal_leaves():
         p = int(rows[i])
         ref = oracle.attention(f64(qr[i:i + 1]), [p], f64(k), f64(v), scale)
         assert row_rel_err(f64(dec[i:i + 1]), ref).max() <= TOL_BF16, p
+
+
+def test_longest_rows_and_max_kv_len_bound_change_no_bits():
+    # max_kv_len only sizes the grid and the workspace: rows of up to 70000
+    # keys (274 chunks, so the merge's binary counter uses nine slots) give
+    # the same bits under three bounds -- the longest row, 300 chunks and the
+    # library's maximum -- through decode (nodes of up to four chunks) and
+    # through one-token prefill (leaves); two rows against the oracle.
+    Hq, Hkv, D = 32, 8, 128
+    L = 70000
+    scale = 1 / math.sqrt(D)
+    k, v = synth.random_kv(L, Hkv, D, 131, DEV)
+    cache, _ = make_cache([L], Hkv, D, 132, seqs=[(k, v)])
+    rows = np.array([0, 255, 256, 40000, 65279, 65280, 65535, L - 1], dtype=np.int64)
+    n = len(rows)
+    qr = synth.normal((n, Hq, D), 1.0, 133, DEV)
+    pt = cache.page_table[:1].expand(n, -1).contiguous()
+    kv_lens = torch.as_tensor(rows + 1, dtype=torch.int32, device=DEV)
+    cu = torch.arange(n + 1, dtype=torch.int32, device=DEV)
+    outs = []
+    for bound in (L, 300 * 256, bd.MAX_KV_LEN):
+        outs.append(binv.attn_decode(qr, cache.k_cache, cache.v_cache, pt, kv_lens, bound, scale))
+        outs.append(binv.attn_prefill(qr, cu, cache.k_cache, cache.v_cache, pt, kv_lens, 1,
+                                      bound, scale))
+    for i, o in enumerate(outs[1:], 1):
+        assert_bitwise_equal(o, outs[0], f"output {i} vs decode under the tightest bound")
+    for i in (3, n - 1):
+        p = int(rows[i])
+        ref = oracle.attention(f64(qr[i:i + 1]), [p], f64(k), f64(v), scale)
+        assert row_rel_err(f64(outs[0][i:i + 1]), ref).max() <= TOL_BF16, p
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (32, 2)])
