@@ -373,7 +373,7 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
                 const float p = (v == -INFINITY) ? 0.0f : exp2f(v - r.m[rt][e]);
                 const int row = 16 * rt + 4 * ag + e;
                 *reinterpret_cast<bf16_t*>(sh.p + p_off(row, key >> 3) + 2 * (key & 7)) =
-                    (bf16_t)f32_to_bf16(p);
+                    (bf16_t)f32_to_bf16_branch(p);
             }
         }
     if constexpr (VL) {                                // this wave's V copies landed

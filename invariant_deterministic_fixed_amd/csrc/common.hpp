@@ -16,7 +16,21 @@ constexpr int WAVE = 64;
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // fp32 -> bf16 bits, round to nearest, ties to even.  NaN stays a quiet NaN.
+// Both results are formed and one is selected: written as an early return,
+// the NaN test became a branch with exec-mask save / restore around every
+// converted value.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t qnan = ((u >> 16) | 0x40u) & 0xffffu;
+    const uint32_t nan_mask = 0u - (uint32_t)((u & 0x7fffffffu) > 0x7f800000u);
+    return (qnan & nan_mask) | (rne & ~nan_mask);
+}
+
+// The same function with the NaN case as a branch: one register fewer per
+// value in flight, for a kernel at the edge of its register budget (the
+// select form made the decode chunk kernel spill at 128 VGPRs).
+__device__ __forceinline__ uint32_t f32_to_bf16_branch(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
     u += 0x7fffu + ((u >> 16) & 1u);
