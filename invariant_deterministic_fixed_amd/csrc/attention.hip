@@ -409,7 +409,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float v = sc[kt][e];
-            const float p = (v == -INFINITY) ? 0.0f : exp2f(v - mx[e]);
+            const float p = (v == -INFINITY) ? 0.0f : exp2_score(v - mx[e]);
             *reinterpret_cast<bf16_t*>(pt + p_off(4 * ag + e, key >> 3) + 2 * (key & 7)) =
                 (bf16_t)f32_to_bf16(p);
         }

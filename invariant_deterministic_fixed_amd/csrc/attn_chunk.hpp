@@ -22,6 +22,15 @@ constexpr int NT = 256;
 constexpr int ROWS = 16;           // rows of one MFMA row tile
 constexpr int STACK = 10;          // binary counter slots: enough for 1023 leaves
 
+// p = 2^(s - m) of a score, s <= m: the hardware v_exp_f32 as it stands.
+// exp2f adds a range reduction that keeps results below 2^-126 (weights more
+// than 126 binary orders under the row's largest) as fp32 denormals, five
+// more vector instructions per score; every kernel that forms p (decode, the
+// prefill block and chunk paths, the tuned comparator) calls this one
+// function, so they agree bit for bit.
+__device__ __forceinline__ float exp2_score(float x) { return __builtin_amdgcn_exp2f(x); }
+
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // Workgroup barrier for LDS data only: this wave's LDS accesses done, then
@@ -370,7 +379,7 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float v = s[rt][u][e];
-                const float p = (v == -INFINITY) ? 0.0f : exp2f(v - r.m[rt][e]);
+                const float p = (v == -INFINITY) ? 0.0f : exp2_score(v - r.m[rt][e]);
                 const int row = 16 * rt + 4 * ag + e;
                 *reinterpret_cast<bf16_t*>(sh.p + p_off(row, key >> 3) + 2 * (key & 7)) =
                     (bf16_t)f32_to_bf16_branch(p);
