@@ -32,6 +32,30 @@ def test_split_kernel_matches_oracle_split_bitwise():
     np.testing.assert_array_equal(got[:, :K] + got[:, K:2 * K] + got[:, 2 * K:], x.double().cpu().numpy())
 
 
+def test_split_rounding_edge_cases_bitwise():
+    # The kernels' fp32 -> bf16 rounding, through the split's three parts:
+    # ties to even around 1 and in the denormal range, the largest denormal
+    # rounding up to 2^-126, the smallest denormal, the largest finite value
+    # that still rounds to a finite bf16, signed zeros -- against the oracle's
+    # nearest-even rounding (which spaces values 2^-133 apart below 2^-126).
+    bits = [0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001, 0xBF808000, 0xBF818000,
+            0x00008000, 0x00018000, 0x00007FFF, 0x00008001, 0x80018000, 0x00000001,
+            0x007FFFFF, 0x00800000, 0x00FF8000, 0x7F7F7FFF, 0xFF7F7FFF, 0x00000000,
+            0x80000000, 0x3EAAAAAB, 0x4B7FFFFF, 0x33800001]
+    n = 64
+    raw = np.array((bits * ((n + len(bits) - 1) // len(bits)))[:n], dtype=np.uint32)
+    x = torch.from_numpy(raw.view(np.int32).reshape(1, n).copy()).view(torch.float32).to(DEV)
+    out = binv.split_bf16x3(x)
+    hi, mid, lo = oracle.split_bf16x3(x.double().cpu().numpy())
+    got = out.float().double().cpu().numpy()
+    np.testing.assert_array_equal(got[:, :n], hi)
+    np.testing.assert_array_equal(got[:, n:2 * n], mid)
+    np.testing.assert_array_equal(got[:, 2 * n:], lo)
+    # signed zeros keep their sign in the high part
+    sign = np.signbit(out.float().cpu().numpy()[:, :n])
+    np.testing.assert_array_equal(sign, np.signbit(raw.view(np.float32).reshape(1, n)))
+
+
 def _oracle_chain(x, weights, eps):
     h = f64(x)
     ones = np.ones(h.shape[1])
