@@ -368,52 +368,55 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
             sc[kt] = mfma16x16x32(qf[ks], kf, sc[kt]);
         }
     }
-    // scale, mask (key <= the row's position), row max over the 256 keys.
-    // Below the diagonal every key of the chunk is valid for every row of the
-    // wave and the mask is skipped (a wave-uniform branch, same values).
+    // scale, mask (key <= the row's position), row max over the 256 keys, then
+    // p = bf16(2^(s - m)) into this tile's 8 KB of the K area.  Below the
+    // diagonal every key of the chunk is valid for every row of the wave and
+    // the mask is left out; the two versions are separate wave-uniform paths
+    // (same values), each with the one barrier that frees the K area.
+    // p = 0 for a masked key comes from 2^(-inf - m): a row whose keys are all
+    // masked (m = -inf) takes m = 0 there, which gives p = 0 as well -- the
+    // per-score test v == -inf of the chunk kernel, per row instead.
     float mx[4];
-    const bool all_seen = __all(j0 + CHUNK - 1 <= min(min(rpos[0], rpos[1]), min(rpos[2], rpos[3])));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        mx[e] = -INFINITY;
-        if (all_seen) {
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                const float v = sc[kt][e] * scale_log2;
-                sc[kt][e] = v;
-                mx[e] = fmaxf(mx[e], v);
-            }
-        } else {
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                const bool valid = j0 + 16 * kt + ar <= rpos[e];
-                const float v = valid ? sc[kt][e] * scale_log2 : -INFINITY;
-                sc[kt][e] = v;
-                mx[e] = fmaxf(mx[e], v);
-            }
-        }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], off));
-    }
-    if (ar == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mrow[4 * ag + e] = mx[e];
-    }
-    lds_barrier();                                    // every tile done with K: its area takes p
-
-    // ---- p = bf16(exp2(s - m)) into this tile's 8 KB of the K area
     char* pt = kbuf + wave * (16 * CHUNK * 2);
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-        const int key = 16 * kt + ar;
+    auto softmax = [&](auto masked) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float v = sc[kt][e];
-            const float p = (v == -INFINITY) ? 0.0f : exp2_score(v - mx[e]);
-            *reinterpret_cast<bf16_t*>(pt + p_off(4 * ag + e, key >> 3) + 2 * (key & 7)) =
-                (bf16_t)f32_to_bf16(p);
+            mx[e] = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                float v = sc[kt][e] * scale_log2;
+                if constexpr (decltype(masked)::value) {
+                    if (j0 + 16 * kt + ar > rpos[e]) v = -INFINITY;
+                }
+                sc[kt][e] = v;
+                mx[e] = fmaxf(mx[e], v);
+            }
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], off));
         }
-    }
+        if (ar == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mrow[4 * ag + e] = mx[e];
+        }
+        lds_barrier();                                // every tile done with K: its area takes p
+        float mu[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mu[e] = (mx[e] == -INFINITY) ? 0.0f : mx[e];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+            const int key = 16 * kt + ar;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p = exp2_score(sc[kt][e] - mu[e]);
+                *reinterpret_cast<bf16_t*>(pt + p_off(4 * ag + e, key >> 3) + 2 * (key & 7)) =
+                    (bf16_t)f32_to_bf16(p);
+            }
+        }
+    };
+    if (__all(j0 + CHUNK - 1 <= min(min(rpos[0], rpos[1]), min(rpos[2], rpos[3]))))
+        softmax(std::false_type{});
+    else
+        softmax(std::true_type{});
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile's p, read below by its own wave
 
     // ---- l of row ar: segments 4(lane>>4) .. +3 summed key by key, then the
