@@ -402,13 +402,22 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
         float mu[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) mu[e] = (mx[e] == -INFINITY) ? 0.0f : mx[e];
+        // p_off(row, key >> 3) + 2 (key & 7) with row = 4 ag + e, key = 16 kt + ar:
+        // (key >> 3) ^ row = 2 kt ^ ((ar >> 3) ^ row), so the byte offset is a
+        // per-row base plus (32 kt) ^ z -- one xor-add per store
+        int base[4], z[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 4 * ag + e;
+            base[e] = (row << 9) + 2 * (ar & 7);
+            z[e] = ((ar >> 3) ^ (row & 31)) << 4;
+        }
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
-            const int key = 16 * kt + ar;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float p = exp2_score(sc[kt][e] - mu[e]);
-                *reinterpret_cast<bf16_t*>(pt + p_off(4 * ag + e, key >> 3) + 2 * (key & 7)) =
+                *reinterpret_cast<bf16_t*>(pt + (((32 * kt) ^ z[e]) + base[e])) =
                     (bf16_t)f32_to_bf16(p);
             }
         }
