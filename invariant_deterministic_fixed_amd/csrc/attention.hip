@@ -391,8 +391,18 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
                 sc[kt][e] = v;
                 mx[e] = fmaxf(mx[e], v);
             }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], off));
+            // max over the 16 lanes of the row group: rotations by 1, 2, 4, 8
+            // within each 16-lane DPP row (max is exact, so the order of the
+            // exchange does not matter; one VALU op each instead of an LDS
+            // permute round trip)
+            mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
+                                     0, __float_as_int(mx[e]), 0x121, 0xf, 0xf, false)));
+            mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
+                                     0, __float_as_int(mx[e]), 0x122, 0xf, 0xf, false)));
+            mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
+                                     0, __float_as_int(mx[e]), 0x124, 0xf, 0xf, false)));
+            mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
+                                     0, __float_as_int(mx[e]), 0x128, 0xf, 0xf, false)));
         }
         if (ar == 0) {
 #pragma unroll
