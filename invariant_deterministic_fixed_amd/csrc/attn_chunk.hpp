@@ -350,8 +350,18 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
                 s[rt][u][e] = v;
                 mx[e] = fmaxf(mx[e], v);
             }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], off));
+            {
+                // max over the 16 lanes of the row group by DPP row rotations
+                // (max is exact, so the exchange order does not reach the bits)
+                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
+                                         0, __float_as_int(mx[e]), 0x121, 0xf, 0xf, false)));
+                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
+                                         0, __float_as_int(mx[e]), 0x122, 0xf, 0xf, false)));
+                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
+                                         0, __float_as_int(mx[e]), 0x124, 0xf, 0xf, false)));
+                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
+                                         0, __float_as_int(mx[e]), 0x128, 0xf, 0xf, false)));
+            }
         }
         if ((lane & 15) == 0) {
 #pragma unroll
