@@ -34,6 +34,10 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--ramp-seconds S] [-
                                   per case)
        [--profile-copy]   (adds one 1 GiB device copy, the calibration kernel
                            for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+       python bench.py --gemm M,N,K [--gemm ...] [--reps R]
+                          (the invariant GEMM alone on the given shapes, cold
+                           operands, one JSON line per shape: for per-shape
+                           kernel traces and counters)
 """
 import argparse
 import hashlib
@@ -486,6 +490,35 @@ def sweep(dev="cuda:0"):
                  ms_B1=round(ms[1], 4), ms_B64=round(ms[64], 4), ms_B1024=round(ms[1024], 4))
 
 
+def gemm_shapes(shapes, reps, dev="cuda:0"):
+    """The invariant GEMM alone, per shape (M, N, K): weights rotated over
+    enough copies to exceed the last-level cache, R timed launches."""
+    import torch
+    import invariant_deterministic_fixed_amd as binv
+    from invariant_deterministic_fixed_amd import synth
+
+    a = torch.randn((8192, 4096), device=dev).to(torch.bfloat16)
+    b = torch.randn((4096, 4096), device=dev).to(torch.bfloat16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:                  # clock ramp
+        binv.gemm(a, b)
+        torch.cuda.synchronize()
+    del a, b
+    for (M, N, K) in shapes:
+        Ws = [synth.normal((K, N), 0.02, 7 + i, dev) for i in range(_copies(2 * N * K))]
+        A = synth.normal((M, K), 1.0, 3, dev)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        t = _cold_ms([lambda W=W: binv.gemm(A, W, out=C) for W in Ws], reps=reps)
+        flops = 2.0 * M * N * K
+        nbytes = 2 * (M * K + K * N + M * N)
+        roof_ms = max(flops / PEAK_BF16_TFLOPS / 1e9, nbytes / PEAK_HBM_GBPS / 1e6)
+        print(json.dumps({"gemm": [M, N, K], "us": round(t * 1e3, 2),
+                          "TFLOPs": round(flops / t / 1e9, 2), "GBps": round(nbytes / t / 1e6, 1),
+                          "roofline_frac": round(roof_ms / t, 4)}), flush=True)
+        del Ws, A, C
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -496,6 +529,9 @@ def main():
     ap.add_argument("--profile-copy", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="per-shape figures (one JSON line per case) instead of the bench line")
+    ap.add_argument("--gemm", action="append", default=[],
+                    help="M,N,K: time the invariant GEMM alone on this shape (repeatable)")
+    ap.add_argument("--reps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -508,6 +544,9 @@ def main():
     torch.cuda.set_device(0)
     if args.sweep:
         sweep(dev)
+        return
+    if args.gemm:
+        gemm_shapes([tuple(int(v) for v in g.split(",")) for g in args.gemm], args.reps, dev)
         return
     w = build_workload(dev)
     work = algorithmic(w)

@@ -50,5 +50,34 @@ def build_library(verbose=False):
     return LIB
 
 
+# test-only HIP code (kernels that check a device function of the library on
+# every input); built beside the tests, never linked into libbinv
+TEST_SUPPORT = os.path.join(ROOT, "tests", "gpu_support")
+TEST_LIBS = {"libconvcheck.so": ["conv_check.hip"]}
+
+
+def build_test_support(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    out = []
+    for lib, srcs in TEST_LIBS.items():
+        objs = []
+        for src in srcs:
+            obj = os.path.join(BUILD, "test_" + src + ".o")
+            cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(TEST_SUPPORT, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}{r.stderr}")
+            objs.append(obj)
+        path = os.path.join(TEST_SUPPORT, lib)
+        subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", path + ".tmp"]
+                       + objs, check=True)
+        os.replace(path + ".tmp", path)
+        out.append(path)
+    return out
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_test_support(verbose=True))

@@ -154,11 +154,17 @@ class Decoder:
         self.logits = torch.empty((max_seqs, cfg["vocab"]), dtype=torch.float32, device=dev)
         self.max_tokens, self.max_seqs = T, max_seqs
 
-    def step(self, items, protected=None):
+    def step(self, items, protected=None, on_layer=None):
         """items: list of (slot, new token ids, start position).  Returns
         (logits fp32 [n, V], top ids int32 [n, k], top values fp32 [n, k]) for
         the last token of each item, as device tensors, in item order.
-        protected: a set of slots to run locked (see the class note)."""
+        protected: a set of slots to run locked (see the class note).
+        on_layer(i, h): called with the residual stream h [T, H] (fp32, device,
+        the step's tokens in item order) before layer i and, with i = the
+        layer count, after the last layer -- for tests that check one layer at
+        a time.  After the call, self.hl / self.xl hold the last tokens'
+        residual rows and their final-norm output (bf16), rows in item order
+        unless `protected` reordered them."""
         cfg, pool, dev = self.cfg, self.pool, self.pool.device
         order = None
         if protected is not None:
@@ -221,6 +227,8 @@ class Decoder:
 
         B.embed(ids_d, self.w["embed"], out=h)
         for li, lw in enumerate(self.w["layers"]):
+            if on_layer is not None:
+                on_layer(li, h)
             norm(h, x, rows_tok)
             mm(x, lw["wqkv"], qkv, rows_tok)
             B.rope_kv_write(qkv, tseq_d, tpos_d, Hq, Hkv, D, cfg["theta"], pool.k[li], pool.v[li],
@@ -238,6 +246,8 @@ class Decoder:
             B.swiglu(gu, out=s)
             mm(s, lw["wd"], o, rows_tok)
             B.residual_add(h, o)
+        if on_layer is not None:
+            on_layer(len(self.w["layers"]), h)
         hl, xl, logits = self.hl[:nb], self.xl[:nb], self.logits[:nb]
         rows_seq = split(n_prot if locked else 0)
         B.gather_rows(h, last_d, out=hl)

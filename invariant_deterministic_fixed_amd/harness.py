@@ -27,14 +27,16 @@ class Seq:
 
 
 def run(decoder, pool, target_prompt, n_new, neighbours=(), budget=None, seed=0,
-        record_logits=False, lock_target=False):
+        record_logits=False, lock_target=False, record_neighbours=False):
     """Greedy-decode `n_new` tokens of the target (slot order and batch order
     randomised by `seed`).  neighbours: list of prompts, each decoded greedily
     alongside.  budget: max prompt tokens per step (None: whole prompts at once).
     lock_target: run the target locked and everyone else on the tuned
     comparators (Decoder.step's selective locking).
     Returns a dict with the target's tokens, top-20 ids / values per token
-    (host tensors) and, if asked, the full logits rows."""
+    (host tensors) and, if asked, the full logits rows; with record_neighbours
+    also "neighbours": per neighbour (in the order given) its generated tokens
+    and the logits row that chose each."""
     rng = np.random.default_rng(int(seed))
     # slots are taken in a shuffled order so the target's page-table row moves too
     seqs = []
@@ -48,6 +50,7 @@ def run(decoder, pool, target_prompt, n_new, neighbours=(), budget=None, seed=0,
         seqs.append(Seq(slots[i], p, n_new if i == 0 else 10 ** 9))
     target = seqs[0]
     out = {"tokens": [], "top_ids": [], "top_vals": [], "logits": []}
+    nb_rec = {id(s): {"tokens": [], "logits": []} for s in seqs[1:]}
     while not target.finished():
         items, owners = [], []
         left = budget if budget is not None else float("inf")
@@ -75,6 +78,9 @@ def run(decoder, pool, target_prompt, n_new, neighbours=(), budget=None, seed=0,
                 if s.done_prefill < len(s.prompt):
                     continue                      # mid-prompt chunk: nothing generated yet
             s.generated.append(int(ids_h[k, 0]))
+            if record_neighbours and s is not target:
+                nb_rec[id(s)]["tokens"].append(int(ids_h[k, 0]))
+                nb_rec[id(s)]["logits"].append(logits[k].cpu().clone())
             if s is target:
                 out["tokens"].append(int(ids_h[k, 0]))
                 out["top_ids"].append(ids_h[k].clone())
@@ -87,6 +93,8 @@ def run(decoder, pool, target_prompt, n_new, neighbours=(), budget=None, seed=0,
     out["top_vals"] = torch.stack(out["top_vals"])
     if record_logits:
         out["logits"] = torch.stack(out["logits"])
+    if record_neighbours:
+        out["neighbours"] = [nb_rec[id(s)] for s in seqs[1:]]
     return out
 
 

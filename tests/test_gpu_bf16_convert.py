@@ -1,0 +1,43 @@
+"""The two fp32 -> bf16 conversions the kernels use agree on every input.
+
+The decode chunk kernel rounds p with the integer formulation
+(f32_to_bf16_branch) and the prefill block kernel, GEMM and RMSNorm with
+gfx950's conversion instruction (f32_to_bf16); a prefill row equals the
+decode of the same position bit for bit only if the two give the same bits
+for every fp32 value (tom-jerr.github.io "Batch-Invariant Kernel", Flash
+Attention: prefill and decode intermediates bit-identical).  A test-only
+kernel (tests/gpu_support/conv_check.hip, built by the package build) runs
+both, and the round-to-nearest-even rule written out from the format's
+definition, over all 2^32 bit patterns, NaNs included."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "gpu_support", "libconvcheck.so")
+
+
+def test_bf16_conversions_agree_on_all_2_32_inputs():
+    assert os.path.exists(LIB), "tests/gpu_support/libconvcheck.so missing: run the package build"
+    lib = ctypes.CDLL(LIB)
+    lib.conv_check_all_inputs.restype = ctypes.c_int
+    lib.conv_check_all_inputs.argtypes = [ctypes.c_void_p] * 3
+    counts = torch.full((3 * 65536,), 0xFFFF, dtype=torch.int32, device="cuda:0")
+    first = torch.zeros(65536, dtype=torch.int32, device="cuda:0")
+    st = lib.conv_check_all_inputs(ctypes.c_void_p(counts.data_ptr()),
+                                   ctypes.c_void_p(first.data_ptr()),
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy().astype(np.int64).reshape(-1, 3)
+    hw_vs_branch, hw_vs_rule, branch_vs_rule = (int(x) for x in c.sum(axis=0))
+    f = first.cpu().numpy().view(np.uint32)
+    bad = f[f != 0xFFFFFFFF]
+    print(f"mismatches over 2^32 inputs: hw vs branch {hw_vs_branch}, hw vs rule {hw_vs_rule}, "
+          f"branch vs rule {branch_vs_rule}", flush=True)
+    assert (hw_vs_branch, hw_vs_rule, branch_vs_rule) == (0, 0, 0), \
+        f"first differing inputs: {[hex(int(x)) for x in bad[:8]]}"
