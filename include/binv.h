@@ -29,8 +29,9 @@
  *   - Preconditions that live in device memory (kv_lens, cu_q, page-table
  *     entries) cannot be checked without a synchronisation; they are the
  *     caller's contract and are stated per entry point.
- *   - The library keeps no mutable global state; calls from several host
- *     threads are safe.
+ *   - The library keeps no mutable global state (one exception: the entry
+ *     point that allocates nothing caches the address of its fixed device
+ *     array per GPU, under a lock); calls from several host threads are safe.
  */
 #ifndef BINV_H
 #define BINV_H
@@ -47,7 +48,9 @@ typedef enum {
     BINV_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad leading dimension, misalignment */
     BINV_ERR_UNSUPPORTED = 2,   /* a size or shape outside what the kernels implement */
     BINV_ERR_WORKSPACE = 3,     /* workspace missing or smaller than binv_attn_workspace_bytes() */
-    BINV_ERR_LAUNCH = 4         /* the HIP runtime rejected a launch */
+    BINV_ERR_LAUNCH = 4,        /* the HIP runtime rejected a launch */
+    BINV_ERR_SCRATCH = 5        /* the call needs more than the fixed scratch of the
+                                   entry point that allocates nothing */
 } binv_status;
 
 typedef enum { BINV_F32 = 0, BINV_BF16 = 1 } binv_dtype;
@@ -186,6 +189,37 @@ int binv_attn_prefill_paged(const void* q, const int32_t* cu_q,
                             int64_t B, int64_t T, int64_t max_q_len, int64_t max_kv_len,
                             int Hq, int Hkv, int D, int page_size, float scale,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, contract and results (bit for bit)
+ * as binv_attn_decode_paged, whose kernels it runs; the fp32 partials go to a
+ * fixed device array inside the library instead of a caller workspace.
+ *
+ *   - The array holds BINV_NOALLOC_SCRATCH_BYTES (128 MiB) on every GPU the
+ *     library's kernels are loaded on, until the process ends.  A call needing
+ *     more than that -- binv_attn_workspace_bytes(B, Hq, D, max_kv_len) above
+ *     the limit, e.g. B * ceil(max_kv_len / 256) > 8065 at Hq = 32, D = 128 --
+ *     returns BINV_ERR_SCRATCH and enqueues nothing.
+ *   - The call makes no hipMalloc / hipFree and no allocating library call.
+ *     Its first call on a device looks up that device's copy of the array
+ *     (hipGetSymbolAddress) and keeps the address; the stream must belong to
+ *     the current device.
+ *   - Every call on one GPU shares that GPU's array.  Nothing in it needs to
+ *     start at zero (every partial a call reads, the same call wrote first),
+ *     but two calls that overlap in time on one GPU (different streams, or
+ *     host threads without ordering) race on it: order them.
+ * ------------------------------------------------------------------------ */
+#define BINV_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+int binv_attn_decode_paged_noalloc(const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* page_table, int64_t pt_stride,
+                                   const int32_t* kv_lens,
+                                   void* out,
+                                   int64_t B, int64_t max_kv_len, int Hq, int Hkv, int D,
+                                   int page_size, float scale, void* stream);
 
 /* ------------------------------------------------------------------------
  * Shape-tuned comparators.  NOT batch-invariant, on purpose: they choose their

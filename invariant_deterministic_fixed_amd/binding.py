@@ -45,6 +45,8 @@ def _declare(lib):
                                         f32, vp, sz, vp]),
         "binv_attn_prefill_paged": (ci, [vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, i64,
                                          ci, ci, ci, ci, f32, vp, sz, vp]),
+        "binv_attn_decode_paged_noalloc": (ci, [vp, vp, vp, vp, i64, vp, vp, i64, i64, ci, ci,
+                                                ci, ci, f32, vp]),
         "binv_attn_decode_tuned_workspace_bytes": (sz, [i64, ci, ci, i64]),
         "binv_attn_decode_paged_tuned": (ci, [vp, vp, vp, vp, i64, vp, vp, i64, i64, ci, ci, ci,
                                               ci, f32, vp, sz, vp]),
@@ -187,6 +189,23 @@ def attn_decode(q, k_cache, v_cache, page_table, kv_lens, max_kv_len, scale, out
             _ptr(kv_lens), _ptr(out), B, int(max_kv_len), Hq, Hkv, D, page, float(scale),
             _ptr(ws), nbytes, _stream(q))
     _check(st, fn.__name__)
+    return out
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, page_table, kv_lens, max_kv_len, scale, out):
+    """binv_attn_decode_paged_noalloc: decode with the library's fixed partials
+    buffer instead of a workspace; `out` [B, Hq, D] bf16 must be given (nothing
+    is allocated on this path)."""
+    _dev(q, k_cache, v_cache, page_table, kv_lens, out)
+    B, Hq, D = q.shape
+    assert q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()
+    assert page_table.dtype == torch.int32 and kv_lens.dtype == torch.int32
+    assert page_table.dim() == 2 and page_table.stride(1) == 1 and out.is_contiguous()
+    st = lib().binv_attn_decode_paged_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), page_table.stride(0),
+        _ptr(kv_lens), _ptr(out), B, int(max_kv_len), Hq, k_cache.shape[1], D,
+        k_cache.shape[2], float(scale), _stream(q))
+    _check(st, "binv_attn_decode_paged_noalloc")
     return out
 
 

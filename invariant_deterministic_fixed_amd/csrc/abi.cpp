@@ -81,6 +81,9 @@ const char* binv_status_str(int status) {
         case BINV_ERR_UNSUPPORTED: return "BINV_ERR_UNSUPPORTED: size or shape not supported";
         case BINV_ERR_WORKSPACE: return "BINV_ERR_WORKSPACE: workspace missing or too small";
         case BINV_ERR_LAUNCH: return "BINV_ERR_LAUNCH: kernel launch failed";
+        case BINV_ERR_SCRATCH:
+            return "BINV_ERR_SCRATCH: the call needs more partials memory than the fixed "
+                   "BINV_NOALLOC_SCRATCH_BYTES of the no-alloc entry point";
         default: return "unknown binv status";
     }
 }
@@ -154,6 +157,27 @@ int binv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cac
     binv::AttnArgs a{q, nullptr, k_cache, v_cache, page_table, pt_stride, kv_lens, out, B, B, 1,
                      max_kv_len, Hq, Hkv, D, (float)((double)scale * 1.4426950408889634),
                      (float*)workspace};
+    return status_of(binv::launch_attention(a, (hipStream_t)stream));
+}
+
+int binv_attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* page_table, int64_t pt_stride,
+                                   const int32_t* kv_lens, void* out, int64_t B,
+                                   int64_t max_kv_len, int Hq, int Hkv, int D, int page_size,
+                                   float scale, void* stream) {
+    if (B < 0) return BINV_ERR_INVALID_ARG;
+    if (B == 0) return BINV_OK;
+    int st = check_attn_common(k_cache, v_cache, page_table, pt_stride, kv_lens, B, max_kv_len,
+                               Hq, Hkv, D, page_size, scale);
+    if (st != BINV_OK) return st;
+    if (!q || !out || !aligned16(q) || !aligned16(out)) return BINV_ERR_INVALID_ARG;
+    if (binv::attn_workspace_bytes(B, Hq, D, max_kv_len) > BINV_NOALLOC_SCRATCH_BYTES)
+        return BINV_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (binv::noalloc_scratch(&ws) != hipSuccess) return BINV_ERR_LAUNCH;
+    binv::AttnArgs a{q, nullptr, k_cache, v_cache, page_table, pt_stride, kv_lens, out, B, B, 1,
+                     max_kv_len, Hq, Hkv, D, (float)((double)scale * 1.4426950408889634),
+                     (float*)ws};
     return status_of(binv::launch_attention(a, (hipStream_t)stream));
 }
 

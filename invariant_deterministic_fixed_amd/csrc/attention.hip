@@ -46,7 +46,10 @@
 // has 0 * 0: the two agree except for the sign of an exactly-zero result, so
 // outputs are written with -0 turned into +0.
 #include "attn_chunk.hpp"
+#include "binv.h"
 #include "kernels.hpp"
+
+#include <mutex>
 
 namespace binv {
 
@@ -769,6 +772,36 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Fixed partials buffer of the decode entry point that allocates nothing.
+// Each GPU that loads this code object holds its own copy for the life of the
+// process.  Host code must never pass `scratch` itself to a kernel (on the host
+// the name stands for a host-side shadow, not a device address): the device
+// address comes from hipGetSymbolAddress, once per device, below.
+static __device__ __align__(256) char scratch[BINV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 size_t attn_workspace_bytes(int64_t n_tokens, int Hq, int D, int64_t max_kv_len) {
     const int64_t C = (max_kv_len + CHUNK - 1) / CHUNK;

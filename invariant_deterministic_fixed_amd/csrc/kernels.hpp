@@ -42,6 +42,9 @@ struct AttnArgs {
 
 size_t attn_workspace_bytes(int64_t n_tokens, int Hq, int D, int64_t max_kv_len);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// device address of this device's fixed no-alloc partials buffer
+// (BINV_NOALLOC_SCRATCH_BYTES), looked up on the first call per device
+hipError_t noalloc_scratch(void** ptr);
 size_t attn_tuned_workspace_bytes(int64_t B, int Hq, int D, int64_t max_kv_len);
 hipError_t launch_attention_decode_tuned(const AttnArgs& a, hipStream_t s);
 

@@ -13,7 +13,7 @@ from invariant_deterministic_fixed_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "binv.h")
 
-OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+OK, INVALID, UNSUPPORTED, WORKSPACE, SCRATCH = 0, 1, 2, 3, 5
 
 
 def declared_functions():
@@ -100,6 +100,34 @@ def test_attention_decode_validation():
     assert _dec(ws=L) == WORKSPACE
     assert _dec(scale=float("nan")) == INVALID
     assert _dec(B=70000) == UNSUPPORTED
+
+
+def _dec_noalloc(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, pt=FAKE, pts=4, kl=FAKE, out=FAKE, B=2, maxl=64, Hq=8,
+             Hkv=2, D=128, page=16, scale=0.1, s=L)
+    a.update(over)
+    return _lib().binv_attn_decode_paged_noalloc(a["q"], a["k"], a["v"], a["pt"], a["pts"],
+                                                 a["kl"], a["out"], a["B"], a["maxl"], a["Hq"],
+                                                 a["Hkv"], a["D"], a["page"], a["scale"], a["s"])
+
+
+def test_attention_decode_noalloc_validation():
+    # argument checks and the scratch limit are decided on the host, before the
+    # entry point looks up its device array or launches anything
+    assert _dec_noalloc(B=0) == OK
+    assert _dec_noalloc(q=L) == INVALID
+    assert _dec_noalloc(out=FAKE + 8) == INVALID
+    assert _dec_noalloc(Hq=6, Hkv=2) == UNSUPPORTED
+    assert _dec_noalloc(maxl=256 * 512 + 1) == UNSUPPORTED
+    assert "SCRATCH" in binv.status_str(SCRATCH)
+    limit = 128 << 20                                   # BINV_NOALLOC_SCRATCH_BYTES
+    per_b_chunk = 32 * (128 + 2) * 4                    # Hq = 32, D = 128
+    fits = limit // per_b_chunk                         # 8065 (sequence, chunk) slots
+    assert binv.attn_workspace_bytes(fits, 32, 128, 256) <= limit
+    assert binv.attn_workspace_bytes(fits + 1, 32, 128, 256) > limit
+    assert _dec_noalloc(B=fits + 1, maxl=256, Hq=32, Hkv=8) == SCRATCH
+    assert _dec_noalloc(B=64, maxl=32768, Hq=32, Hkv=8) == SCRATCH
+    assert _dec_noalloc(B=32, maxl=65536, Hq=32, Hkv=8) == SCRATCH
 
 
 def test_attention_prefill_validation():
