@@ -157,6 +157,63 @@ def run_step(w, events=None):
     rec(ev[5])
 
 
+def side_measurements(w, reps):
+    """Figures beside the step, each on operands rotated over copies larger
+    than the last-level cache: RMSNorm alone as back-to-back launches at the
+    step's shape and at the largest RMSNorm workload (16384 rows), and the
+    GEMM against hipBLASLt (torch.mm as a black box) and against the
+    library's shape-tuned split-K comparator, on the same operands."""
+    import torch
+    import invariant_deterministic_fixed_amd as binv
+    from invariant_deterministic_fixed_amd import synth
+
+    dev = w["x"].device
+    res = {}
+    b2b = {}
+    for M in (RMS_M, 16384):
+        n = _copies(4 * M * HIDDEN, floor=600 << 20)
+        xs = [synth.normal((M, HIDDEN), 3.0, 31 + i, dev).to(torch.bfloat16) for i in range(n)]
+        y = torch.empty_like(xs[0])
+        for x in xs:
+            binv.rmsnorm(x, w["gamma"], 1e-6, out=y)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        launches = max(reps, 4 * n)
+        e0.record()
+        for k in range(launches):
+            binv.rmsnorm(xs[k % n], w["gamma"], 1e-6, out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / launches * 1e-3
+        nbytes = 4 * M * HIDDEN + 2 * HIDDEN
+        b2b[f"{M}x{HIDDEN}"] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+                                "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4),
+                                "launches": launches, "input_copies": n}
+        del xs, y
+    res["rmsnorm_back_to_back"] = b2b
+
+    nW = _copies(2 * GEMM_K * GEMM_N, floor=600 << 20)
+    Ws = [w["W"]] + [w["W"].clone() for _ in range(nW - 1)]
+    C2 = torch.empty_like(w["C"])
+    ws = torch.empty(binv.lib().binv_gemm_bf16_tuned_workspace_bytes(GEMM_M, GEMM_N, GEMM_K),
+                     dtype=torch.uint8, device=dev)
+    y = w["y"]
+    t_inv = _cold_ms([lambda W=W: binv.gemm(y, W, out=C2) for W in Ws], reps=max(20, reps))
+    t_mm = _cold_ms([lambda W=W: torch.mm(y, W, out=C2) for W in Ws], reps=max(20, reps))
+    t_tun = _cold_ms([lambda W=W: binv.gemm(y, W, out=C2, tuned=True, workspace=ws) for W in Ws],
+                     reps=max(20, reps))
+    fl = 2.0 * GEMM_M * GEMM_N * GEMM_K
+    res["gemm_vs_hipblaslt"] = {
+        "invariant_TFLOPs": round(fl / t_inv / 1e9, 1),
+        "hipblaslt_torch_mm_TFLOPs": round(fl / t_mm / 1e9, 1),
+        "tuned_splitk_TFLOPs": round(fl / t_tun / 1e9, 1),
+        "invariant_over_hipblaslt_speed": round(t_mm / t_inv, 3),
+        "invariant_over_tuned_speed": round(t_tun / t_inv, 3)}
+    del Ws, C2, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def algorithmic(w):
     """Algorithmic work per launch of each leg (what the method must move / compute)."""
     lens = w["dec_lens"]
@@ -205,6 +262,44 @@ def traffic_for(kernel_key):
     return rec["hbm_bytes_per_launch"]
 
 
+def tiny_oracle_ms():
+    """The oracle on the whole tiny single-layer workload (RMSNorm of 8 fp32
+    rows of 256, the 256 x 256 GEMM, decode attention of 8 sequences with 4
+    heads of 64 and lengths U[1, 300]), on one thread and on every core."""
+    import oracle
+    from invariant_deterministic_fixed_amd import synth
+
+    x = synth.normal((8, 256), 1.0, synth.seed_for(1), dtype=torch_f32()).double().numpy()
+    g = synth.uniform((256,), 0.5, 1.5, synth.seed_for(1) + 2).double().numpy()
+    W = synth.normal((256, 256), 0.02, synth.seed_for(1) + 3).double().numpy()
+    lens = synth.uniform_int_lengths(8, 1, 300, synth.seed_for(1) + 1)
+    kv = [synth.random_kv(int(L), 4, 64, synth.seed_for(1) + 10 + i) for i, L in enumerate(lens)]
+    kv = [(k.double().numpy(), v.double().numpy()) for k, v in kv]
+
+    def run():
+        y = oracle.round_bf16(oracle.rmsnorm(x, g, 1e-6))
+        q = oracle.round_bf16(oracle.gemm(y, W)).reshape(8, 4, 64)
+        for b, (k, v) in enumerate(kv):
+            oracle.attention(q[b:b + 1], [int(lens[b]) - 1], k, v, 0.125)
+
+    full = oracle.num_threads()
+    out = {}
+    for n in (1, full):
+        oracle.set_num_threads(n)
+        run()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            run()
+        out[f"threads_{n}"] = round((time.perf_counter() - t0) / 5 * 1e3, 3)
+    oracle.set_num_threads(full)
+    return out
+
+
+def torch_f32():
+    import torch
+    return torch.float32
+
+
 def cpu_baseline(w, gemm_rows=GEMM_M, max_seqs=DEC_B, prefill_rows=512):
     """The fp64 oracle on a bounded sample of the same workload (the very same
     input values, copied from HBM to the host), on the host cores."""
@@ -238,10 +333,12 @@ def cpu_baseline(w, gemm_rows=GEMM_M, max_seqs=DEC_B, prefill_rows=512):
     oracle.attention(pq, rows, kd, vd, w["scale"])
     t_pf = time.perf_counter() - t0
     pf_flops = 4 * HQ * HD * sum(r + 1 for r in rows)
+    tiny = tiny_oracle_ms()
     return {
         "value": gemm_tflops,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
+        "tiny_layer_ms": tiny,
         "kind": "oracle",
         "sample": (f"fp64 RMSNorm + GEMM of {gemm_rows} of the {GEMM_M} rows ({t_gemm:.1f} s); "
                    f"fp64 decode attention of {n_seq} of the {DEC_B} sequences "
@@ -522,8 +619,8 @@ def gemm_shapes(shapes, reps, dev="cuda:0"):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--ramp-seconds", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-copy", action="store_true")
@@ -569,7 +666,11 @@ def main():
     wall = time.perf_counter() - t0
 
     legs = ["rmsnorm", "gemm", "decode_attn", "prefill_attn", "decoder_glue"]
-    ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(legs)}
+    per = {n: sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i, n in enumerate(legs)}
+    ms = {n: sum(v) / len(v) for n, v in per.items()}
+
+    def pct(v, q):
+        return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
     s = {n: ms[n] * 1e-3 for n in legs}
     gemm_tflops = work["gemm_flops"] / s["gemm"] / 1e12
     dec_gbps = work["decode_bytes"] / s["decode_attn"] / 1e9
@@ -599,6 +700,8 @@ def main():
         torch.cuda.synchronize()
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
+
+    extra = side_measurements(w, args.steps)
 
     gemm_traffic = traffic_for("gemm_bf16_kernel")
     dec_traffic = traffic_for("attn_decode")
@@ -632,6 +735,9 @@ def main():
                                      "kernel": "attn_chunk_kernel + attn_merge_kernel",
                                      "per_launch": {"bytes": work["decode_bytes"]}}},
         "legs_ms": {n: round(ms[n], 4) for n in legs},
+        "legs_ms_median": {n: round(pct(per[n], 0.5), 4) for n in legs},
+        "legs_ms_p10": {n: round(pct(per[n], 0.1), 4) for n in legs},
+        "legs_ms_p90": {n: round(pct(per[n], 0.9), 4) for n in legs},
         "rmsnorm_GBps": round(rms_gbps, 1),
         "rmsnorm_frac_hbm": round(rms_gbps / PEAK_HBM_GBPS, 4),
         "rmsnorm_vs_device_copy": {"copy_GBps": round(copy_gbps, 1),
@@ -639,6 +745,7 @@ def main():
         "prefill_attn_TFLOPs": round(pf_tflops, 2),
         "decoder_glue_GBps": round(glue_gbps, 1),
     }
+    out.update(extra)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

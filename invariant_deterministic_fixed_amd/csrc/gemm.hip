@@ -14,14 +14,16 @@
 // tile configuration is what pins that order; here no tile parameter enters
 // the chain at all (a row's slot in a tile only decides which lane carries
 // it), so the output tile can follow the shape without the bits following:
-//   * 256 x 256 tiles when that gives >= 192 tiles (large M),
-//   * strips of 16, 32 or 64 columns for M <= 64 (decode batches;
-//     gemm_skinny_kernel),
-//   * 128 x 128 tiles when that gives >= 192 tiles,
+//   * 256 x 256 tiles when that gives >= 192 tiles (large M; gemm_pp_kernel,
+//     its two wave groups taking turns at LDS reads and MFMAs),
+//   * for M <= 64 (decode batches), strips of 16 or 32 columns held by a
+//     four-wave workgroup up to 8192-wide outputs (gemm_strip_kernel), strips
+//     of 64 columns one wave each beyond (gemm_skinny_kernel),
+//   * 128 x 128 tiles (four LDS stages) when that gives >= 192 tiles,
 //   * 64 x 64 tiles (4 waves of 32 x 32, four LDS stages) otherwise.
-// Tests check a row's bits across M = 1 .. 8192, i.e. across all three.  The
-// comparator below (128 x 128 with split-K chosen from the tile count) is the
-// one that does change with M.
+// Tests check a row's bits across M = 1 .. 8192 and every kernel against the
+// others.  The comparator below (128 x 128 with split-K chosen from the tile
+// count) is the one that does change with M.
 //
 // Tile kernel (256 x 256 shown; 128 x 128 and 64 x 64 are the same code with
 // 4 waves, 64 x 64 with four LDS stages and 64-column W rows swizzled by
@@ -174,6 +176,42 @@ struct Tile {
         }
     }
 
+    // the wave's FM x FN accumulator tiles -> C rows r0 .., columns c0 ..
+    // (lane l holds rows 4(l/16) + e, column l % 16 of each 16 x 16 tile)
+    __device__ static void store_c(const f32x4 (&acc)[FM][FN], void* __restrict__ C, int64_t ldc,
+                                   int r0, int c0, int lane, int M, int N, int c_f32) {
+        const int col_base = c0 + (lane & 15);
+        const int row_base = r0 + 4 * (lane >> 4);
+        if (c_f32) {
+            float* Cf = reinterpret_cast<float*>(C);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int col = col_base + 16 * j;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = row_base + 16 * i + e;
+                        if (row < M && col < N) Cf[(int64_t)row * ldc + col] = acc[i][j][e];
+                    }
+                }
+        } else {
+            bf16_t* Cb = reinterpret_cast<bf16_t*>(C);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int col = col_base + 16 * j;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = row_base + 16 * i + e;
+                        if (row < M && col < N)
+                            Cb[(int64_t)row * ldc + col] = (bf16_t)f32_to_bf16(acc[i][j][e]);
+                    }
+                }
+        }
+    }
+
     // K-tiles [kt_begin, kt_end) of tile blockIdx.x; fp32 partials of split z
     // go to C + z * split_stride (comparator only).
     template <bool SPLIT>
@@ -221,36 +259,10 @@ struct Tile {
             compute(As, As + A_BYTES, acc, wm, wn, lane);
         }
 
-        const int col_base = n0 + wn * TN + (lane & 15);
-        const int row_base = m0 + wm * TM + 4 * (lane >> 4);
-        if (c_f32) {
-            float* Cf = reinterpret_cast<float*>(C) + (SPLIT ? (int64_t)blockIdx.z * split_stride : 0);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int col = col_base + 16 * j;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int row = row_base + 16 * i + e;
-                        if (row < M && col < N) Cf[(int64_t)row * ldc + col] = acc[i][j][e];
-                    }
-                }
-        } else {
-            bf16_t* Cb = reinterpret_cast<bf16_t*>(C);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int col = col_base + 16 * j;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int row = row_base + 16 * i + e;
-                        if (row < M && col < N)
-                            Cb[(int64_t)row * ldc + col] = (bf16_t)f32_to_bf16(acc[i][j][e]);
-                    }
-                }
-        }
+        store_c(acc, SPLIT ? (void*)((char*)C + (c_f32 ? 4 : 2) * (int64_t)blockIdx.z *
+                                                  split_stride)
+                           : C,
+                ldc, m0 + wm * TM, n0 + wn * TN, lane, M, N, c_f32);
     }
 };
 
@@ -418,9 +430,428 @@ hipError_t launch_skinny(const void* A, int64_t lda, const void* W, int64_t ldw,
     return hipGetLastError();
 }
 
+// ------------------------------------------------------- few rows, four waves
+// M <= 64 (decode batches).  A single wave can issue only about one 1 KB
+// HBM -> LDS copy (buffer_load ... lds) per ~70 cycles, however deep its ring
+// (measured: ~13 bytes per clock per CU from one wave, ~47 from eight), so a
+// strip streamed by one wave is bound by that issue rate, not by memory.  Here
+// a workgroup of four waves owns one strip of 16 FN columns of W and all M
+// rows (RT row tiles of 16).  K-tile kt (64 rows of W, the matching 64 columns
+// of A) is copied into stage kt % (4 R) of an LDS ring by wave kt % 4; one
+// round = four consecutive K-tiles, one per wave; copies run up to D rounds
+// ahead.  One workgroup barrier per round publishes the next round's stages
+// and frees the current round's stages for the copies of round r + D (D <= R),
+// so a computing wave reads round r + 1's fragments while round r's MFMAs run.
+// Wave w computes row tile w (rows 16w .. 16w + 15) if it holds rows < M.
+// Each element's arithmetic is the tile kernels' exactly: one fp32
+// accumulator, v_mfma_f32_16x16x32_bf16 over the same 32-wide k-blocks in
+// ascending order, the same zero padding of a ragged K-tile and of columns
+// past N (copies of rows k >= K and of columns n >= N read zero).
+// LDS layout per stage: A [16 RT][64] as in the big tile (chunk c of row r at
+// c ^ (r & 7)), W [64][16 FN] as in gemm_skinny_kernel (wpos).
+template <int FN, int RT, int R, int D>
+__global__ __launch_bounds__(256) void gemm_strip_kernel(const bf16_t* __restrict__ A, int64_t lda,
+                                                         const bf16_t* __restrict__ W, int64_t ldw,
+                                                         void* __restrict__ C, int64_t ldc, int M,
+                                                         int N, int K, int c_f32) {
+    constexpr int NWV = 4;
+    // copying waves: with one row tile the computing wave 0 copies nothing
+    // (each copy instruction costs its wave tens of cycles to issue), and a
+    // round is two K-tiles per copying wave; with four row tiles every wave
+    // copies one K-tile per round
+    constexpr int NCW = RT == 1 ? 3 : 4, CW0 = NWV - NCW, PER = RT == 1 ? 2 : 1;
+    constexpr int KR = NCW * PER;                              // K-tiles per round
+    constexpr int BN = 16 * FN, RB = 2 * BN;                 // row bytes of the W strip
+    constexpr int A_BYTES = 16 * RT * BK * 2, W_BYTES = BK * RB, STAGE = A_BYTES + W_BYTES;
+    constexpr int PA = A_BYTES / 1024, PW = W_BYTES / 1024, P = PER * (PA + PW);
+    constexpr int NSTG = KR * R;
+    constexpr int RPI = 1024 / RB, LPR = RB / 16;             // W rows per copy, lanes per row
+    static_assert(D >= 2 && D <= R, "copies run at most R rounds ahead");
+    static_assert((D - 1) * P <= 63, "vmcnt holds 6 bits");
+    __shared__ __attribute__((aligned(1024))) char smem[NSTG * STAGE];
+    // the wave index as a scalar, so that every copy's LDS address is known
+    // to be wave-uniform (no per-lane loop around the copies)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int b = blockIdx.x, x = b & 7, local = b >> 3;
+    constexpr int GS = (FN >= 8) ? 1 : 8 / FN;                // strips per 128-byte line group
+    const int n0 = ((local / GS) * 8 * GS + x * GS + (local % GS)) * BN;
+    if (n0 >= N) return;                                      // whole workgroup
+    const int nk = (K + BK - 1) / BK;
+    const int nr = (nk + KR - 1) / KR;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)A, (short)0, (int)((int64_t)M * lda * 2), RSRC_WORD3);
+    // this wave's first K-tile of round rd (copying waves only)
+    const int cw = wave - CW0;
+    auto first_kt = [&](int rd) { return KR * rd + PER * cw; };
+    auto wpos = [&](int k, int c) -> int {
+        if constexpr (FN == 1) return skinny_row(k) * RB + c * 16;
+        else if constexpr (FN == 2) return k * RB + ((c ^ (2 * ((k >> 3) & 1))) << 4);
+        else return k * RB + ((c ^ (2 * (((k >> 1) & 1) + 2 * ((k >> 3) & 1)))) << 4);
+    };
+    auto issue = [&](int kt) {
+        char* As = smem + (kt % NSTG) * STAGE;
+        char* Ws = As + A_BYTES;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int u = 0; u < PA; ++u) {
+            const int row = 8 * u + (lane >> 3);
+            const int c = (lane & 7) ^ swz_a(row);
+            const int kk = k0 + 8 * c;
+            const int off = (row < M && kk < K) ? (row * (int)lda + kk) * 2 : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(As + u * 1024), 16, off, 0, 0, 0);
+        }
+        const int krows = min(BK, K - k0);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(W + (int64_t)k0 * ldw + n0), (short)0, (int)((int64_t)krows * ldw * 2), RSRC_WORD3);
+#pragma unroll
+        for (int u = 0; u < PW; ++u) {
+            const int pr = RPI * u + lane / LPR, pcpos = lane % LPR;
+            int kr, pc;
+            if constexpr (FN == 1) { kr = skinny_row(pr); pc = pcpos; }
+            else if constexpr (FN == 2) { kr = pr; pc = pcpos ^ (2 * ((pr >> 3) & 1)); }
+            else { kr = pr; pc = pcpos ^ (2 * (((pr >> 1) & 1) + 2 * ((pr >> 3) & 1))); }
+            const int off = (kr < krows && n0 + 8 * pc < N) ? (kr * (int)ldw + 8 * pc) * 2 : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(Ws + u * 1024), 16, off, 0, 0, 0);
+        }
+    };
+    // the copies of round rd by this wave (its PER K-tiles that exist)
+    auto copy_round = [&](int rd) {
+        if (cw < 0) return;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int kt = first_kt(rd) + p;
+            if (kt < nk) issue(kt);
+        }
+    };
+#pragma unroll
+    for (int rr = 0; rr < D; ++rr) copy_round(rr);
+    f32x4 acc[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool computes = (wave < RT) && (16 * wave < M);
+    // fragments of one round, as the computing wave reads them from LDS
+    struct Frags {
+        u32x2 p0[KR][2][FN], p1[KR][2][FN];
+        u32x4 a[KR][2];
+    };
+    // read round rd's fragments (stages of K-tiles >= nk hold stale data that
+    // is read but never fed to an MFMA).  With one row tile the computing wave
+    // issues no copies and reads through the compiler's transposing-read
+    // builtin, so the compiler tracks the reads (its wait for outstanding LDS
+    // copies before them is empty for this wave) and they may stay in flight
+    // across the next barrier.  With four row tiles every wave also copies, so
+    // the reads are inline asm (no wait for the wave's own copies in flight)
+    // and are waited for before anything else uses their registers.
+    constexpr bool PIPE = (RT == 1);
+    auto read_round = [&](Frags& f, int rd) {
+#pragma unroll
+        for (int j = 0; j < KR; ++j) {
+            const char* As = smem + ((KR * rd + j) % NSTG) * STAGE;
+            const char* Ws = As + A_BYTES;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int k_lo = 32 * ks + 8 * g + (r >> 2), k_hi = k_lo + 4;
+#pragma unroll
+                for (int jj = 0; jj < FN; ++jj) {
+                    const int c = 2 * jj + ((r & 3) >> 1);
+                    const char* plo = Ws + wpos(k_lo, c) + 8 * (r & 1);
+                    const char* phi = Ws + wpos(k_hi, c) + 8 * (r & 1);
+                    if constexpr (PIPE) {
+                        f.p0[j][ks][jj] = __builtin_bit_cast(
+                            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)plo));
+                        f.p1[j][ks][jj] = __builtin_bit_cast(
+                            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)phi));
+                    } else {
+                        f.p0[j][ks][jj] = ds_read_tr_b64(plo);
+                        f.p1[j][ks][jj] = ds_read_tr_b64(phi);
+                    }
+                }
+                const int row = 16 * wave + r;
+                f.a[j][ks] = *reinterpret_cast<const u32x4*>(
+                    As + (row << 7) + (((4 * ks + g) ^ swz_a(row)) << 4));
+            }
+        }
+        if constexpr (!PIPE) {
+#pragma unroll
+            for (int j = 0; j < KR; ++j)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int jj = 0; jj < FN; ++jj)
+                        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.p0[j][ks][jj]), "+v"(f.p1[j][ks][jj]) : : "memory");
+        }
+    };
+    // MFMAs of round rd, K-tiles in order, each k-step in order
+    auto mfma_tile = [&](Frags& f, int j) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj) {
+                const u32x4 bf = u32x4{f.p0[j][ks][jj][0], f.p0[j][ks][jj][1],
+                                       f.p1[j][ks][jj][0], f.p1[j][ks][jj][1]};
+                acc[jj] = mfma16x16x32(f.a[j][ks], bf, acc[jj]);
+            }
+    };
+    auto mfma_round = [&](Frags& f, int rd) {
+        if (KR * (rd + 1) <= nk) {                    // a full round: no per-tile test
+#pragma unroll
+            for (int j = 0; j < KR; ++j) mfma_tile(f, j);
+        } else {
+#pragma unroll
+            for (int j = 0; j < KR; ++j)
+                if (KR * rd + j < nk) mfma_tile(f, j);
+        }
+    };
+    // barrier certifying round rd: this wave's copies of round rd have landed
+    // (`later` rounds after it may still be in flight: an exact count only
+    // while every one of them was issued, else wait for everything) and so
+    // have every other wave's; the computing waves have finished reading the
+    // rounds before rd
+    auto certify = [&](int rd, auto later) {
+        constexpr int L = decltype(later)::value;
+        if (cw < 0) {
+        } else if (first_kt(rd + L) + PER - 1 < nk) {
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(L * P) : "memory");
+        } else {
+            wait_vm0();
+        }
+        // every LDS read retired, as a builtin so that the compiler knows it
+        // (no further wait for them before the MFMAs that use them): gfx9
+        // s_waitcnt encoding, lgkmcnt 0, vmcnt 63 and expcnt 7 (no wait)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    Frags fa, fb;
+    certify(0, std::integral_constant<int, D - 1>{});
+    if (computes) read_round(fa, 0);
+    // round rd: certify round rd + 1, copy round rd + D into the stage of
+    // round rd + D - R (read before this barrier, as D <= R), read round
+    // rd + 1 while round rd's MFMAs run
+    auto step = [&](Frags& cur, Frags& nxt, int rd) {
+        if (rd + 1 < nr) certify(rd + 1, std::integral_constant<int, D - 2>{});
+        if (rd + 1 < nr) copy_round(rd + D);
+        if (computes) {
+            if (rd + 1 < nr) read_round(nxt, rd + 1);
+            mfma_round(cur, rd);
+        }
+    };
+    for (int rd = 0; rd < nr; rd += 2) {
+        step(fa, fb, rd);
+        if (rd + 1 < nr) step(fb, fa, rd + 1);
+    }
+    if (!computes) return;
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj) {
+        const int col = n0 + 16 * jj + r;
+        if (col >= N) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * wave + 4 * g + e;
+            if (row >= M) continue;
+            if (c_f32)
+                reinterpret_cast<float*>(C)[(int64_t)row * ldc + col] = acc[jj][e];
+            else
+                reinterpret_cast<bf16_t*>(C)[(int64_t)row * ldc + col] = (bf16_t)f32_to_bf16(acc[jj][e]);
+        }
+    }
+}
+
+template <int FN, int RT, int R, int D>
+hipError_t launch_strip(const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
+                        int64_t ldc, int M, int N, int K, int c_f32, hipStream_t s) {
+    const int strips = (N + 16 * FN - 1) / (16 * FN);
+    constexpr int GS = (FN >= 8) ? 1 : 8 / FN;
+    const int grid = (strips + 8 * GS - 1) / (8 * GS) * (8 * GS);
+    hipLaunchKernelGGL((gemm_strip_kernel<FN, RT, R, D>), dim3((unsigned)grid), dim3(256), 0, s,
+                       (const bf16_t*)A, lda, (const bf16_t*)W, ldw, C, ldc, M, N, K, c_f32);
+    return hipGetLastError();
+}
+
 using BigTile = Tile<256, 256, 2, 4, 8>;
-using MidTile = Tile<128, 128, 2, 2, 8>;         // also the comparator's tile
+using MidTile = Tile<128, 128, 2, 2, 8>;         // the comparator's tile
+using MidTile4 = Tile<128, 128, 2, 2, 8, 4>;     // the same with four LDS stages
 using SmallTile = Tile<64, 64, 2, 2, 8, 4>;      // 4 waves of 32 x 32, four stages
+
+// ------------------------------------------------------------------ large M
+// The 256 x 256 tile of BigTile (same LDS stages, same DMA, same fragments,
+// same per-element MFMA chain, so the same bits), scheduled so that the matrix
+// cores of a SIMD are not kept waiting on LDS reads.  The eight waves form two
+// groups of four: group 0 (waves 0-3) owns tile rows 0-127, group 1 rows
+// 128-255, and each SIMD runs one wave of each group.  Per K-tile a wave has
+// two phases: M, reading all its A and W fragments of the K-tile (both
+// 32-wide k-steps) from LDS into registers, and C, its 64 MFMAs on those
+// registers alone.  Group 1 starts one workgroup barrier behind group 0, and
+// every wave passes one barrier per phase, so the two waves on a SIMD are
+// always in opposite phases: one feeds its MFMAs back to back while the other
+// reads LDS.  With barrier events e1, e2, ...:
+//   group 0: e(2kt+1) M(kt) e(2kt+2) C(kt)       (one extra barrier at the end)
+//   group 1: e(2kt+2) M(kt) e(2kt+3) C(kt)       (one extra barrier at the start)
+// Stage kt & 1 is read by group 0 in [e(2kt+1), e(2kt+2)] and by group 1 in
+// [e(2kt+2), e(2kt+3)], so it is free after e(2kt+3).  K-tile kt + 2 goes into
+// it then: group 0 requests its share during M(kt + 1), group 1 at the start
+// of C(kt); each wave waits for its own share before the barrier at which
+// group 0 starts reading that K-tile (e(2kt+5)), two phases later.  Every
+// barrier is preceded by lgkmcnt(0), so no LDS read is in flight when a stage
+// is handed to the DMA.
+__device__ __forceinline__ void pp_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class T>
+__device__ __forceinline__ void pp_load(const char* As, const char* Ws, u32x4 (&a)[2][T::FM],
+                                        u32x4 (&b)[2][T::FN], int wm, int wn, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+            const int c = (wn * T::TN + 16 * j + 4 * (r & 3)) >> 3;
+            const int k_lo = 32 * ks + 8 * g + (r >> 2), k_hi = k_lo + 4;
+            const v4i16 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(Ws + k_lo * T::BN_ * 2 + ((c ^ T::swzw(k_lo)) << 4) + 8 * (r & 1)));
+            const v4i16 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(Ws + k_hi * T::BN_ * 2 + ((c ^ T::swzw(k_hi)) << 4) + 8 * (r & 1)));
+            const u32x2 p0 = __builtin_bit_cast(u32x2, h0), p1 = __builtin_bit_cast(u32x2, h1);
+            b[ks][j] = u32x4{p0[0], p0[1], p1[0], p1[1]};
+        }
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+            const int row = wm * T::TM + 16 * i + r;
+            a[ks][i] = *reinterpret_cast<const u32x4*>(As + (row << 7) +
+                                                       (((4 * ks + g) ^ swz_a(row)) << 4));
+        }
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void pp_mfma(const u32x4 (&a)[2][T::FM], const u32x4 (&b)[2][T::FN],
+                                        f32x4 (&acc)[T::FM][T::FN]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) acc[i][j] = mfma16x16x32(a[ks][i], b[ks][j], acc[i][j]);
+}
+
+// DMA of K-tile kt into stage kt & 1 for a tile that lies wholly inside A, W
+// and C with K a multiple of 64 (the tiles that take the two-group schedule): the same copies as Tile::issue (same LDS
+// positions, same swizzles), with no bounds tests, each lane's offset a
+// per-lane base plus a wave-uniform part.
+struct PPFull {
+    int va, vw0, vw1;          // per-lane byte offsets: A; W rows of even / odd u
+    __device__ PPFull(int64_t lda, int64_t ldw, int wave, int lane) {
+        const int ra = lane >> 3;
+        va = ra * (int)lda * 2 + (((lane & 7) ^ swz_a(ra)) << 4);
+        const int rw = lane >> 5;
+        vw0 = rw * (int)ldw * 2 + (((lane & 31) ^ swz_w(8 * wave + 0 + rw)) << 4);
+        vw1 = rw * (int)ldw * 2 + (((lane & 31) ^ swz_w(8 * wave + 2 + rw)) << 4);
+    }
+    __device__ void issue(char* smem, int kt, const bf16_t* A, int64_t lda, const bf16_t* W,
+                          int64_t ldw, int m0, int n0, int wave) const {
+        using T = BigTile;
+        char* As = smem + (kt & 1) * T::STAGE;
+        char* Ws = As + T::A_BYTES;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(A + (int64_t)m0 * lda), (short)0, (int)(T::BM_ * lda * 2), RSRC_WORD3);
+#pragma unroll
+        for (int u = 0; u < T::A_PW; ++u) {
+            const int j = wave * T::A_PW + u;                  // rows 8j .. 8j + 7
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(As + j * 1024), 16, va,
+                                                     8 * j * (int)lda * 2 + kt * BK * 2, 0, 0);
+        }
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(W + (int64_t)kt * BK * ldw + n0), (short)0, (int)(BK * ldw * 2), RSRC_WORD3);
+#pragma unroll
+        for (int u = 0; u < T::W_PW; ++u) {
+            const int j = wave * T::W_PW + u;                  // rows 2j, 2j + 1
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(Ws + j * 1024), 16,
+                                                     (u & 1) ? vw1 : vw0, 2 * j * (int)ldw * 2, 0,
+                                                     0);
+        }
+    }
+};
+static_assert(BigTile::W_PW == 4 && BigTile::WROWS == 2 && BigTile::BN_ / 8 == 32,
+              "PPFull assumes the 256 x 256 tile's W copy geometry");
+
+__device__ __forceinline__ void pp_body(const bf16_t* __restrict__ A, int64_t lda,
+                                        const bf16_t* __restrict__ W, int64_t ldw,
+                                        void* __restrict__ C, int64_t ldc, int M, int N, int K,
+                                        int c_f32, int m0, int n0, char* smem) {
+    using T = BigTile;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int grp = wave >> 2, wm = grp, wn = wave & 3;
+    const int nk = (K + BK - 1) / BK;
+    f32x4 acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 a[2][T::FM], b[2][T::FN];
+    const PPFull pf(lda, ldw, wave, lane);
+    auto issue = [&](int kt) { pf.issue(smem, kt, A, lda, W, ldw, m0, n0, wave); };
+    if (grp == 0) {
+        if (nk > 0) issue(0);
+        wait_vm0();
+        for (int kt = 0; kt < nk; ++kt) {
+            pp_barrier();                                         // e(2kt+1)
+            const char* As = smem + (kt & 1) * T::STAGE;
+            pp_load<T>(As, As + T::A_BYTES, a, b, wm, wn, lane);
+            if (kt + 1 < nk) issue(kt + 1);                       // stage (kt+1)&1 freed at e(2kt+1)
+            pp_barrier();                                         // e(2kt+2)
+            pp_mfma<T>(a, b, acc);
+            // the wait stays after the MFMAs (the scheduler would otherwise
+            // hoist it above them and stall on the copy just issued)
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm0();                                           // this wave's share of kt+1
+        }
+        pp_barrier();                                             // e(2nk+1)
+    } else {
+        if (nk > 0) issue(0);
+        if (nk > 1) {
+            issue(1);
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(T::PW) : "memory");
+        } else {
+            wait_vm0();
+        }
+        pp_barrier();                                             // e1
+        for (int kt = 0; kt < nk; ++kt) {
+            pp_barrier();                                         // e(2kt+2)
+            const char* As = smem + (kt & 1) * T::STAGE;
+            pp_load<T>(As, As + T::A_BYTES, a, b, wm, wn, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm0();                                           // this wave's share of kt+1
+            pp_barrier();                                         // e(2kt+3): stage kt&1 free
+            if (kt + 2 < nk) issue(kt + 2);
+            pp_mfma<T>(a, b, acc);
+        }
+    }
+    T::store_c(acc, C, ldc, m0 + wm * T::TM, n0 + wn * T::TN, lane, M, N, c_f32);
+}
+
+__global__ __launch_bounds__(512) void gemm_pp_kernel(const bf16_t* __restrict__ A, int64_t lda,
+                                                      const bf16_t* __restrict__ W, int64_t ldw,
+                                                      void* __restrict__ C, int64_t ldc, int M,
+                                                      int N, int K, int c_f32) {
+    using T = BigTile;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+    int tm, tn;
+    tile_of<8>(blockIdx.x, (M + T::BM_ - 1) / T::BM_, (N + T::BN_ - 1) / T::BN_, tm, tn);
+    const int m0 = tm * T::BM_, n0 = tn * T::BN_;
+    // A tile wholly inside A, W and C with no ragged K-tile takes the two-group
+    // schedule, whose copies need no bounds tests; a tile on the edge of C or
+    // of a ragged K takes BigTile's one-group schedule with its bounds-tested
+    // copies (uniform branch).  Both run the same per-element MFMA chain.
+    if (m0 + T::BM_ <= M && n0 + T::BN_ <= N && K % BK == 0)
+        pp_body(A, lda, W, ldw, C, ldc, M, N, K, c_f32, m0, n0, smem);
+    else
+        T::template run<false>(A, lda, W, ldw, C, ldc, 0, M, N, K, 0, c_f32, smem);
+}
 
 template <class T, bool SPLIT>
 __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(const bf16_t* __restrict__ A, int64_t lda,
@@ -478,29 +909,40 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, v
     if (M == 0 || N == 0) return hipSuccess;
     const int nk = (K + BK - 1) / BK;
     const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    if (big_tiles >= 192)
-        return launch_tile<BigTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
-                                    c_f32, s);
+    if (big_tiles >= 192) {
+        hipLaunchKernelGGL(gemm_pp_kernel, dim3((unsigned)big_tiles), dim3(512), 0, s,
+                           (const bf16_t*)A, lda, (const bf16_t*)W, ldw, C, ldc, M, N, K, c_f32);
+        return hipGetLastError();
+    }
     if (M > 64) {
         const int64_t mid_tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
         if (mid_tiles >= 192)
-            return launch_tile<MidTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
-                                        c_f32, s);
+            return launch_tile<MidTile4>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
+                                         c_f32, s);
         return launch_tile<SmallTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
                                       c_f32, s);
     }
     {
+        // strips of 16 FN columns, FN the widest that still gives >= 192 strips.
+        // Up to 8192-wide outputs (FN = 1, 2: at most 512 strips) a strip is one
+        // four-wave workgroup (gemm_strip_kernel, one row tile for decode
+        // batches of up to 16, four up to 64; ring of R rounds, copies D rounds
+        // ahead, sized to the LDS and the 6-bit copy counter; FN = 2 with one
+        // row tile fits two workgroups per CU).  Wider outputs (FN = 4) give
+        // each CU several one-wave strips (gemm_skinny_kernel), whose copies
+        // then come from several waves as well.
         const int fn = (N / 64 >= 192) ? 4 : (N / 32 >= 192) ? 2 : 1;
-#define BINV_SKINNY(FM, NS1, NS2, NS4)                                                        \
-    switch (fn) {                                                                          \
-        case 4: return launch_skinny<FM, 4, NS4>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s); \
-        case 2: return launch_skinny<FM, 2, NS2>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s); \
-        default: return launch_skinny<FM, 1, NS1>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s); \
-    }
-        if (M <= 16) { BINV_SKINNY(1, 4, 6, 6) }
-        if (M <= 32) { BINV_SKINNY(2, 4, 4, 4) }
-        BINV_SKINNY(4, 4, 4, 4)
-#undef BINV_SKINNY
+        if (fn == 4) {
+            if (M <= 16) return launch_skinny<1, 4, 6>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
+            if (M <= 32) return launch_skinny<2, 4, 4>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
+            return launch_skinny<4, 4, 4>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
+        }
+        if (M <= 16) {
+            if (fn == 2) return launch_strip<2, 1, 3, 3>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
+            return launch_strip<1, 1, 6, 6>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
+        }
+        if (fn == 2) return launch_strip<2, 4, 3, 3>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
+        return launch_strip<1, 4, 3, 3>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
     }
     return hipErrorInvalidValue;        // not reached
 }

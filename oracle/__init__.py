@@ -43,6 +43,8 @@ def _load():
     i64 = ctypes.c_int64
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     lib.oracle_round_bf16.restype = ctypes.c_double
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
     lib.oracle_round_bf16_array.restype = None
@@ -73,6 +75,11 @@ def _p(a):
 def num_threads():
     """OpenMP threads the oracle's row loops use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n):
+    """Threads for the oracle's row loops from now on (results do not change)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def round_bf16(x):

@@ -33,6 +33,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Sets the number of OpenMP threads the row loops use (for timing the oracle
+ * on one core or on all of them; the arithmetic of every row is unchanged). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* bf16 rounding: nearest value with 8 significant bits, ties to even.       */
 /* bf16 = 1 sign bit, 8 exponent bits (same range as binary32), 7 stored     */
