@@ -101,7 +101,8 @@ def build_workload(device="cuda:0", seed_base=0):
     w["pf_q"] = synth.normal((PREFILL_T, HQ, HD), 1.0, s4 + 11, device)
     w["pf_cu"] = torch.tensor([0, PREFILL_T], dtype=torch.int32, device=device)
     w["pf_out"] = torch.empty_like(w["pf_q"])
-    w["pf_ws"] = torch.empty(binv.attn_workspace_bytes(PREFILL_T, HQ, HD, PREFILL_T),
+    w["pf_ws"] = torch.empty(binv.attn_prefill_workspace_bytes(1, PREFILL_T, PREFILL_T, PREFILL_T,
+                                                               HQ, HKV, HD),
                              dtype=torch.uint8, device=device)
     w["scale"] = 1.0 / math.sqrt(HD)
 
@@ -479,7 +480,9 @@ def sweep(dev="cuda:0"):
     c = paged([T], synth.seed_for(4) + 3)
     q = synth.normal((T, HQ, HD), 1.0, 13, dev)
     out = torch.empty_like(q)
-    ws = torch.empty(binv.attn_workspace_bytes(T, HQ, HD, T), dtype=torch.uint8, device=dev)
+    # sized for the largest piece; every smaller piece needs less
+    ws = torch.empty(binv.attn_prefill_workspace_bytes(1, T, T, T, HQ, HKV, HD), dtype=torch.uint8,
+                     device=dev)
     scale = 1.0 / math.sqrt(HD)
     for chunk in [T, 2048, 512, 256]:
         parts = []
@@ -508,7 +511,8 @@ def sweep(dev="cuda:0"):
         out = torch.empty_like(q)
         cu = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32, device=dev)
         kvl = torch.full((B,), ctx, dtype=torch.int32, device=dev)
-        ws = torch.empty(binv.attn_workspace_bytes(T, HQ, HD, ctx), dtype=torch.uint8, device=dev)
+        ws = torch.empty(binv.attn_prefill_workspace_bytes(B, T, run_len, ctx, HQ, HKV, HD),
+                         dtype=torch.uint8, device=dev)
         t = _cold_ms([lambda: binv.attn_prefill(q, cu, c.k_cache, c.v_cache, c.page_table, kvl,
                                                 run_len, ctx, 1.0 / math.sqrt(HD), out=out,
                                                 workspace=ws)], reps=5)

@@ -150,10 +150,22 @@ int binv_gemm_bf16(const void* A, int64_t lda,
  *   either path and in any call.  An output element that is exactly zero is
  *   written as +0.
  *
- * Workspace: fp32 partials, caller-owned, at least
- *   binv_attn_workspace_bytes(n_query_tokens, Hq, D, max_kv_len) bytes.
+ * Workspace: fp32 partials, caller-owned.  Decode needs at least
+ *   binv_attn_workspace_bytes(B, Hq, D, max_kv_len) bytes (one partial per
+ *   query row and chunk); prefill at least
+ *   binv_attn_prefill_workspace_bytes(B, T, max_q_len, max_kv_len, Hq, Hkv, D),
+ *   which never exceeds binv_attn_workspace_bytes(T, Hq, D, max_kv_len).
+ *   Prefill rows of long new-token runs (D = 128, a sequence with at least
+ *   ceil(64 / (Hq / Hkv)) new tokens) keep only the merge tree's pending
+ *   subtrees, at most floor(log2(ceil(max_kv_len / 256))) per row, so a
+ *   single-sequence prefill needs T * Hq * that many * (D + 2) * 4 bytes; rows
+ *   of short runs keep one partial per chunk, indexed per sequence when that
+ *   is smaller than per token.  Both functions return 0 for arguments the
+ *   entry points reject.
  * ------------------------------------------------------------------------ */
 size_t binv_attn_workspace_bytes(int64_t n_query_tokens, int Hq, int D, int64_t max_kv_len);
+size_t binv_attn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t max_q_len,
+                                         int64_t max_kv_len, int Hq, int Hkv, int D);
 
 /* Decode: one query token per sequence.
  * q    bf16 [B, Hq, D]

@@ -41,6 +41,7 @@ def _declare(lib):
         "binv_gemm_bf16_tuned_workspace_bytes": (sz, [i64, i64, i64]),
         "binv_gemm_bf16_tuned": (ci, [vp, i64, vp, i64, vp, ci, i64, i64, i64, i64, vp, sz, vp]),
         "binv_attn_workspace_bytes": (sz, [i64, ci, ci, i64]),
+        "binv_attn_prefill_workspace_bytes": (sz, [i64, i64, i64, i64, ci, ci, ci]),
         "binv_attn_decode_paged": (ci, [vp, vp, vp, vp, i64, vp, vp, i64, i64, ci, ci, ci, ci,
                                         f32, vp, sz, vp]),
         "binv_attn_prefill_paged": (ci, [vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, i64,
@@ -166,6 +167,10 @@ def attn_workspace_bytes(n_query_tokens, Hq, D, max_kv_len):
     return lib().binv_attn_workspace_bytes(n_query_tokens, Hq, D, max_kv_len)
 
 
+def attn_prefill_workspace_bytes(B, T, max_q_len, max_kv_len, Hq, Hkv, D):
+    return lib().binv_attn_prefill_workspace_bytes(B, T, max_q_len, max_kv_len, Hq, Hkv, D)
+
+
 def attn_decode(q, k_cache, v_cache, page_table, kv_lens, max_kv_len, scale, out=None,
                 workspace=None, tuned=False):
     """q [B, Hq, D] bf16; caches as laid out in include/binv.h."""
@@ -220,7 +225,8 @@ def attn_prefill(q, cu_q, k_cache, v_cache, page_table, kv_lens, max_q_len, max_
     assert q.is_contiguous() and cu_q.dtype == torch.int32
     if out is None:
         out = torch.empty_like(q)
-    need = lib().binv_attn_workspace_bytes(T, Hq, D, max_kv_len)
+    need = lib().binv_attn_prefill_workspace_bytes(B, T, int(max_q_len), int(max_kv_len), Hq, Hkv,
+                                                   D)
     ws, nbytes = _workspace(need, q.device, workspace)
     st = lib().binv_attn_prefill_paged(_ptr(q), _ptr(cu_q), _ptr(k_cache), _ptr(v_cache),
                                        _ptr(page_table), page_table.stride(0), _ptr(kv_lens),

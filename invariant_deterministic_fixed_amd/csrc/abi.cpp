@@ -141,6 +141,14 @@ size_t binv_attn_workspace_bytes(int64_t n_query_tokens, int Hq, int D, int64_t 
     return binv::attn_workspace_bytes(n_query_tokens, Hq, D, max_kv_len);
 }
 
+size_t binv_attn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t max_q_len,
+                                         int64_t max_kv_len, int Hq, int Hkv, int D) {
+    if (B <= 0 || T <= 0 || max_q_len <= 0 || max_kv_len <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 ||
+        Hq % Hkv != 0)
+        return 0;
+    return binv::attn_prefill_workspace_bytes(B, T, max_q_len, max_kv_len, Hq, Hkv, D);
+}
+
 int binv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* page_table, int64_t pt_stride, const int32_t* kv_lens,
                            void* out, int64_t B, int64_t max_kv_len, int Hq, int Hkv, int D,
@@ -198,7 +206,7 @@ int binv_attn_prefill_paged(const void* q, const int32_t* cu_q, const void* k_ca
     const int G = Hq / Hkv;
     const int64_t nqt = (max_q_len + 16 / G - 1) / (16 / G);
     if (nqt * Hkv > I32MAX) return BINV_ERR_UNSUPPORTED;
-    const size_t need = binv::attn_workspace_bytes(T, Hq, D, max_kv_len);
+    const size_t need = binv::attn_prefill_workspace_bytes(B, T, max_q_len, max_kv_len, Hq, Hkv, D);
     if (!workspace || ws_bytes < need || !aligned16(workspace)) return BINV_ERR_WORKSPACE;
     binv::AttnArgs a{q, cu_q, k_cache, v_cache, page_table, pt_stride, kv_lens, out, B, T,
                      max_q_len, max_kv_len, Hq, Hkv, D,

@@ -41,6 +41,8 @@ struct AttnArgs {
 };
 
 size_t attn_workspace_bytes(int64_t n_tokens, int Hq, int D, int64_t max_kv_len);
+size_t attn_prefill_workspace_bytes(int64_t B, int64_t T, int64_t max_q_len, int64_t max_kv_len,
+                                    int Hq, int Hkv, int D);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // device address of this device's fixed no-alloc partials buffer
 // (BINV_NOALLOC_SCRATCH_BYTES), looked up on the first call per device

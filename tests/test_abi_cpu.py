@@ -150,6 +150,39 @@ def test_workspace_sizes():
     assert binv.attn_workspace_bytes(0, 32, 128, 100) == 0
 
 
+def test_prefill_workspace_sizes():
+    f = binv.attn_prefill_workspace_bytes
+    node = 32 * (128 + 2) * 4                      # one partial of every head of a token
+    # one long sequence: the pending subtrees only, floor(log2(chunks)) per row
+    assert f(1, 4096, 4096, 4096, 32, 8, 128) == 4096 * 4 * node
+    assert f(1, 4096, 4096, 32768, 32, 8, 128) == 4096 * 7 * node
+    assert f(1, 64, 64, 256, 32, 8, 128) == 64 * 1 * node
+    # four long sequences: stacks per token plus leaves for at most 15 short
+    # tokens per sequence (the block kernel takes runs of 16 or more at G = 4)
+    assert f(4, 4096, 1024, 4096, 32, 8, 128) == (4096 * 4 + 4 * 15 * 16) * node
+    # one prompt chunk among decode rows: leaves per token are smaller
+    T = 512 + 63
+    assert f(64, T, 512, 1024, 32, 8, 128) == binv.attn_workspace_bytes(T, 32, 128, 1024)
+    # short runs only, and D = 64: one leaf per row and chunk
+    assert f(8, 8, 1, 4096, 32, 8, 128) == binv.attn_workspace_bytes(8, 32, 128, 4096)
+    assert f(1, 4096, 4096, 4096, 8, 8, 64) == binv.attn_workspace_bytes(4096, 8, 64, 4096)
+    # never more than one partial per row and chunk
+    for B in (1, 2, 7, 64):
+        for T in (B, 3 * B, 100, 4096):
+            if T < B:
+                continue
+            for mq in sorted({1, 15, 16, 64, T - B + 1}):
+                for kv in (256, 1000, 4096, 131072):
+                    if mq > kv:
+                        continue
+                    for (hq, hkv) in ((32, 8), (32, 32), (16, 1)):
+                        assert 0 < f(B, T, mq, kv, hq, hkv, 128) <= \
+                            binv.attn_workspace_bytes(T, hq, 128, kv)
+    # rejected arguments
+    assert f(0, 16, 16, 256, 32, 8, 128) == 0
+    assert f(1, 16, 16, 256, 32, 7, 128) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libbinv.so")

@@ -298,6 +298,47 @@ def test_prefill_head_groups_parity_and_decode_bitwise(Hq, Hkv):
     assert_bitwise_equal(dec, out, "decode vs prefill")
 
 
+@pytest.mark.parametrize("lens,qlens", [
+    ([2000], [700]),                            # one sequence: pending subtrees only
+    ([1500, 900, 300], [400, 7, 300]),          # leaves of short runs indexed per sequence
+    ([1024] * 40, [100] + [1] * 39),            # leaves indexed per token, stacks among them
+])
+def test_prefill_workspace_layouts(lens, qlens):
+    # The workspace of a prefill call is laid out by its shape: stacks of the
+    # merge tree's pending subtrees for rows of long runs, one leaf per chunk
+    # for rows of short runs.  With a workspace of exactly the reported size,
+    # filled with NaN, every row equals the decode of its position bit for bit
+    # (a slot read before it is written would carry the NaN into the output).
+    Hq, Hkv, D = 32, 8, 128
+    cache, seqs = make_cache(lens, Hkv, D, 91 + len(lens))
+    T = sum(qlens)
+    q = synth.normal((T, Hq, D), 1.0, 92 + len(lens), DEV)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    scale = 1 / math.sqrt(D)
+    need = binv.attn_prefill_workspace_bytes(len(lens), T, max(qlens), max(lens), Hq, Hkv, D)
+    assert 0 < need <= binv.attn_workspace_bytes(T, Hq, D, max(lens))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    out = binv.attn_prefill(q, torch.as_tensor(cu, dtype=torch.int32, device=DEV), cache.k_cache,
+                            cache.v_cache, cache.page_table,
+                            torch.as_tensor(lens, dtype=torch.int32, device=DEV), max(qlens),
+                            max(lens), scale, workspace=ws)
+    assert bool(torch.isfinite(out.float()).all())
+    b_of = np.repeat(np.arange(len(lens)), qlens)
+    pos_of = np.concatenate([[lens[b] - qlens[b] + i for i in range(qlens[b])]
+                             for b in range(len(lens))])
+    pt = cache.page_table[torch.as_tensor(b_of, device=DEV)].contiguous()
+    kv = torch.as_tensor(pos_of + 1, dtype=torch.int32, device=DEV)
+    dec = binv.attn_decode(q, cache.k_cache, cache.v_cache, pt, kv, max(lens), scale)
+    assert_bitwise_equal(dec, out, "decode vs prefill")
+    # sampled rows against the oracle: first, last and a middle row of each run
+    for b, (k, v) in enumerate(seqs[:3]):
+        n = qlens[b]
+        for i in sorted({0, n // 2, n - 1}):
+            r = int(cu[b]) + i
+            ref = oracle.attention(f64(q[r:r + 1]), [lens[b] - n + i], f64(k), f64(v), scale)
+            assert row_rel_err(f64(out[r:r + 1]), ref).max() <= TOL_BF16, (b, i)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (32, 2)])
 def test_prefill_short_and_long_query_runs_bitwise_equal(Hq, Hkv):
     # At D = 128 a prefill call whose longest new-token run fills less than
