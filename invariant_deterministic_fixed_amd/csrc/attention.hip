@@ -111,11 +111,10 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     const int32_t* __restrict__ kv_lens, float* __restrict__ ws_o,
     float2* __restrict__ ws_ml, int Hq, int Hkv, int n_chunks, int max_kv_len,
     float scale_log2, int q_skip, int leaf_seq) {
-    constexpr bool VL = (R == 1);           // V through LDS for single-tile (decode) workgroups
     // prefill: sequences with q_skip or more new tokens belong to the block kernel
     if (cu_q && cu_q[blockIdx.z + 1] - cu_q[blockIdx.z] >= q_skip) return;
     static_assert(LOOP || GMAX == 0, "workgroups that take one chunk write leaves");
-    __shared__ ChunkLds<D, R, VL> sh;
+    __shared__ ChunkLds<D, R> sh;
     constexpr int JT = ChunkShape<D>::JT;
     const int kv_len_b = kv_lens[blockIdx.z];          // read once, kept in a register
     const int pos_max = tile_ctx_len<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
@@ -136,7 +135,7 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
             load_k<D>(x1, blockIdx.y * gs, phys_next, kc, pt_stride, Hkv, kf, threadIdx.x);
             // the tile's q, the same for every chunk, staged in LDS once
             if constexpr (LOOP) {
-                stage_q<D, G, R, VL>(x1, q, Hq, sh, threadIdx.x);
+                stage_q<D, G, R>(x1, q, Hq, sh, threadIdx.x);
                 lds_barrier();
             }
         }
@@ -170,7 +169,7 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
                     c_nx = c_next;
                 }
             }
-            ChunkOut<R> carry = chunk_compute<D, G, R, VL, LOOP>(
+            ChunkOut<R> carry = chunk_compute<D, G, R, LOOP>(
                 x, c, phys, page_table, q, kc, vc, pt_stride, Hq, Hkv, scale_log2, sh, t, kf, c_nx,
                 phys_next);
             // binary increment: equal-size subtrees merge, the older one on the left
@@ -201,29 +200,22 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
         }
         int t = threadIdx.x;
         if constexpr (LOOP) asm volatile("" : "+v"(t));
-        const int lane = t & 63, wave = t >> 6, ag = lane >> 4;
+        const int lane = t & 63, wave = t >> 6, ar = lane & 15, ag = lane >> 4;
         const TileCtx x = tile_ctx_len<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
                                              kv_len_b, pt_stride, max_kv_len);
         const int j0 = node * gs * CHUNK;
-        // partials of the rows that see at least one key of this node
+        // partials of the rows that see at least one key of this node: lane
+        // (ag, ar) writes features 16 wave + 4 ag .. + 3 of row 16 rt + ar,
+        // lanes ag = 0 of wave 0 the row's (max, sum)
 #pragma unroll
-        for (int rt = 0; rt < R; ++rt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const RowInfo ri = row_info<G, R>(16 * rt + 4 * ag + e, x.b, x.g, x.qt, x.q_len,
-                                                  x.q_start, x.kv_len);
-                if (ri.token < 0 || ri.pos < j0) continue;
-                const int64_t lr = leaf_seq ? (int64_t)x.b * leaf_seq + (ri.token - x.q_start) : ri.token;
-                const int64_t slot_i = (lr * n_chunks + node) * Hq + ri.head;
-                ws_o[slot_i * D + 16 * wave + (lane & 15)] = r.o[rt][e];
-            }
-        if (t < 256 * R && (t & 15) == 0) {
-            const RowInfo ri = row_info<G, R>(t >> 4, x.b, x.g, x.qt, x.q_len, x.q_start, x.kv_len);
-            if (ri.token >= 0 && ri.pos >= j0) {
-                const int64_t lr = leaf_seq ? (int64_t)x.b * leaf_seq + (ri.token - x.q_start) : ri.token;
-                const int64_t slot_i = (lr * n_chunks + node) * Hq + ri.head;
-                ws_ml[slot_i] = make_float2(r.ml_m, r.l);
-            }
+        for (int rt = 0; rt < R; ++rt) {
+            const RowInfo ri = row_info<G, R>(16 * rt + ar, x.b, x.g, x.qt, x.q_len, x.q_start,
+                                              x.kv_len);
+            if (ri.token < 0 || ri.pos < j0) continue;
+            const int64_t lr = leaf_seq ? (int64_t)x.b * leaf_seq + (ri.token - x.q_start) : ri.token;
+            const int64_t slot_i = (lr * n_chunks + node) * Hq + ri.head;
+            *reinterpret_cast<f32x4*>(ws_o + slot_i * D + 16 * wave + 4 * ag) = r.o[rt];
+            if (wave == 0 && ag == 0) ws_ml[slot_i] = make_float2(r.m[rt], r.l[rt]);
         }
         if constexpr (!LOOP) break;
     }
@@ -237,13 +229,14 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
 // cross-wave reduction; each chunk's K and V pages are copied HBM -> LDS once
 // (global_load_lds) and read by all eight tiles, so 128 rows share one load
 // of the chunk where a chunk-kernel workgroup shares it among 16.  Every
-// per-element operation is the chunk kernel's, in the same order: q.k as
-// v_mfma_f32_16x16x32_bf16 over features 32ks + 8(lane>>4) .. +8, ks
-// ascending; scale, mask, exact max; p = bf16(exp2(s - m)); l = sixteen
-// sequential 16-key sums combined as the pairwise tree ((s0+s1)+(s2+s3)) +
-// ... (what the chunk kernel's xor butterfly forms); p.v over keys 32ks +
-// 8(lane>>4) .. +8, ks ascending, V slots at or past kv_len read as zero --
-// so a row's chunk partial has the same bits as from the chunk kernel.
+// per-element operation is the chunk kernel's, in the same order: S^T = K Q^T
+// as v_mfma_f32_16x16x32_bf16 over features 32 ks + 8 (lane >> 4) .. + 8, ks
+// ascending; scale, mask, exact max; p = bf16(exp2(s - m)); l and
+// O^T = V^T P^T in the key order of the p.v products (attn_chunk.hpp), V
+// slots at or past kv_len read as zero -- so a row's chunk partial has the
+// same bits as from the chunk kernel.  Lane (ag, ar) of a wave holds one row,
+// ar, throughout: its scores of keys 16 kt + 4 ag + e, then its p as the p.v
+// operand (p never leaves the registers), then features 16 f + 4 ag + e.
 // The partials are merged in the workgroup as they come, by the merge
 // kernel's binary counter and combine (the left-aligned tree padded to a fixed
 // depth): the counter's lowest slot (a single chunk) stays in registers, the
@@ -259,36 +252,37 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
 // the output).  The root o / l, bf16, is the merge kernel's last step; so a
 // prefill row equals the decode of the same position bit for bit.
 // LDS: K [16 pages][16 keys][128] with 16-byte chunk c of key k at c ^ (k & 15);
-// V [16 pages][128 features][16 slots] with the 16-byte half h of feature d
-// at h ^ ((d >> 3) & 1); once every tile has its scores, the K area holds each
-// tile's p [16 rows][256 keys] (8 KB per wave, the chunk kernel's swizzle).
-// The q area holds the block's 128 query rows for all chunks.
+// V [16 pages][128 features][16 slots] swizzled as in v_src; q [128 rows][128], 16-byte chunk c of
+// row r at c ^ (r & 15), for all chunks.  The K area is free once every tile
+// has its scores, and the next chunk's K is copied into it while the scores
+// become p and p.v runs; the next chunk's V is copied once p.v is done, while
+// the partial is merged and the next chunk's q.k runs.
 constexpr int PF_WAVES = 8;
 constexpr int PF_ROWS = 16 * PF_WAVES;
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8; the other counters left at their no-wait maxima), given to the
+// compiler's own builtin so that its wait insertion knows they were done
+constexpr int WAIT_VM8 = 0x0F78;   // vmcnt(8)
+constexpr int WAIT_VM0 = 0x0F70;   // vmcnt(0)
 
-// a chunk partial (or a subtree of them) of a wave's 16 rows as the block
-// kernel holds it: the max of rows 4(lane>>4) + e (me) and of row lane & 15
-// (mr), the sum of weights of row lane & 15 (lr), and the weighted values of
-// rows 4(lane>>4) + e, features 16 f + (lane & 15) (o)
+// a chunk partial (or a subtree of them) of one row as a lane of the block
+// kernel holds it: the row's max and sum of weights, and its weighted values
+// of features 16 f + 4 (lane >> 4) + e
 struct PfNode {
-    float me[4];
-    float mr, lr;
+    float m, l;
     f32x4 o[8];
 };
 
 // the merge kernel's combine (combine_scale, combine_val), a on the left
 __device__ __forceinline__ PfNode pf_combine(const PfNode& a, const PfNode& b) {
     PfNode r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        float fa, fb;
-        combine_scale(a.me[e], b.me[e], r.me[e], fa, fb);
-#pragma unroll
-        for (int f = 0; f < 8; ++f) r.o[f][e] = combine_val(fa, a.o[f][e], fb, b.o[f][e]);
-    }
     float fa, fb;
-    combine_scale(a.mr, b.mr, r.mr, fa, fb);
-    r.lr = combine_val(fa, a.lr, fb, b.lr);
+    combine_scale(a.m, b.m, r.m, fa, fb);
+    r.l = combine_val(fa, a.l, fb, b.l);
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.o[f][e] = combine_val(fa, a.o[f][e], fb, b.o[f][e]);
     return r;
 }
 
@@ -303,19 +297,20 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     constexpr int D = 128, KS = D / 32, NKT = CHUNK / 16;
     // sequences with fewer than q_min new tokens belong to the chunk kernel
     if (cu_q[blockIdx.z + 1] - cu_q[blockIdx.z] < q_min) return;
-    // one object, so that the compiler can tell the V copy's destination from
-    // the q and K areas read while it is in flight
+    // one object, so that the compiler can tell the copies' destinations from
+    // the areas read while they are in flight
     struct PfLds {
-        __attribute__((aligned(1024))) char k[16 * PAGE * D * 2];   // K, then p
+        __attribute__((aligned(1024))) char k[16 * PAGE * D * 2];
         __attribute__((aligned(1024))) char v[16 * D * PAGE * 2];
-        // q of the block's 128 rows [row][D], 16-byte chunk c of row r at c ^ (r & 15)
         __attribute__((aligned(1024))) char q[PF_ROWS * D * 2];
     };
     __shared__ PfLds sh;
     char* const kbuf = sh.k;
     char* const vbuf = sh.v;
     char* const qbuf = sh.q;
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    // (the mask bounds the value for the compiler, which then can tell the K
+    // and V areas' copies and reads apart and waits only for what a read needs)
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) & (PF_WAVES - 1);
     // blocks in reverse order: the blocks that see the most chunks start first
     const int g = blockIdx.x % Hkv, qb = nqb - 1 - (int)(blockIdx.x / Hkv), b = blockIdx.z;
     const TileCtx x = tile_ctx<G, PF_WAVES>(b, g, qb, cu_q, kv_lens, pt_stride, max_kv_len);
@@ -357,21 +352,19 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
                 (__attribute__((address_space(3))) void*)(qbuf + wave * (16 * D * 2) + part * 1024),
                 16, 0, 0);
     }
-    // K and then V pages 2 wave, 2 wave + 1 of chunk c (pages past the
-    // sequence copy page 0 of the cache: their keys are masked, their V slots
-    // read as zero).  Copies retire in issue order, so q.k waits for K while V
-    // is in flight.
-    auto copy_kv = [&](int c, int lane) {
-        const char* ksrc[2];
-        const char* vsrc[2];
+    // K or V pages 2 wave, 2 wave + 1 of chunk c, 8 copies of 1 KB per wave
+    // (pages past the sequence copy page 0 of the cache: their keys are
+    // masked, their V slots read as zero)
+    auto page_of = [&](int c, int u) -> int64_t {
+        const int pidx = 16 * c + 2 * wave + u;
+        const bool ok = pidx < x.n_pages && pidx < pt_stride;
+        return ok ? (int64_t)page_table[x.pt_row + pidx] : 0;
+    };
+    auto copy_k = [&](int c, int lane) {
+        const char* src[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int pidx = 16 * c + 2 * wave + u;
-            const bool ok = pidx < x.n_pages && pidx < pt_stride;
-            const int64_t ph = ok ? (int64_t)page_table[x.pt_row + pidx] : 0;
-            ksrc[u] = reinterpret_cast<const char*>(kc + (ph * Hkv + g) * (PAGE * D));
-            vsrc[u] = reinterpret_cast<const char*>(vc + (ph * Hkv + g) * (D * PAGE));
-        }
+        for (int u = 0; u < 2; ++u)
+            src[u] = reinterpret_cast<const char*>(kc + (page_of(c, u) * Hkv + g) * (PAGE * D));
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int pl = 2 * wave + u;
@@ -380,245 +373,181 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
                 // LDS position part*1024 + 16 lane: key 4 part + lane / 16, chunk lane & 15
                 const int key = 4 * part + (lane >> 4), pos = lane & 15;
                 __builtin_amdgcn_global_load_lds(
-                    (const void*)(ksrc[u] + key * (D * 2) + ((pos ^ key) << 4)),
+                    (const void*)(src[u] + key * (D * 2) + ((pos ^ key) << 4)),
                     (__attribute__((address_space(3))) void*)(kbuf + pl * (PAGE * D * 2) + part * 1024),
                     16, 0, 0);
             }
         }
+    };
+    auto copy_v = [&](int c, int lane) {
+        const char* src[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            src[u] = reinterpret_cast<const char*>(vc + (page_of(c, u) * Hkv + g) * (D * PAGE));
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int pl = 2 * wave + u;
 #pragma unroll
-            for (int part = 0; part < 4; ++part) {
-                // LDS position part*1024 + 16 lane: feature 32 part + lane / 2, half lane & 1
-                const int d = 32 * part + (lane >> 1), h = lane & 1;
+            for (int part = 0; part < 4; ++part)
                 __builtin_amdgcn_global_load_lds(
-                    (const void*)(vsrc[u] + d * (PAGE * 2) + ((h ^ ((d >> 3) & 1)) << 4)),
+                    (const void*)(src[u] + v_src(part, lane)),
                     (__attribute__((address_space(3))) void*)(vbuf + pl * (D * PAGE * 2) + part * 1024),
                     16, 0, 0);
-            }
         }
     };
-    copy_kv(0, lane_id());
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // this wave's q and K copies landed
-    lds_barrier();                                    // every wave's: q and K of the block in LDS
+    {
+        const int lane = lane_id();
+        copy_k(0, lane);
+        copy_v(0, lane);
+    }
 
     // ---- the per-row stack of the counter's slots >= 1: level s of a row at
     // ((token * st_stride + s - 1) * Hq + head); each lane stores and loads only
-    // the values it holds (o of rows 4(lane>>4) + e; (max, sum) of row lane & 15
-    // by the lanes of group 0, passed to the other lanes by shuffles)
-    auto slot_of = [&](int r, int s) -> int64_t {
-        const RowInfo ri = row(r);
+    // the values it holds (features 16 f + 4 ag .. + 3 of row ar; the row's
+    // (max, sum) by the lanes of group 0, passed to the others by shuffles)
+    auto slot_of = [&](int ar, int s) -> int64_t {
+        const RowInfo ri = row(ar);
         return ri.token < 0 ? (int64_t)-1 : ((ri.token * st_stride + (s - 1)) * Hq + ri.head);
     };
     auto stack_store = [&](int s, const PfNode& nd, int lane) {
         const int ar = lane & 15, ag = lane >> 4;
+        const int64_t sl = slot_of(ar, s);
+        if (sl < 0) return;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t sl = slot_of(4 * ag + e, s);
-            if (sl < 0) continue;
-#pragma unroll
-            for (int f = 0; f < 8; ++f) st_o[sl * D + 16 * f + ar] = nd.o[f][e];
-        }
-        if (ag == 0) {
-            const int64_t sl = slot_of(ar, s);
-            if (sl >= 0) st_ml[sl] = make_float2(nd.mr, nd.lr);
-        }
+        for (int f = 0; f < 8; ++f) *reinterpret_cast<f32x4*>(st_o + sl * D + 16 * f + 4 * ag) = nd.o[f];
+        if (ag == 0) st_ml[sl] = make_float2(nd.m, nd.l);
     };
     auto stack_load = [&](int s, int lane) -> PfNode {
         const int ar = lane & 15, ag = lane >> 4;
+        const int64_t sl = slot_of(ar, s);
         PfNode nd;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t sl = slot_of(4 * ag + e, s);
-#pragma unroll
-            for (int f = 0; f < 8; ++f) nd.o[f][e] = sl < 0 ? 0.0f : st_o[sl * D + 16 * f + ar];
-        }
         float2 ml = make_float2(-INFINITY, 0.0f);
-        if (ag == 0) {
-            const int64_t sl = slot_of(ar, s);
-            if (sl >= 0) ml = st_ml[sl];
-        }
-        nd.mr = __shfl(ml.x, ar);
-        nd.lr = __shfl(ml.y, ar);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) nd.me[e] = __shfl(ml.x, 4 * ag + e);
+        for (int f = 0; f < 8; ++f)
+            nd.o[f] = sl < 0 ? f32x4{0.f, 0.f, 0.f, 0.f}
+                             : *reinterpret_cast<const f32x4*>(st_o + sl * D + 16 * f + 4 * ag);
+        if (ag == 0 && sl >= 0) ml = st_ml[sl];
+        nd.m = __shfl(ml.x, ar);
+        nd.l = __shfl(ml.y, ar);
         return nd;
     };
+
+    __builtin_amdgcn_s_waitcnt(WAIT_VM8);             // this wave's q and K copies landed
+    lds_barrier();                                    // every wave's: q and K(0) in LDS
 
     PfNode slot0;
     unsigned count = 0;
 #pragma clang loop unroll(disable)
     for (int c = 0; c < nc; ++c) {
         const int j0 = c * CHUNK;
+        const bool more = c + 1 < nc;
         const int lane = lane_id(), ar = lane & 15, ag = lane >> 4;
         if (c > 0) {
-            copy_kv(c, lane);
-            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // this wave's K copies landed
-            lds_barrier();                                    // every wave's
+            // K(c) and the stack stores landed (only V(c) may be in flight)
+            __builtin_amdgcn_s_waitcnt(WAIT_VM8);
+            lds_barrier();                                    // every wave's K(c) in LDS
         }
-        int rpos[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rpos[e] = row(4 * ag + e).pos;
-        char* const pt = kbuf + wave * (16 * CHUNK * 2);     // this tile's p
+        const int rpos = row(ar).pos;
 
-        // ---- S = Q K^T: key tile kt holds keys 16 kt .. 16 kt + 15 of the
-        // chunk; q fragments: row 16 wave + (lane & 15), features 32 ks +
-        // 8 (lane >> 4) .. +8
+        // ---- S^T = K Q^T: tile kt holds, in lane (ag, ar), row ar against
+        // keys 16 kt + 4 ag + e; q fragment: row 16 wave + ar, features
+        // 32 ks + 8 ag .. + 8; K fragment: key 16 kt + ar, the same features
         f32x4 sc[NKT];
         {
-            u32x4 qf[KS];
+            // k-steps outer, the 16 independent tiles inner (each tile's
+            // chain still runs over ks ascending)
             const char* qrow = qbuf + (16 * wave + ar) * (D * 2);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qf[ks] = *reinterpret_cast<const u32x4*>(qrow + (((4 * ks + ag) ^ ar) << 4));
+            for (int kt = 0; kt < NKT; ++kt) sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const char* krow = kbuf + (16 * kt + ar) * (D * 2);
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + (((4 * ks + ag) ^ ar) << 4));
-                    sc[kt] = mfma16x16x32(qf[ks], kf, sc[kt]);
-                }
-            }
-        }
-        // scale, mask (key <= the row's position), row max over the 256 keys,
-        // then p = bf16(2^(s - m)) into this tile's 8 KB of the K area.  Below
-        // the diagonal every key of the chunk is valid for every row of the
-        // wave and the mask is left out; the two versions are separate
-        // wave-uniform paths (same values), each with the one barrier that
-        // frees the K area.  p = 0 for a masked key comes from 2^(-inf - m): a
-        // row whose keys are all masked (m = -inf) takes m = 0 there, which
-        // gives p = 0 as well -- the per-score test v == -inf of the chunk
-        // kernel, per row instead.
-        float mx[4];
-        auto softmax = [&](auto masked) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                mx[e] = -INFINITY;
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 qf = *reinterpret_cast<const u32x4*>(qrow + (((4 * ks + ag) ^ ar) << 4));
+                const int kofs = ar * (D * 2) + (((4 * ks + ag) ^ ar) << 4);
 #pragma unroll
                 for (int kt = 0; kt < NKT; ++kt) {
-                    float v = sc[kt][e] * scale_log2;
-                    if constexpr (decltype(masked)::value) {
-                        if (j0 + 16 * kt + ar > rpos[e]) v = -INFINITY;
-                    }
-                    sc[kt][e] = v;
-                    mx[e] = fmaxf(mx[e], v);
+                    const u32x4 kf = *reinterpret_cast<const u32x4*>(kbuf + kt * (16 * D * 2) + kofs);
+                    sc[kt] = mfma16x16x32(kf, qf, sc[kt]);
                 }
-                // max over the 16 lanes of the row group: rotations by 1, 2, 4, 8
-                // within each 16-lane DPP row (max is exact, so the order of the
-                // exchange does not matter)
-                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
-                                         0, __float_as_int(mx[e]), 0x121, 0xf, 0xf, false)));
-                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
-                                         0, __float_as_int(mx[e]), 0x122, 0xf, 0xf, false)));
-                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
-                                         0, __float_as_int(mx[e]), 0x124, 0xf, 0xf, false)));
-                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
-                                         0, __float_as_int(mx[e]), 0x128, 0xf, 0xf, false)));
             }
-            lds_barrier();                            // every tile done with K: its area takes p
-            float mu[4];
+        }
+        lds_barrier();                                    // every tile done with K(c)
+        if (more) copy_k(c + 1, lane);
+
+        // ---- mask (key <= the row's position), the row's max over its four
+        // lane groups, p = bf16(2^(s c - m)) packed as the p.v operand, and l
+        // in the key order of the p.v products.  Below the diagonal every key
+        // of the chunk is valid for every row of the wave and the mask is left
+        // out.  p = 0 for a masked key (s = -inf) comes from 2^(-inf): a row
+        // whose keys are all masked (m = -inf) takes m = 0 there, which gives
+        // p = 0 as well -- the per-score test s == -inf of the chunk kernel.
+        float mx = -INFINITY;
+        const int key_lane = j0 + 4 * ag;                 // + 16 kt + e
+        if (__all(j0 + CHUNK - 1 <= rpos)) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) mu[e] = (mx[e] == -INFINITY) ? 0.0f : mx[e];
-            // p_off(row, key >> 3) + 2 (key & 7) with row = 4 ag + e, key = 16 kt + ar:
-            // (key >> 3) ^ row = 2 kt ^ ((ar >> 3) ^ row), so the byte offset is a
-            // per-row base plus (32 kt) ^ z -- one xor-add per store
-            int base[4], z[4];
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * ag + e;
-                base[e] = (r << 9) + 2 * (ar & 7);
-                z[e] = ((ar >> 3) ^ (r & 31)) << 4;
-            }
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[kt][e]);
+        } else {
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p = exp2_score(sc[kt][e] - mu[e]);
-                    *reinterpret_cast<bf16_t*>(pt + (((32 * kt) ^ z[e]) + base[e])) =
-                        (bf16_t)f32_to_bf16(p);
+                    const float v = key_lane + 16 * kt + e <= rpos ? sc[kt][e] : -INFINITY;
+                    sc[kt][e] = v;
+                    mx = fmaxf(mx, v);
                 }
-            }
-        };
-        if (__all(j0 + CHUNK - 1 <= min(min(rpos[0], rpos[1]), min(rpos[2], rpos[3]))))
-            softmax(std::false_type{});
-        else
-            softmax(std::true_type{});
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile's p, read below by its own wave
-
-        // ---- l of row ar: segments 4(lane>>4) .. +3 summed key by key, then the
-        // pairwise tree over the 16 segment sums
-        float lrow;
-        {
-            float seg[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int sg = 4 * ag + k;
-                const u32x4 p0 = *reinterpret_cast<const u32x4*>(pt + p_off(ar, 2 * sg));
-                const u32x4 p1 = *reinterpret_cast<const u32x4*>(pt + p_off(ar, 2 * sg + 1));
-                float acc = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { acc += lo_bf16(p0[i]); acc += hi_bf16(p0[i]); }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { acc += lo_bf16(p1[i]); acc += hi_bf16(p1[i]); }
-                seg[k] = acc;
-            }
-            float c4 = (seg[0] + seg[1]) + (seg[2] + seg[3]);
-            c4 += __shfl_xor(c4, 16);
-            c4 += __shfl_xor(c4, 32);
-            lrow = c4;
         }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx *= scale_log2;                                 // the row's max, log2 domain
+        const float mu = (mx == -INFINITY) ? 0.0f : mx;
+        u32x4 pb[8];
+        float acc = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    pb[kb][2 * h + i] = p_pack(p_of(sc[2 * kb + h][2 * i], scale_log2, mu),
+                                               p_of(sc[2 * kb + h][2 * i + 1], scale_log2, mu));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = l_add(pb[kb][i], acc);
+        }
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
 
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's V copies landed
-        lds_barrier();                                    // every wave's: V of the chunk in LDS
+        // V(c) landed (K(c + 1) may still be in flight), in every wave
+        if (more) __builtin_amdgcn_s_waitcnt(WAIT_VM8);
+        else __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+        lds_barrier();
 
-        // ---- O = P V: feature tile f holds features 16 f .. 16 f + 15; keys
-        // ascending in k-blocks of 32 per (tile, f)
+        // ---- O^T = V^T P^T: feature tile f holds, in lane (ag, ar), row ar,
+        // features 16 f + 4 ag + e; 32-key blocks ascending.  V slots at or
+        // past kv_len exist only in the sequence's last chunk.
         PfNode leaf;
         {
-            u32x4 pa[8];
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-                pa[ks] = *reinterpret_cast<const u32x4*>(pt + p_off(ar, 4 * ks + ag));
-            // V slots at or past kv_len exist only in the sequence's last chunk;
-            // in every other chunk the zeroing is skipped (block-uniform branch)
+            // key blocks outer, the 8 independent feature tiles inner (each
+            // tile's chain still runs over kb ascending); the masked loop only
+            // for the sequence's last chunk (block-uniform branch)
+            const lds_cptr vl = v_lane(vbuf, ar, ag);         // feature tile f at + 16 f * 32
             auto pv = [&](auto masked) {
 #pragma unroll
-                for (int f = 0; f < D / 16; ++f) {
-                    leaf.o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const int d = 16 * f + ar;
+                for (int f = 0; f < D / 16; ++f) leaf.o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < 8; ++ks) {
-                        const int pl = 2 * ks + (ag >> 1), h = ag & 1;
-                        u32x4 v = *reinterpret_cast<const u32x4*>(
-                            vbuf + pl * (D * PAGE * 2) + d * (PAGE * 2) + ((h ^ ((d >> 3) & 1)) << 4));
-                        if constexpr (decltype(masked)::value) {
-                            const int nvalid = kv_len - ((16 * c + pl) * PAGE + 8 * h);
+                for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                if (2 * i + 1 >= nvalid) v[i] &= (2 * i < nvalid) ? 0x0000ffffu : 0u;
-                            }
-                        }
-                        leaf.o[f] = mfma16x16x32(pa[ks], v, leaf.o[f]);
-                    }
-                }
+                    for (int f = 0; f < D / 16; ++f)
+                        leaf.o[f] = mfma16x16x32(
+                            v_frag<D, decltype(masked)::value>(vl + f * (16 * PAGE * 2), kb, ag, kv_len - j0),
+                            pb[kb], leaf.o[f]);
             };
             if (j0 + CHUNK > kv_len) pv(std::true_type{});
             else pv(std::false_type{});
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) leaf.me[e] = mx[e];
-        {
-            // the max of row lane & 15, from a lane of its row group
-            const int src = 16 * (ar >> 2);
-            const float m0 = __shfl(mx[0], src), m1 = __shfl(mx[1], src);
-            const float m2 = __shfl(mx[2], src), m3 = __shfl(mx[3], src);
-            const int e = ar & 3;
-            leaf.mr = e == 0 ? m0 : e == 1 ? m1 : e == 2 ? m2 : m3;
-        }
-        leaf.lr = lrow;
+        leaf.m = mx;
+        leaf.l = acc;
+        lds_barrier();                                    // every tile done with V(c)
 
         // ---- push the chunk into the binary counter: equal-size subtrees
         // merge, the older one on the left (uniform over the block)
@@ -635,7 +564,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
             stack_store(sl, carry, lane);
         }
         ++count;
-        lds_barrier();                                    // K, p and V free for the next chunk
+        if (more) copy_v(c + 1, lane);
     }
 
     // ---- the root: remaining subtrees, smallest (rightmost) first
@@ -650,15 +579,16 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
         }
     }
     // out = o / l as bf16, an exact zero written as +0 (the merge kernel's last step)
+    const RowInfo ri = row(ar);
+    if (ri.token >= 0) {
+        bf16_t* orow = out + (ri.token * Hq + ri.head) * D + 4 * ag;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float l = __shfl(res.lr, 4 * ag + e);
-        const RowInfo ri = row(4 * ag + e);
-        if (ri.token < 0) continue;
-        bf16_t* orow = out + (ri.token * Hq + ri.head) * D;
-#pragma unroll
-        for (int f = 0; f < 8; ++f)
-            orow[16 * f + ar] = (bf16_t)f32_to_bf16(res.o[f][e] / l + 0.0f);
+        for (int f = 0; f < 8; ++f) {
+            uint2 w;
+            w.x = pack_bf16x2(res.o[f][0] / res.l + 0.0f, res.o[f][1] / res.l + 0.0f);
+            w.y = pack_bf16x2(res.o[f][2] / res.l + 0.0f, res.o[f][3] / res.l + 0.0f);
+            *reinterpret_cast<uint2*>(orow + 16 * f) = w;
+        }
     }
 }
 

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_spl
     const int32_t* __restrict__ page_table, int64_t pt_stride, const int32_t* __restrict__ kv_lens,
     float* __restrict__ ws_o, float2* __restrict__ ws_ml, int Hq, int Hkv, int s_target,
     int s_max, int max_kv_len, float scale_log2) {
-    __shared__ ChunkLds<D, 1, true> sh;
+    __shared__ ChunkLds<D, 1> sh;
     const int s = blockIdx.y;
     const TileCtx x = tile_ctx<G, 1>(blockIdx.z, blockIdx.x, 0, nullptr, kv_lens, pt_stride, max_kv_len);
     if (x.pos_max < 0) return;
@@ -52,47 +52,32 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_spl
     split_range(n, s_target, s, c0, c1);
     if (c0 >= c1) return;
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, ag = lane >> 4;
-    float M[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // lane (ag, ar) of every wave: row ar, features 16 wave + 4 ag .. + 3
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, ar = lane & 15, ag = lane >> 4;
+    float M = -INFINITY, L = 0.0f;
     f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
-    float L = 0.0f, MR = -INFINITY;
     for (int c = c0; c < c1; ++c) {
         __syncthreads();                           // LDS of the previous chunk is free
         int phys[ChunkShape<D>::JT];
         load_phys<D>(x, c, page_table, pt_stride, phys, t);
         u32x4 kf[ChunkShape<D>::JT][ChunkShape<D>::KS];
-        const ChunkOut<1> r = chunk_compute<D, G, 1, true>(x, c, phys, page_table, q, kc, vc,
-                                                           pt_stride, Hq, Hkv, scale_log2, sh, t,
-                                                           kf);
+        const ChunkOut<1> r = chunk_compute<D, G, 1>(x, c, phys, page_table, q, kc, vc,
+                                                     pt_stride, Hq, Hkv, scale_log2, sh, t, kf);
+        if (r.m[0] != -INFINITY) {
+            const float mn = fmaxf(M, r.m[0]);
+            const float fa = (M == -INFINITY) ? 0.0f : exp2f(M - mn);
+            const float fb = exp2f(r.m[0] - mn);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (r.m[0][e] == -INFINITY) continue;
-            const float mn = fmaxf(M[e], r.m[0][e]);
-            const float fa = (M[e] == -INFINITY) ? 0.0f : exp2f(M[e] - mn);
-            const float fb = exp2f(r.m[0][e] - mn);
-            O[e] = fa * O[e] + fb * r.o[0][e];
-            M[e] = mn;
-        }
-        if (t < 256 && (t & 15) == 0 && r.ml_m != -INFINITY) {
-            const float mn = fmaxf(MR, r.ml_m);
-            const float fa = (MR == -INFINITY) ? 0.0f : exp2f(MR - mn);
-            L = fa * L + exp2f(r.ml_m - mn) * r.l;
-            MR = mn;
+            for (int e = 0; e < 4; ++e) O[e] = fa * O[e] + fb * r.o[0][e];
+            L = fa * L + fb * r.l[0];
+            M = mn;
         }
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const RowInfo ri = row_info<G, 1>(4 * ag + e, x.b, x.g, 0, x.q_len, x.q_start, x.kv_len);
-        if (ri.token < 0) continue;
+    const RowInfo ri = row_info<G, 1>(ar, x.b, x.g, 0, x.q_len, x.q_start, x.kv_len);
+    if (ri.token >= 0) {
         const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)s_max + s;
-        ws_o[slot * D + 16 * wave + (lane & 15)] = O[e];
-    }
-    if (t < 256 && (t & 15) == 0) {
-        const RowInfo ri = row_info<G, 1>(t >> 4, x.b, x.g, 0, x.q_len, x.q_start, x.kv_len);
-        if (ri.token >= 0) {
-            const int64_t slot = (ri.token * Hq + ri.head) * (int64_t)s_max + s;
-            ws_ml[slot] = make_float2(MR, L);
-        }
+        *reinterpret_cast<f32x4*>(ws_o + slot * D + 16 * wave + 4 * ag) = O;
+        if (wave == 0 && ag == 0) ws_ml[slot] = make_float2(M, L);
     }
 }
 

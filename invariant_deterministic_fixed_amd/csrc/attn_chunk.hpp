@@ -11,6 +11,8 @@
 // fixed k-blocks, the max is exact, and l is summed in one fixed order; R only
 // decides how many rows share one load of the chunk's K and V.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace binv {
@@ -22,13 +24,33 @@ constexpr int NT = 256;
 constexpr int ROWS = 16;           // rows of one MFMA row tile
 constexpr int STACK = 10;          // binary counter slots: enough for 1023 leaves
 
-// p = 2^(s - m) of a score, s <= m: the hardware v_exp_f32 as it stands.
-// exp2f adds a range reduction that keeps results below 2^-126 (weights more
-// than 126 binary orders under the row's largest) as fp32 denormals, five
-// more vector instructions per score; every kernel that forms p (decode, the
-// prefill block and chunk paths, the tuned comparator) calls this one
-// function, so they agree bit for bit.
-__device__ __forceinline__ float exp2_score(float x) { return __builtin_amdgcn_exp2f(x); }
+// The softmax weights of a chunk, as every kernel that forms them (decode, the
+// prefill block and chunk paths, the tuned comparator) computes them, so they
+// agree bit for bit.  s is a raw score q.k, c = scale * log2(e); the row's
+// max in the log2 domain is m = c * max_j s_j (rounded once: since rounding
+// is monotonic this is the max of the rounded c s_j), and
+//   p = bf16(2^(fma(s, c, -m)))
+// with the hardware v_exp_f32 as it stands (exp2f adds a range reduction
+// that keeps results below 2^-126, weights more than 126 binary orders under
+// the row's largest, as fp32 denormals: five more instructions per score).
+// The fused form rounds s c - m once; for the row's largest score it can be a
+// few units of the last place above 0, which the bf16 rounding of p absorbs.
+__device__ __forceinline__ float p_of(float s, float c, float m) {
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(s, c, -m));
+}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two weights -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32), lo first
+__device__ __forceinline__ uint32_t p_pack(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+// l += p_lo + p_hi of a packed pair, by v_dot2c_f32_bf16 against (1, 1): the
+// sum of a row's weights in every kernel is this chain over its pairs in the
+// key order of the p.v products
+__device__ __forceinline__ float l_add(uint32_t pk, float acc) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), one, acc, false);
+}
 
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -42,9 +64,6 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// P tile in LDS: [16 R rows][256 keys] bf16, rows of 512 bytes = 32 chunks of
-// 16 bytes; chunk ch of row r is stored at position ch ^ (r & 31).
-__device__ __forceinline__ int p_off(int r, int ch) { return (r << 9) + ((ch ^ (r & 31)) << 4); }
 
 struct RowInfo {
     int64_t token;   // global query-token index (row of q / out / partials), -1 if padding
@@ -123,28 +142,41 @@ __device__ __forceinline__ TileCtx tile_ctx(int b, int g, int qt, const int32_t*
     return tile_ctx_len<G, R>(b, g, qt, cu_q, kv_lens[b], pt_stride, max_kv_len);
 }
 
-template <int D, int R, bool VL>
+// The order of the keys in the k-slots of a p.v product.  The scores are
+// formed transposed (S^T = K Q^T): in 16-key tile kt, lane (ag, ar) = (lane
+// >> 4, lane & 15) holds row ar's scores of keys 16 kt + 4 ag + e, e = 0..3.
+// The p.v products (O^T = V^T P^T) take the keys in 32-key blocks kb whose
+// k-slots 8 ag .. 8 ag + 7 hold keys 32 kb + 4 ag + (0..3) and then
+// 32 kb + 16 + 4 ag + (0..3): exactly the p values lane (ag, ar) computed in
+// tiles 2 kb and 2 kb + 1, so p reaches the matrix cores without changing
+// lanes.  Every kernel (chunk, block, comparator) uses this order; the sum l
+// of a row's p is taken in the same order too: per lane group sequentially
+// over kb ascending and then the 8 slots ascending, and the four group sums
+// as (g0 + g1) + (g2 + g3).
+
+template <int D, int R>
 struct ChunkLds {
-    // with VL: the chunk's 16 V page blocks of this KV head, [page][D][16 slots]
-    // bf16, copied HBM -> LDS by global_load_lds (one 1 KB piece per instruction)
-    __attribute__((aligned(1024))) char v[VL ? 16 * D * PAGE * 2 : 16];
-    __attribute__((aligned(16))) char p[ROWS * R * CHUNK * 2];
+    // the chunk's 16 V page blocks of this KV head, [page][D][16 slots] bf16
+    // with the 16-byte half h of feature d at h ^ ((d >> 3) & 1) (v_src),
+    // copied HBM -> LDS by global_load_lds (one 1 KB piece per instruction)
+    __attribute__((aligned(1024))) char v[16 * D * PAGE * 2];
+    // p as p.v operand: [row tile][32-key block][lane] 16 bytes each
+    __attribute__((aligned(16))) char p[R * 8 * 64 * 16];
     float red_max[ChunkShape<D>::NW][ROWS * R];
     // q fragments of the tile for a workgroup that loops over chunks (its rows
     // do not change): [row tile][k-step][lane] 16 bytes each
     __attribute__((aligned(16))) char qf[R * ChunkShape<D>::KS * 64 * 16];
 };
 
-// Result of one chunk for the workgroup's 16R rows:
-//   m[rt][e]  max of row 16 rt + 4*(lane>>4) + e (every lane), -inf if the row
-//             sees no key
-//   o[rt]     p.v of those rows for features 16*wave + (lane&15)
-//   l, ml_m   (threads t < 256R with t % 16 == 0) sum of p and max of row t >> 4
+// Result of one chunk for the workgroup's 16R rows; lane (ag, ar) of every
+// wave holds row 16 rt + ar:
+//   m[rt]  the row's max, -inf if the row sees no key
+//   l[rt]  the row's sum of p
+//   o[rt]  the row's p.v for features 16 wave + 4 ag + i, i = 0..3
 template <int R>
 struct ChunkOut {
-    float m[R][4];
+    float m[R], l[R];
     f32x4 o[R];
-    float l, ml_m;
 };
 
 // Page-table entries of the JT pages this wave reads in chunk c (independent
@@ -167,7 +199,7 @@ __device__ __forceinline__ void load_phys(const TileCtx& x, int c,
     }
 }
 
-// K fragments (B operand of q.k) of chunk c: page 16c + JT*wave + u, key slot
+// K fragments (A operand of q.k) of chunk c: page 16c + JT*wave + u, key slot
 // lane&15, features 32ks + 8(lane>>4) .. +8.  Pages past the sequence's last
 // one read page 0 of the cache instead (no branch around the loads): all
 // their keys are past every row's position and masked.
@@ -190,9 +222,9 @@ __device__ __forceinline__ void load_k(const TileCtx& x, int c, const int (&phys
 // q fragments of the workgroup's tile -> sh.qf (wave 0 loads and writes them;
 // the caller's barrier makes them visible).  A padding row reads the tile's
 // first token: every key is masked for it.
-template <int D, int G, int R, bool VL>
+template <int D, int G, int R>
 __device__ __forceinline__ void stage_q(const TileCtx& x, const bf16_t* __restrict__ q, int Hq,
-                                        ChunkLds<D, R, VL>& sh, int t) {
+                                        ChunkLds<D, R>& sh, int t) {
     constexpr int KS = ChunkShape<D>::KS;
     const int lane = t & 63, ar = lane & 15, ag = lane >> 4;
     if (t >= 64) return;
@@ -207,28 +239,74 @@ __device__ __forceinline__ void stage_q(const TileCtx& x, const bf16_t* __restri
     }
 }
 
-// The per-chunk arithmetic shared by decode, prefill and the comparator: keys
-// [256c, 256c+256) of the tile's sequence, each row limited to keys <= its
-// position.  LDS may be reused only after a __syncthreads().  t = threadIdx.x.
-// VL: V reaches the matrix cores through LDS (copied while q.k runs; decode)
-// or straight from memory into registers after q.k (prefill, where 16R rows
-// share each V fragment and LDS is better spent on more workgroups per CU).
-// Either way every lane feeds the same V values into the same p.v chain.
-// KPRE: kf already holds chunk c's K (requested by the previous chunk); once
-// this chunk's V is requested, chunk c_nx's K (c_nx >= 0) is requested into
-// kf, to arrive while this chunk's softmax and p.v run.  Without KPRE chunk
-// c's K is requested here.
-template <int D, int G, int R, bool VL, bool KPRE = false>
+// V page blocks in LDS: [D][16 slots] bf16 per page, the 16-byte half h of
+// feature d stored at position h ^ ((d >> 3) & 1).  With that swizzle the 8-byte
+// reads of v_frag from 16 consecutive features by four lane groups hit every
+// bank once per half wave (unswizzled, features 8 apart share banks).  v_src:
+// the source offset (bytes, within a page block) of the 16 bytes that
+// global_load_lds lane `lane` of copy `part` (1 KB) puts at part * 1024 + 16 lane.
+__device__ __forceinline__ int v_src(int part, int lane) {
+    const int d = 32 * part + (lane >> 1), h = lane & 1;
+    return d * (PAGE * 2) + ((h ^ ((d >> 3) & 1)) << 4);
+}
+
+// V^T fragment (A operand of p.v) from a [page][D][16 slots] block of LDS:
+// feature d, the 8 keys of 32-key block kb that lane group ag holds (pages
+// 2 kb and 2 kb + 1 of the chunk, slots 4 ag .. 4 ag + 3 of each); with
+// MASK, slots at or past the sequence end (chunk-relative key >= nvalid)
+// read as zero -- they may hold any bits, NaN included.  MASK is a template
+// argument: callers pick the masked loop once per chunk (only a sequence's
+// last chunk has such slots), so no fragment read waits behind a branch.
+// vlane = V block + d * 32 + 8 ag is formed once per lane (and kept opaque):
+// the fragments then differ from it by constants, which the reads carry in
+// their offset fields instead of one address register per fragment.
+typedef const __attribute__((address_space(3))) char* lds_cptr;
+__device__ __forceinline__ lds_cptr v_lane(const char* vbuf, int d, int ag) {
+    // slots 4 ag .. 4 ag + 3: half ag >> 1, swizzled, then 8 (ag & 1) bytes in
+    lds_cptr p = (lds_cptr)(vbuf + d * (PAGE * 2) + 8 * (ag ^ ((d >> 2) & 2)));
+    asm volatile("" : "+v"(p));
+    return p;
+}
+template <int D, bool MASK>
+__device__ __forceinline__ u32x4 v_frag(lds_cptr vlane, int kb, int ag, int nvalid) {
+    lds_cptr p0 = vlane + (2 * kb) * (D * PAGE * 2);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 a = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(p0);
+    const u32x2 b = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(p0 + D * PAGE * 2);
+    u32x4 v = u32x4{a.x, a.y, b.x, b.y};
+    if constexpr (MASK) {
+        // dword 2 h + i holds keys 32 kb + 16 h + 4 ag + 2 i, + 1
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int n = nvalid - (32 * kb + 16 * h + 4 * ag);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (2 * i + 1 >= n) v[2 * h + i] &= (2 * i < n) ? 0x0000ffffu : 0u;
+            }
+        }
+    }
+    return v;
+}
+
+// The per-chunk arithmetic shared by decode, short prefill runs and the
+// comparator: keys [256c, 256c+256) of the tile's sequence, each row limited
+// to keys <= its position.  LDS may be reused only after a __syncthreads().
+// t = threadIdx.x.  V reaches the matrix cores through LDS, copied while q.k
+// runs.  KPRE: kf already holds chunk c's K (requested by the previous
+// chunk); once this chunk's V is requested, chunk c_nx's K (c_nx >= 0) is
+// requested into kf, to arrive while this chunk's softmax and p.v run.
+// Without KPRE chunk c's K is requested here.
+template <int D, int G, int R, bool KPRE = false>
 __device__ __forceinline__ ChunkOut<R> chunk_compute(
     const TileCtx& x, int c, const int (&phys_in)[ChunkShape<D>::JT],
     const int32_t* __restrict__ page_table, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, int64_t pt_stride,
-    int Hq, int Hkv, float scale_log2, ChunkLds<D, R, VL>& sh, int t,
+    int Hq, int Hkv, float scale_log2, ChunkLds<D, R>& sh, int t,
     u32x4 (&kf)[ChunkShape<D>::JT][ChunkShape<D>::KS], int c_nx = -1,
     const int (&phys_nx)[ChunkShape<D>::JT] = {}) {
     using S = ChunkShape<D>;
     constexpr int NW = S::NW, JT = S::JT, KS = S::KS;
-    static_assert(S::NTH >= 256 * R, "one thread per (row, 16-key segment) for l");
+    static_assert(JT % 2 == 0, "a wave's pages form whole 32-key blocks");
     const int lane = t & 63, wave = t >> 6;
     const int ar = lane & 15, ag = lane >> 4;
     const int j0 = c * CHUNK;
@@ -237,15 +315,13 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
 
     // ---- this wave's JT pages; entries past the sequence's last page are not used
     int64_t phys[JT];
-    bool page_ok[JT];
 #pragma unroll
     for (int u = 0; u < JT; ++u) {
         const int pidx = 16 * c + JT * wave + u;
-        page_ok[u] = pidx < x.n_pages && pidx < pt_stride;
-        phys[u] = page_ok[u] ? (int64_t)phys_in[u] : 0;
+        phys[u] = (pidx < x.n_pages && pidx < pt_stride) ? (int64_t)phys_in[u] : 0;
     }
 
-    // ---- Q fragments (A operand) of each row tile: row 16 rt + (lane&15),
+    // ---- Q fragments (B operand) of each row tile: row 16 rt + (lane&15),
     // features 32ks + 8(lane>>4) .. +8.  A padding row (no token) reads the
     // tile's first token instead of branching around its load: every key is
     // masked for it (position -1), so its scores, p and partial are never
@@ -268,11 +344,11 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
                 qf[rt][ks] = ld16(q + (tok * Hq + a_row.head) * D + 32 * ks + 8 * ag);
         }
     }
-    // ---- K fragments (B operand of q.k)
+    // ---- K fragments (A operand of q.k)
     if constexpr (!KPRE) load_k<D>(x, c, phys_in, kc, pt_stride, Hkv, kf, t);
 
-
-    // ---- S = Q K^T on the matrix cores
+    // ---- S^T = K Q^T on the matrix cores: tile (rt, u) holds, in lane
+    // (ag, ar), row 16 rt + ar against keys 16 (JT wave + u) + 4 ag + e
     f32x4 s[R][JT];
 #pragma unroll
     for (int rt = 0; rt < R; ++rt)
@@ -280,32 +356,28 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
         for (int u = 0; u < JT; ++u) {
             s[rt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) s[rt][u] = mfma16x16x32(qf[rt][ks], kf[u][ks], s[rt][u]);
+            for (int ks = 0; ks < KS; ++ks) s[rt][u] = mfma16x16x32(kf[u][ks], qf[rt][ks], s[rt][u]);
         }
-    if constexpr (VL) {
 #pragma unroll
-        for (int rt = 0; rt < R; ++rt)
+    for (int rt = 0; rt < R; ++rt)
 #pragma unroll
-            for (int u = 0; u < JT; ++u) asm volatile("" : "+v"(s[rt][u]) : : "memory");
-    }
+        for (int u = 0; u < JT; ++u) asm volatile("" : "+v"(s[rt][u]) : : "memory");
     // ---- V page blocks of the same JT pages -> LDS (4 KB at D = 128, 2 KB at
     // D = 64, 1 KB per instruction), requested once the q.k products are
     // issued (the fence ties the scores to this point), so that q.k waits for
     // q and K only and V arrives while the scores are masked, reduced and
     // turned into p.  Pages past the sequence end copy page 0 of the cache;
     // all their slots are >= kv_len and are zeroed when read.
-    if constexpr (VL) {
 #pragma unroll
-        for (int u = 0; u < JT; ++u) {
-            const int pl = JT * wave + u;                      // page within the chunk
-            const char* src = reinterpret_cast<const char*>(vc + (phys[u] * Hkv + g) * (D * PAGE));
+    for (int u = 0; u < JT; ++u) {
+        const int pl = JT * wave + u;                      // page within the chunk
+        const char* src = reinterpret_cast<const char*>(vc + (phys[u] * Hkv + g) * (D * PAGE));
 #pragma unroll
-            for (int part = 0; part < D * PAGE * 2 / 1024; ++part)
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)(src + part * 1024 + 16 * lane),
-                    (__attribute__((address_space(3))) void*)(sh.v + pl * (D * PAGE * 2) + part * 1024),
-                    16, 0, 0);
-        }
+        for (int part = 0; part < D * PAGE * 2 / 1024; ++part)
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(src + v_src(part, lane)),
+                (__attribute__((address_space(3))) void*)(sh.v + pl * (D * PAGE * 2) + part * 1024),
+                16, 0, 0);
     }
     // ---- the next chunk's K, requested after this chunk's V (loads retire in
     // issue order: the wait for V below leaves these JT*KS loads in flight)
@@ -316,143 +388,88 @@ __device__ __forceinline__ ChunkOut<R> chunk_compute(
         if (kpre) load_k<D>(x, c_nx, phys_nx, kc, pt_stride, Hkv, kf, t);
     }
 
-    // ---- without VL: V fragments straight into registers, issued once the
-    // q.k products are queued: feature d = 16 wave + (lane&15), keys
-    // 32ks + 8(lane>>4) .. +8 = page 16c + 2ks + (ag>>1), slots 8(ag&1) .. +8
-    u32x4 vreg[VL ? 1 : 8];
-    if constexpr (!VL) {
-        const int d = 16 * wave + (lane & 15);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int pidx = 16 * c + 2 * ks + (ag >> 1);
-            const bool ok = pidx < x.n_pages && pidx < pt_stride;
-            const int64_t ph = ok ? (int64_t)page_table[x.pt_row + pidx] : 0;
-            vreg[ks] = ok ? ld16(vc + ((ph * Hkv + g) * D + d) * PAGE + 8 * (ag & 1))
-                          : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-
-    // lane holds rows 16 rt + 4*(lane>>4) + e, key j0 + 16*(JT*wave + u) + (lane&15)
-    const int key_lane = j0 + 16 * JT * wave + (lane & 15);
+    // ---- mask (key <= the row's position), row max of the raw scores: over
+    // the lane's keys, its row's four lane groups, then the waves (through LDS)
+    const int key_lane = j0 + 16 * JT * wave + 4 * ag;     // + 16 u + e
     ChunkOut<R> r;
 #pragma unroll
     for (int rt = 0; rt < R; ++rt) {
-        float mx[4];
+        const int rpos = row_info<G, R>(16 * rt + ar, x.b, g, x.qt, x.q_len, x.q_start, kv_len).pos;
+        float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int rpos = row_info<G, R>(16 * rt + 4 * ag + e, x.b, g, x.qt, x.q_len,
-                                            x.q_start, kv_len).pos;
-            mx[e] = -INFINITY;
+        for (int u = 0; u < JT; ++u)
 #pragma unroll
-            for (int u = 0; u < JT; ++u) {
-                const bool valid = key_lane + 16 * u <= rpos;
-                const float v = valid ? s[rt][u][e] * scale_log2 : -INFINITY;
+            for (int e = 0; e < 4; ++e) {
+                const bool valid = key_lane + 16 * u + e <= rpos;
+                const float v = valid ? s[rt][u][e] : -INFINITY;
                 s[rt][u][e] = v;
-                mx[e] = fmaxf(mx[e], v);
+                mx = fmaxf(mx, v);
             }
-            {
-                // max over the 16 lanes of the row group by DPP row rotations
-                // (max is exact, so the exchange order does not reach the bits)
-                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
-                                         0, __float_as_int(mx[e]), 0x121, 0xf, 0xf, false)));
-                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
-                                         0, __float_as_int(mx[e]), 0x122, 0xf, 0xf, false)));
-                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
-                                         0, __float_as_int(mx[e]), 0x124, 0xf, 0xf, false)));
-                mx[e] = fmaxf(mx[e], __int_as_float(__builtin_amdgcn_update_dpp(
-                                         0, __float_as_int(mx[e]), 0x128, 0xf, 0xf, false)));
-            }
-        }
-        if ((lane & 15) == 0) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sh.red_max[wave][16 * rt + 4 * ag + e] = mx[e];
-        }
+        // max is exact, so the exchange order does not reach the bits
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (ag == 0) sh.red_max[wave][16 * rt + ar] = mx;
     }
     lds_barrier();     // every wave's row maxima visible (V may still be in flight)
 #pragma unroll
+    for (int rt = 0; rt < R; ++rt) {
+        float mm = sh.red_max[0][16 * rt + ar];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) mm = fmaxf(mm, sh.red_max[w][16 * rt + ar]);
+        r.m[rt] = mm * scale_log2;
+    }
+
+    // ---- P = bf16(2^(s c - m)) into LDS as p.v operand: this wave's tiles
+    // 2 kb, 2 kb + 1 form block kb of the key order above
+#pragma unroll
     for (int rt = 0; rt < R; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * rt + 4 * ag + e;
-            float mm = sh.red_max[0][row];
+        for (int u2 = 0; u2 < JT / 2; ++u2) {
+            const int kb = (JT / 2) * wave + u2;
+            u32x4 pk;
 #pragma unroll
-            for (int w = 1; w < NW; ++w) mm = fmaxf(mm, sh.red_max[w][row]);
-            r.m[rt][e] = mm;
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    float pp[2];
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const float v = s[rt][2 * u2 + h][2 * i + k];
+                        pp[k] = (v == -INFINITY) ? 0.0f : p_of(v, scale_log2, r.m[rt]);
+                    }
+                    pk[2 * h + i] = p_pack(pp[0], pp[1]);
+                }
+            *reinterpret_cast<u32x4*>(sh.p + ((rt * 8 + kb) * 64 + lane) * 16) = pk;
         }
+    if (kpre)                                          // this wave's V copies landed
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(KPRE_LOADS) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();     // p and every wave's V pages visible
 
-    // ---- P = bf16(exp2(s - m)) into LDS
+    // ---- l of each row (key order above) and O^T = V^T P^T on the matrix
+    // cores, 32-key blocks ascending; the wave owns features 16 wave .. + 15
+    const lds_cptr vl = v_lane(sh.v, 16 * wave + ar, ag);
+    auto pv = [&](auto masked) {
 #pragma unroll
-    for (int rt = 0; rt < R; ++rt)
+        for (int rt = 0; rt < R; ++rt) {
+            r.o[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            float acc = 0.0f;
 #pragma unroll
-        for (int u = 0; u < JT; ++u) {
-            const int key = 16 * (JT * wave + u) + (lane & 15);       // key within the chunk
+            for (int kb = 0; kb < 8; ++kb) {
+                const u32x4 pb = *reinterpret_cast<const u32x4*>(sh.p + ((rt * 8 + kb) * 64 + lane) * 16);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float v = s[rt][u][e];
-                const float p = (v == -INFINITY) ? 0.0f : exp2_score(v - r.m[rt][e]);
-                const int row = 16 * rt + 4 * ag + e;
-                *reinterpret_cast<bf16_t*>(sh.p + p_off(row, key >> 3) + 2 * (key & 7)) =
-                    (bf16_t)f32_to_bf16_branch(p);
+                for (int i = 0; i < 4; ++i) acc = l_add(pb[i], acc);
+                const u32x4 v = v_frag<D, decltype(masked)::value>(vl, kb, ag, kv_len - j0);
+                r.o[rt] = mfma16x16x32(v, pb, r.o[rt]);
             }
+            acc += __shfl_xor(acc, 16);
+            acc += __shfl_xor(acc, 32);
+            r.l[rt] = acc;
         }
-    if constexpr (VL) {                                // this wave's V copies landed
-        if (kpre)
-            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(KPRE_LOADS) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    lds_barrier();     // p, and with VL every wave's V pages, visible
-
-    // ---- l (threads 0 .. 256R-1): thread t sums keys 16(t&15) .. +15 of row t>>4
-    // in key order, then a 4-level xor butterfly over the 16 segment sums of the row
-    r.l = 0.0f;
-    r.ml_m = -INFINITY;
-    if (t < 256 * R) {
-        const int row = t >> 4, seg = t & 15;
-        const u32x4 p0 = *reinterpret_cast<const u32x4*>(sh.p + p_off(row, 2 * seg));
-        const u32x4 p1 = *reinterpret_cast<const u32x4*>(sh.p + p_off(row, 2 * seg + 1));
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { acc += lo_bf16(p0[i]); acc += hi_bf16(p0[i]); }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { acc += lo_bf16(p1[i]); acc += hi_bf16(p1[i]); }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
-        r.l = acc;
-        float mm = sh.red_max[0][row];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) mm = fmaxf(mm, sh.red_max[w][row]);
-        r.ml_m = mm;
-    }
-
-    // ---- O = P V on the matrix cores, keys ascending; wave owns features 16 wave ..
-    // V fragment: feature d = 16 wave + (lane&15), keys 32ks + 8(lane>>4) .. +8,
-    // i.e. page 2ks + (ag>>1) of the chunk, slots 8(ag&1) .. +8; slots at or
-    // past kv_len read as 0.  Each V fragment serves all R row tiles.
-#pragma unroll
-    for (int rt = 0; rt < R; ++rt) r.o[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-        const int d = 16 * wave + (lane & 15);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int pl = 2 * ks + (ag >> 1);
-            u32x4 v;
-            if constexpr (VL)
-                v = *reinterpret_cast<const u32x4*>(sh.v + pl * (D * PAGE * 2) + d * (PAGE * 2) + 16 * (ag & 1));
-            else
-                v = vreg[ks];
-            const int nvalid = kv_len - ((16 * c + pl) * PAGE + 8 * (ag & 1));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (2 * i + 1 >= nvalid) v[i] &= (2 * i < nvalid) ? 0x0000ffffu : 0u;
-            }
-#pragma unroll
-            for (int rt = 0; rt < R; ++rt) {
-                const u32x4 pa = *reinterpret_cast<const u32x4*>(sh.p + p_off(16 * rt + ar, 4 * ks + ag));
-                r.o[rt] = mfma16x16x32(pa, v, r.o[rt]);
-            }
-        }
-    }
+    };
+    if (j0 + CHUNK > kv_len) pv(std::true_type{});
+    else pv(std::false_type{});
     return r;
 }
 
@@ -485,22 +502,19 @@ __device__ __forceinline__ Partial combine(const Partial& a, const Partial& b) {
     return r;
 }
 
-// the same combine on chunk results as a workgroup holds them: per lane the
-// o and m of its rows, per l-thread the row's l and max
+// the same combine on chunk results as a workgroup holds them (per lane one
+// row: its max, sum and four features)
 template <int R>
 __device__ __forceinline__ ChunkOut<R> combine_out(const ChunkOut<R>& a, const ChunkOut<R>& b) {
     ChunkOut<R> r;
 #pragma unroll
-    for (int rt = 0; rt < R; ++rt)
+    for (int rt = 0; rt < R; ++rt) {
+        float fa, fb;
+        combine_scale(a.m[rt], b.m[rt], r.m[rt], fa, fb);
+        r.l[rt] = combine_val(fa, a.l[rt], fb, b.l[rt]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float fa, fb;
-            combine_scale(a.m[rt][e], b.m[rt][e], r.m[rt][e], fa, fb);
-            r.o[rt][e] = combine_val(fa, a.o[rt][e], fb, b.o[rt][e]);
-        }
-    float fa, fb;
-    combine_scale(a.ml_m, b.ml_m, r.ml_m, fa, fb);
-    r.l = combine_val(fa, a.l, fb, b.l);
+        for (int e = 0; e < 4; ++e) r.o[rt][e] = combine_val(fa, a.o[rt][e], fb, b.o[rt][e]);
+    }
     return r;
 }
 
