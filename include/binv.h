@@ -156,9 +156,10 @@ int binv_gemm_bf16(const void* A, int64_t lda,
  *   binv_attn_prefill_workspace_bytes(B, T, max_q_len, max_kv_len, Hq, Hkv, D),
  *   which never exceeds binv_attn_workspace_bytes(T, Hq, D, max_kv_len).
  *   Prefill rows of long new-token runs (D = 128, a sequence with at least
- *   ceil(64 / (Hq / Hkv)) new tokens) keep only the merge tree's pending
- *   subtrees, at most floor(log2(ceil(max_kv_len / 256))) per row, so a
- *   single-sequence prefill needs T * Hq * that many * (D + 2) * 4 bytes; rows
+ *   ceil(64 / (Hq / Hkv)) new tokens) keep in memory only the merge tree's
+ *   pending subtrees of four or more chunks, max(1, floor(log2(ceil(
+ *   max_kv_len / 256))) - 1) per row, so a single-sequence prefill needs
+ *   T * Hq * that many * (D + 2) * 4 bytes; rows
  *   of short runs keep one partial per chunk, indexed per sequence when that
  *   is smaller than per token.  Both functions return 0 for arguments the
  *   entry points reject.

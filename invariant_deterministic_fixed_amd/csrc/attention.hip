@@ -401,13 +401,14 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
         copy_v(0, lane);
     }
 
-    // ---- the per-row stack of the counter's slots >= 1: level s of a row at
-    // ((token * st_stride + s - 1) * Hq + head); each lane stores and loads only
+    // ---- the per-row stack of the counter's slots >= 2 (slots 0 and 1 stay in
+    // registers): level s of a row at ((token * st_stride + s - 2) * Hq + head);
+    // each lane stores and loads only
     // the values it holds (features 16 f + 4 ag .. + 3 of row ar; the row's
     // (max, sum) by the lanes of group 0, passed to the others by shuffles)
     auto slot_of = [&](int ar, int s) -> int64_t {
         const RowInfo ri = row(ar);
-        return ri.token < 0 ? (int64_t)-1 : ((ri.token * st_stride + (s - 1)) * Hq + ri.head);
+        return ri.token < 0 ? (int64_t)-1 : ((ri.token * st_stride + (s - 2)) * Hq + ri.head);
     };
     auto stack_store = [&](int s, const PfNode& nd, int lane) {
         const int ar = lane & 15, ag = lane >> 4;
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     __builtin_amdgcn_s_waitcnt(WAIT_VM8);             // this wave's q and K copies landed
     lds_barrier();                                    // every wave's: q and K(0) in LDS
 
-    PfNode slot0;
+    PfNode slot0, slot1;
     unsigned count = 0;
 #pragma clang loop unroll(disable)
     for (int c = 0; c < nc; ++c) {
@@ -530,7 +531,14 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
             // key blocks outer, the 8 independent feature tiles inner (each
             // tile's chain still runs over kb ascending); the masked loop only
             // for the sequence's last chunk (block-uniform branch)
-            const lds_cptr vl = v_lane(vbuf, ar, ag);         // feature tile f at + 16 f * 32
+            // one opaque lane base per feature tile: the two halves of a
+            // fragment (pages 2 kb and 2 kb + 1) are then the nearest pair of
+            // reads from one base, and are read by one ds_read2st64_b64 into
+            // the fragment's registers (from a shared base the compiler pairs
+            // neighbouring feature tiles instead and moves the halves after)
+            lds_cptr vl[D / 16];
+#pragma unroll
+            for (int f = 0; f < D / 16; ++f) vl[f] = v_lane(vbuf, 16 * f + ar, ag);
             auto pv = [&](auto masked) {
 #pragma unroll
                 for (int f = 0; f < D / 16; ++f) leaf.o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -539,7 +547,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
 #pragma unroll
                     for (int f = 0; f < D / 16; ++f)
                         leaf.o[f] = mfma16x16x32(
-                            v_frag<D, decltype(masked)::value>(vl + f * (16 * PAGE * 2), kb, ag, kv_len - j0),
+                            v_frag<D, decltype(masked)::value>(vl[f], kb, ag, kv_len - j0),
                             pb[kb], leaf.o[f]);
             };
             if (j0 + CHUNK > kv_len) pv(std::true_type{});
@@ -548,6 +556,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
         leaf.m = mx;
         leaf.l = acc;
         lds_barrier();                                    // every tile done with V(c)
+        if (more) copy_v(c + 1, lane);
 
         // ---- push the chunk into the binary counter: equal-size subtrees
         // merge, the older one on the left (uniform over the block)
@@ -555,24 +564,32 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
             slot0 = leaf;
         } else {
             PfNode carry = pf_combine(slot0, leaf);
-            int sl = 1;
+            if (!(count & 2u)) {
+                slot1 = carry;
+            } else {
+                carry = pf_combine(slot1, carry);
+                int sl = 2;
 #pragma clang loop unroll(disable)
-            while (count & (1u << sl)) {
-                carry = pf_combine(stack_load(sl, lane), carry);
-                ++sl;
+                while (count & (1u << sl)) {
+                    carry = pf_combine(stack_load(sl, lane), carry);
+                    ++sl;
+                }
+                stack_store(sl, carry, lane);
             }
-            stack_store(sl, carry, lane);
         }
         ++count;
-        if (more) copy_v(c + 1, lane);
     }
 
     // ---- the root: remaining subtrees, smallest (rightmost) first
     const int lane = lane_id(), ar = lane & 15, ag = lane >> 4;
     PfNode res = slot0;
     bool have = (count & 1u) != 0;
+    if (count & 2u) {
+        res = have ? pf_combine(slot1, res) : slot1;
+        have = true;
+    }
 #pragma clang loop unroll(disable)
-    for (int sl = 1; (count >> sl) != 0; ++sl) {
+    for (int sl = 2; (count >> sl) != 0; ++sl) {
         if (count & (1u << sl)) {
             if (!have) { res = stack_load(sl, lane); have = true; }
             else res = pf_combine(stack_load(sl, lane), res);
@@ -748,7 +765,8 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
 // partial of one chunk or subtree: D floats of o in the o region, (max, sum)
 // in the float2 region after it.
 //   * Leaves (chunk kernel -> merge kernel): [leaf row][chunk][head].
-//   * Block-kernel stacks: [token][level - 1][head], st_stride slots a token.
+//   * Block-kernel stacks: [token][level - 2][head], st_stride slots a token
+//     (the counter's levels 0 and 1 stay in registers).
 // When every leaf row is a token (leaf_seq = 0), the stacks live in the leaf
 // region with st_stride = the chunk count (a token has leaves or a stack,
 // never both); otherwise the stacks come first, then the compact leaves.
@@ -775,9 +793,10 @@ Layout layout_of(int64_t B, int64_t n_tokens, int64_t max_q_len, int64_t max_kv_
     if (!prefill || D != 128 || max_q_len * G < PF_ROWS / 2) return L;
     L.block = true;
     L.q_split = (PF_ROWS / 2 + G - 1) / G;
-    // the counter's slots >= 1 that a row of C chunks can fill: levels 1 .. floor(log2 C)
+    // the counter's slots >= 2 that a row of C chunks can fill: levels
+    // 2 .. floor(log2 C) (at least one slot, so that the layout is never empty)
     int64_t levels = 1;
-    while ((int64_t)2 << levels <= C) ++levels;
+    while ((int64_t)4 << levels <= C) ++levels;
     // one sequence of q_split or more tokens: no leaves at all
     if (B == 1 && n_tokens >= L.q_split) {
         L.leaves = false;

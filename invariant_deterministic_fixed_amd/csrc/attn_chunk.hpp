@@ -481,11 +481,14 @@ struct Partial {
 // left-to-right combine of two partials (m in the log2 domain):
 //   m = max(ma, mb); fa = 2^(ma - m); fb = 2^(mb - m);
 //   l = fa la + fb lb; o = fa oa + fb ob   (one fmaf each, product fb x first)
-// Every combine of the merge tree, wherever it runs, is this function.
+// Every combine of the merge tree, wherever it runs, is this function.  The
+// powers of two use the hardware v_exp_f32 (exact at 0, giving 1, and 0 at
+// -inf, so merging with the identity (-inf, 0, 0) returns the other operand;
+// weights below 2^-126 flush to 0, far below what an fp32 sum can register).
 __device__ __forceinline__ void combine_scale(float ma, float mb, float& m, float& fa, float& fb) {
     m = fmaxf(ma, mb);
-    fa = exp2f(ma - m);
-    fb = exp2f(mb - m);
+    fa = __builtin_amdgcn_exp2f(ma - m);
+    fb = __builtin_amdgcn_exp2f(mb - m);
 }
 __device__ __forceinline__ float combine_val(float fa, float a, float fb, float b) {
     return fmaf(fa, a, fb * b);

@@ -153,13 +153,15 @@ def test_workspace_sizes():
 def test_prefill_workspace_sizes():
     f = binv.attn_prefill_workspace_bytes
     node = 32 * (128 + 2) * 4                      # one partial of every head of a token
-    # one long sequence: the pending subtrees only, floor(log2(chunks)) per row
-    assert f(1, 4096, 4096, 4096, 32, 8, 128) == 4096 * 4 * node
-    assert f(1, 4096, 4096, 32768, 32, 8, 128) == 4096 * 7 * node
+    # one long sequence: the pending subtrees above the two the kernel keeps in
+    # registers only, max(1, floor(log2(chunks)) - 1) per row
+    assert f(1, 4096, 4096, 4096, 32, 8, 128) == 4096 * 3 * node
+    assert f(1, 4096, 4096, 32768, 32, 8, 128) == 4096 * 6 * node
     assert f(1, 64, 64, 256, 32, 8, 128) == 64 * 1 * node
+    assert f(1, 64, 64, 1024, 32, 8, 128) == 64 * 1 * node
     # four long sequences: stacks per token plus leaves for at most 15 short
     # tokens per sequence (the block kernel takes runs of 16 or more at G = 4)
-    assert f(4, 4096, 1024, 4096, 32, 8, 128) == (4096 * 4 + 4 * 15 * 16) * node
+    assert f(4, 4096, 1024, 4096, 32, 8, 128) == (4096 * 3 + 4 * 15 * 16) * node
     # one prompt chunk among decode rows: leaves per token are smaller
     T = 512 + 63
     assert f(64, T, 512, 1024, 32, 8, 128) == binv.attn_workspace_bytes(T, 32, 128, 1024)
