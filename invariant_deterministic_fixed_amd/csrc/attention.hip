@@ -252,13 +252,19 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
 // the output).  The root o / l, bf16, is the merge kernel's last step; so a
 // prefill row equals the decode of the same position bit for bit.
 // LDS: K [16 pages][16 keys][128] with 16-byte chunk c of key k at c ^ (k & 15);
-// V [16 pages][128 features][16 slots] swizzled as in v_src; q [128 rows][128], 16-byte chunk c of
-// row r at c ^ (r & 15), for all chunks.  The K area is free once every tile
-// has its scores, and the next chunk's K is copied into it while the scores
-// become p and p.v runs; the next chunk's V is copied once p.v is done, while
-// the partial is merged and the next chunk's q.k runs.
+// V [16 pages][128 features][16 slots] swizzled as in v_src, the page blocks
+// PF_VPAGE = 4096 + 16 bytes apart: a V fragment's two halves (pages 2 kb and
+// 2 kb + 1) and the same slots of any two pages of a chunk then lie in
+// different banks (4096 bytes apart they share every bank, and the paired
+// read of a fragment's halves ran at half rate).  q stays in registers (its
+// four fragments per lane), which leaves LDS room for that spacing.  The K
+// area is free once every tile has its scores, and the next chunk's K is
+// copied into it while the scores become p and p.v runs; the next chunk's V
+// is copied once p.v is done, while the partial is merged and the next
+// chunk's q.k runs.
 constexpr int PF_WAVES = 8;
 constexpr int PF_ROWS = 16 * PF_WAVES;
+constexpr int PF_VPAGE = 128 * PAGE * 2 + 16;     // LDS bytes between V page blocks
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
 // 11:8; the other counters left at their no-wait maxima), given to the
 // compiler's own builtin so that its wait insertion knows they were done
@@ -301,13 +307,11 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     // the areas read while they are in flight
     struct PfLds {
         __attribute__((aligned(1024))) char k[16 * PAGE * D * 2];
-        __attribute__((aligned(1024))) char v[16 * D * PAGE * 2];
-        __attribute__((aligned(1024))) char q[PF_ROWS * D * 2];
+        __attribute__((aligned(1024))) char v[16 * PF_VPAGE];
     };
     __shared__ PfLds sh;
     char* const kbuf = sh.k;
     char* const vbuf = sh.v;
-    char* const qbuf = sh.q;
     // (the mask bounds the value for the compiler, which then can tell the K
     // and V areas' copies and reads apart and waits only for what a read needs)
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) & (PF_WAVES - 1);
@@ -330,27 +334,16 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
         return row_info<G, PF_WAVES>(16 * wave + r, b, g, qb, x.q_len, x.q_start, kv_len);
     };
 
-    // ---- the block's q rows HBM -> LDS (a row without a token copies the
-    // block's first token: every key is masked for it)
+    // ---- q fragments of this wave's tile, for every chunk: row 16 wave + ar,
+    // features 32 ks + 8 ag .. + 8 (a row without a token reads the block's
+    // first token: every key is masked for it)
+    u32x4 qf[KS];
     {
-        const int lane = lane_id();
-        const char* qsrc[4];
+        const int lane = lane_id(), ar = lane & 15, ag = lane >> 4;
+        const RowInfo ri = row(ar);
+        const int64_t tok = ri.token >= 0 ? ri.token : x.q_start;
 #pragma unroll
-        for (int part = 0; part < 4; ++part) {
-            // LDS position part*1024 + 16 lane: row 4 part + lane / 16 of the wave's
-            // tile, chunk lane & 15 holding feature chunk (lane & 15) ^ row
-            const int rr = 4 * part + (lane >> 4);
-            const RowInfo ri = row(rr);
-            const int64_t tok = ri.token >= 0 ? ri.token : x.q_start;
-            qsrc[part] = reinterpret_cast<const char*>(q + (tok * Hq + ri.head) * D) +
-                         (((lane & 15) ^ rr) << 4);
-        }
-#pragma unroll
-        for (int part = 0; part < 4; ++part)
-            __builtin_amdgcn_global_load_lds(
-                (const void*)qsrc[part],
-                (__attribute__((address_space(3))) void*)(qbuf + wave * (16 * D * 2) + part * 1024),
-                16, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = ld16(q + (tok * Hq + ri.head) * D + 32 * ks + 8 * ag);
     }
     // K or V pages 2 wave, 2 wave + 1 of chunk c, 8 copies of 1 KB per wave
     // (pages past the sequence copy page 0 of the cache: their keys are
@@ -391,7 +384,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
             for (int part = 0; part < 4; ++part)
                 __builtin_amdgcn_global_load_lds(
                     (const void*)(src[u] + v_src(part, lane)),
-                    (__attribute__((address_space(3))) void*)(vbuf + pl * (D * PAGE * 2) + part * 1024),
+                    (__attribute__((address_space(3))) void*)(vbuf + pl * PF_VPAGE + part * 1024),
                     16, 0, 0);
         }
     };
@@ -434,7 +427,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     };
 
     __builtin_amdgcn_s_waitcnt(WAIT_VM8);             // this wave's q and K copies landed
-    lds_barrier();                                    // every wave's: q and K(0) in LDS
+    lds_barrier();                                    // every wave's K(0) in LDS
 
     PfNode slot0, slot1;
     unsigned count = 0;
@@ -451,23 +444,21 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
         const int rpos = row(ar).pos;
 
         // ---- S^T = K Q^T: tile kt holds, in lane (ag, ar), row ar against
-        // keys 16 kt + 4 ag + e; q fragment: row 16 wave + ar, features
-        // 32 ks + 8 ag .. + 8; K fragment: key 16 kt + ar, the same features
+        // keys 16 kt + 4 ag + e; K fragment: key 16 kt + ar, features
+        // 32 ks + 8 ag .. + 8 (the q fragments' features)
         f32x4 sc[NKT];
         {
             // k-steps outer, the 16 independent tiles inner (each tile's
             // chain still runs over ks ascending)
-            const char* qrow = qbuf + (16 * wave + ar) * (D * 2);
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 qf = *reinterpret_cast<const u32x4*>(qrow + (((4 * ks + ag) ^ ar) << 4));
                 const int kofs = ar * (D * 2) + (((4 * ks + ag) ^ ar) << 4);
 #pragma unroll
                 for (int kt = 0; kt < NKT; ++kt) {
                     const u32x4 kf = *reinterpret_cast<const u32x4*>(kbuf + kt * (16 * D * 2) + kofs);
-                    sc[kt] = mfma16x16x32(kf, qf, sc[kt]);
+                    sc[kt] = mfma16x16x32(kf, qf[ks], sc[kt]);
                 }
             }
         }
@@ -531,11 +522,9 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
             // key blocks outer, the 8 independent feature tiles inner (each
             // tile's chain still runs over kb ascending); the masked loop only
             // for the sequence's last chunk (block-uniform branch)
-            // one opaque lane base per feature tile: the two halves of a
-            // fragment (pages 2 kb and 2 kb + 1) are then the nearest pair of
-            // reads from one base, and are read by one ds_read2st64_b64 into
-            // the fragment's registers (from a shared base the compiler pairs
-            // neighbouring feature tiles instead and moves the halves after)
+            // one opaque lane base per feature tile (from a shared base the
+            // compiler would pair reads of neighbouring feature tiles into one
+            // instruction and move the halves into place after)
             lds_cptr vl[D / 16];
 #pragma unroll
             for (int f = 0; f < D / 16; ++f) vl[f] = v_lane(vbuf, 16 * f + ar, ag);
@@ -547,7 +536,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
 #pragma unroll
                     for (int f = 0; f < D / 16; ++f)
                         leaf.o[f] = mfma16x16x32(
-                            v_frag<D, decltype(masked)::value>(vl[f], kb, ag, kv_len - j0),
+                            v_frag<D, decltype(masked)::value, PF_VPAGE>(vl[f], kb, ag, kv_len - j0),
                             pb[kb], leaf.o[f]);
             };
             if (j0 + CHUNK > kv_len) pv(std::true_type{});

@@ -267,12 +267,15 @@ __device__ __forceinline__ lds_cptr v_lane(const char* vbuf, int d, int ag) {
     asm volatile("" : "+v"(p));
     return p;
 }
-template <int D, bool MASK>
+// VP: the byte stride of the page blocks in LDS (D * 32, or more when the
+// blocks are spaced apart so that the same slot of different pages falls in
+// different banks).
+template <int D, bool MASK, int VP = D * PAGE * 2>
 __device__ __forceinline__ u32x4 v_frag(lds_cptr vlane, int kb, int ag, int nvalid) {
-    lds_cptr p0 = vlane + (2 * kb) * (D * PAGE * 2);
+    lds_cptr p0 = vlane + (2 * kb) * VP;
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 a = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(p0);
-    const u32x2 b = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(p0 + D * PAGE * 2);
+    const u32x2 b = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(p0 + VP);
     u32x4 v = u32x4{a.x, a.y, b.x, b.y};
     if constexpr (MASK) {
         // dword 2 h + i holds keys 32 kb + 16 h + 4 ag + 2 i, + 1
