@@ -523,43 +523,61 @@ def sweep(dev="cuda:0"):
         torch.cuda.empty_cache()
 
     # 8B-class decoder: decode tokens/s at batch B with 1024-token contexts, all
-    # invariant, all tuned, and one locked request among tuned neighbours
+    # invariant, all tuned, and one locked request among tuned neighbours; each
+    # step replayed as a HIP graph (the serving configuration) and issued
+    # eagerly (every kernel launched from Python).  The invariant products of
+    # up to 16 rows read strip-packed weights (same bits as row-major)
     cfg = dec.CONFIG5
     w = dec.random_weights(cfg, 5, dev)
+    packed = dec.pack_weights(w)
     for B in [1, 16, 64]:
         res = {}
         for mode in ("invariant", "tuned", "locked"):
             if mode == "locked" and B == 1:
                 continue
-            pool = dec.KVPool(cfg, num_pages=B * (1024 + 64) // 16 + B, max_seqs=B,
-                              max_len=1024 + 64, seed=11, device=dev)
-            d = dec.Decoder(w, cfg, pool, max_tokens=max(1024, B), max_seqs=B,
-                            max_kv_len=1024 + 64, tuned=(mode == "tuned"))
-            r = np.random.default_rng(42)
-            slots = [pool.alloc() for _ in range(B)]
-            prot = {slots[0]} if mode == "locked" else None
-            toks = {}
-            for sl in slots:                          # prefill, untimed
-                _, ids, _ = d.step([(sl, r.integers(0, cfg["vocab"], 1024).tolist(), 0)])
-                toks[sl] = int(ids[0, 0])
-            torch.cuda.synchronize()
-            steps = 8
-            t0 = time.perf_counter()
-            for k in range(steps):
-                _, ids, _ = d.step([(sl, [toks[sl]], 1024 + k) for sl in slots], protected=prot)
+            for graph in (True, False):
+                pool = dec.KVPool(cfg, num_pages=B * (1024 + 64) // 16 + B, max_seqs=B,
+                                  max_len=1024 + 64, seed=11, device=dev)
+                d = dec.Decoder(w, cfg, pool, max_tokens=max(1024, B), max_seqs=B,
+                                max_kv_len=1024 + 64, tuned=(mode == "tuned"),
+                                packed=None if mode == "tuned" else packed)
+                r = np.random.default_rng(42)
+                slots = [pool.alloc() for _ in range(B)]
+                prot = {slots[0]} if mode == "locked" else None
+                toks = {}
+                for sl in slots:                          # prefill, untimed
+                    _, ids, _ = d.step([(sl, r.integers(0, cfg["vocab"], 1024).tolist(), 0)])
+                    toks[sl] = int(ids[0, 0])
+                # one untimed decode step (the graph's capture)
+                _, ids, _ = d.step([(sl, [toks[sl]], 1024) for sl in slots], protected=prot,
+                                   graph=graph)
                 ids = ids.cpu()
                 for i, sl in enumerate(slots):
                     toks[sl] = int(ids[i, 0])
-            torch.cuda.synchronize()
-            res[mode] = B * steps / (time.perf_counter() - t0)
-            del d, pool
-            torch.cuda.empty_cache()
+                torch.cuda.synchronize()
+                steps = 8
+                t0 = time.perf_counter()
+                for k in range(steps):
+                    _, ids, _ = d.step([(sl, [toks[sl]], 1025 + k) for sl in slots],
+                                       protected=prot, graph=graph)
+                    ids = ids.cpu()
+                    for i, sl in enumerate(slots):
+                        toks[sl] = int(ids[i, 0])
+                torch.cuda.synchronize()
+                res[(mode, graph)] = B * steps / (time.perf_counter() - t0)
+                del d, pool
+                torch.cuda.empty_cache()
         emit(sweep="decoder_8b_decode", B=B, context=1024,
-             invariant_tokens_per_s=round(res["invariant"], 1),
-             tuned_tokens_per_s=round(res["tuned"], 1),
-             locked_one_tokens_per_s=round(res["locked"], 1) if "locked" in res else None,
-             slowdown_vs_tuned=round(res["tuned"] / res["invariant"], 3))
-    del w
+             invariant_tokens_per_s=round(res[("invariant", True)], 1),
+             tuned_tokens_per_s=round(res[("tuned", True)], 1),
+             locked_one_tokens_per_s=(round(res[("locked", True)], 1)
+                                      if ("locked", True) in res else None),
+             slowdown_vs_tuned=round(res[("tuned", True)] / res[("invariant", True)], 3),
+             eager_invariant_tokens_per_s=round(res[("invariant", False)], 1),
+             eager_tuned_tokens_per_s=round(res[("tuned", False)], 1),
+             eager_locked_one_tokens_per_s=(round(res[("locked", False)], 1)
+                                            if ("locked", False) in res else None))
+    del w, packed
     torch.cuda.empty_cache()
 
     # fp32-activation mitigation: six RMSNorm -> GEMM blocks at d = 4096 with

@@ -115,6 +115,32 @@ int binv_gemm_bf16(const void* A, int64_t lda,
                    void* C, int c_dt, int64_t ldc,
                    int64_t M, int64_t N, int64_t K, void* stream);
 
+/* Decode batches over pre-packed weights: the same GEMM (same bits as
+ * binv_gemm_bf16 for the same A and W, for every M it accepts) with W
+ * re-laid out once so that the weights of each 16-column strip of C are one
+ * contiguous run (at decode sizes a GEMM is a stream of the weights; a strip
+ * of a row-major W is 32 bytes of every row).  Same method citations as
+ * binv_gemm_bf16.
+ *
+ * Packed layout (bf16, binv_gemm_bf16_packed_bytes(N, K) bytes, 16-byte
+ * aligned, caller-owned): Wp[s][kb][c][kk] = W[32 kb + kk][16 s + c], zero
+ * where 32 kb + kk >= K or 16 s + c >= N; s < ceil(N / 16) strips, kb <
+ * 2 ceil(K / 64) k-blocks, c < 16, kk < 32.
+ *
+ * binv_gemm_bf16_pack: W bf16 [K, N] row-major (ldw) -> Wp, on `stream`.
+ *   Same K, N, ldw rules as binv_gemm_bf16.  K = 0 or N = 0 is a no-op.
+ * binv_gemm_bf16_packed: C [M, N] (c_dt, ldc) = A [M, K] (lda) x W, with W
+ *   given as Wp.  1 <= M <= 64 (else BINV_ERR_UNSUPPORTED; M = 0 is a no-op);
+ *   K and N as for binv_gemm_bf16, and Wp must have been packed for this K
+ *   and N.  C must not overlap A or Wp.
+ * binv_gemm_bf16_packed_bytes returns 0 for negative sizes. */
+size_t binv_gemm_bf16_packed_bytes(int64_t N, int64_t K);
+int binv_gemm_bf16_pack(const void* W, int64_t ldw, int64_t K, int64_t N, void* Wp,
+                        void* stream);
+int binv_gemm_bf16_packed(const void* A, int64_t lda, const void* Wp,
+                          void* C, int c_dt, int64_t ldc,
+                          int64_t M, int64_t N, int64_t K, void* stream);
+
 /* ------------------------------------------------------------------------
  * Paged KV cache layout used by both attention entry points.
  * (The pages describe a KV cache whose reduction length is cached plus new

@@ -39,6 +39,9 @@ def _declare(lib):
         "binv_rmsnorm_tuned": (ci, [vp, ci, i64, vp, ci, vp, ci, i64, i64, i64, f32, vp]),
         "binv_gemm_bf16": (ci, [vp, i64, vp, i64, vp, ci, i64, i64, i64, i64, vp]),
         "binv_gemm_bf16_tuned_workspace_bytes": (sz, [i64, i64, i64]),
+        "binv_gemm_bf16_packed_bytes": (sz, [i64, i64]),
+        "binv_gemm_bf16_pack": (ci, [vp, i64, i64, i64, vp, vp]),
+        "binv_gemm_bf16_packed": (ci, [vp, i64, vp, vp, ci, i64, i64, i64, i64, vp]),
         "binv_gemm_bf16_tuned": (ci, [vp, i64, vp, i64, vp, ci, i64, i64, i64, i64, vp, sz, vp]),
         "binv_attn_workspace_bytes": (sz, [i64, ci, ci, i64]),
         "binv_attn_prefill_workspace_bytes": (sz, [i64, i64, i64, i64, ci, ci, ci]),
@@ -159,6 +162,40 @@ def gemm(a, w, out=None, out_dtype=torch.bfloat16, tuned=False, workspace=None):
     else:
         _check(lib().binv_gemm_bf16(_ptr(a), lda, _ptr(w), ldw, _ptr(out), _dt(out), ldc, M, N,
                                     K, _stream(a)), "binv_gemm_bf16")
+    return out
+
+
+class PackedWeight:
+    """W [K, N] bf16 re-laid out per 16-column strip (binv_gemm_bf16_pack),
+    for gemm_packed; data is a flat device tensor of
+    binv_gemm_bf16_packed_bytes(N, K) bytes."""
+
+    def __init__(self, data, K, N):
+        self.data, self.K, self.N = data, K, N
+
+
+def gemm_pack(w):
+    _dev(w)
+    K, ldw = _rows(w)
+    N = w.shape[1]
+    assert w.dtype == torch.bfloat16
+    data = torch.empty(lib().binv_gemm_bf16_packed_bytes(N, K), dtype=torch.uint8,
+                       device=w.device)
+    _check(lib().binv_gemm_bf16_pack(_ptr(w), ldw, K, N, _ptr(data), _stream(w)),
+           "binv_gemm_bf16_pack")
+    return PackedWeight(data, K, N)
+
+
+def gemm_packed(a, wp, out=None, out_dtype=torch.bfloat16):
+    """a [M <= 64, K] bf16 times the packed weight wp: the bits of gemm(a, w)."""
+    _dev(a, wp.data, out)
+    M, lda = _rows(a)
+    assert a.shape[1] == wp.K and a.dtype == torch.bfloat16
+    if out is None:
+        out = torch.empty((M, wp.N), dtype=out_dtype, device=a.device)
+    _, ldc = _rows(out)
+    _check(lib().binv_gemm_bf16_packed(_ptr(a), lda, _ptr(wp.data), _ptr(out), _dt(out), ldc, M,
+                                       wp.N, wp.K, _stream(a)), "binv_gemm_bf16_packed")
     return out
 
 

@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbinv.so")
-SOURCES = ["abi.cpp", "rmsnorm.hip", "gemm.hip", "attention.hip", "attention_tuned.hip", "glue.hip"]
+SOURCES = ["abi.cpp", "rmsnorm.hip", "gemm.hip", "gemm_packed.hip", "attention.hip",
+           "attention_tuned.hip", "glue.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-fno-fast-math", "-Wall", "-Wno-unused-function",

@@ -119,6 +119,35 @@ int binv_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void*
                                        (int)K, (hipStream_t)stream));
 }
 
+size_t binv_gemm_bf16_packed_bytes(int64_t N, int64_t K) {
+    if (N < 0 || K < 0) return 0;
+    return binv::gemm_packed_bytes(N, K);
+}
+
+int binv_gemm_bf16_pack(const void* W, int64_t ldw, int64_t K, int64_t N, void* Wp,
+                        void* stream) {
+    if (K < 0 || N < 0) return BINV_ERR_INVALID_ARG;
+    if (K == 0 || N == 0) return BINV_OK;
+    if (!W || !Wp || !aligned16(W) || !aligned16(Wp)) return BINV_ERR_INVALID_ARG;
+    if (!ld_ok(ldw, BINV_BF16) || ldw < N) return BINV_ERR_INVALID_ARG;
+    if (K % 8 != 0 || N % 8 != 0) return BINV_ERR_UNSUPPORTED;
+    if (N > I32MAX || K > I32MAX || ldw >= 16000000) return BINV_ERR_UNSUPPORTED;
+    return status_of(binv::launch_gemm_pack(W, ldw, (int)K, (int)N, Wp, (hipStream_t)stream));
+}
+
+int binv_gemm_bf16_packed(const void* A, int64_t lda, const void* Wp, void* C, int c_dt,
+                          int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+    // the plain entry point's checks, with the packed array standing in for W
+    // (its leading dimension is not used: pass N, once N is known to be valid)
+    if (M < 0 || N < 0 || K < 0) return BINV_ERR_INVALID_ARG;
+    if (M > 0 && N % 8 != 0) return BINV_ERR_UNSUPPORTED;
+    const int st = check_gemm(A, lda, Wp, N, C, c_dt, ldc, M, N, K);
+    if (st != BINV_OK || M == 0 || N == 0) return st;
+    if (M > 64) return BINV_ERR_UNSUPPORTED;
+    return status_of(binv::launch_gemm_packed(A, lda, Wp, C, c_dt == BINV_F32, ldc, (int)M,
+                                              (int)N, (int)K, (hipStream_t)stream));
+}
+
 size_t binv_gemm_bf16_tuned_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K < 0) return 0;
     return binv::gemm_tuned_workspace_bytes(M, N, K);

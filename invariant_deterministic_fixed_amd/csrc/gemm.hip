@@ -299,6 +299,12 @@ __device__ __forceinline__ u32x2 ds_read_tr_b64(const char* p) {
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a) : "memory");
     return v;
 }
+__device__ __forceinline__ u32x4 ds_read_b128_asm(const char* p) {
+    u32x4 v;
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a) : "memory");
+    return v;
+}
 
 template <int FM, int FN, int NS>
 __global__ __launch_bounds__(64) void gemm_skinny_kernel(const bf16_t* __restrict__ A, int64_t lda,
@@ -449,7 +455,7 @@ hipError_t launch_skinny(const void* A, int64_t lda, const void* W, int64_t ldw,
 // past N (copies of rows k >= K and of columns n >= N read zero).
 // LDS layout per stage: A [16 RT][64] as in the big tile (chunk c of row r at
 // c ^ (r & 7)), W [64][16 FN] as in gemm_skinny_kernel (wpos).
-template <int FN, int RT, int R, int D>
+template <int FN, int RT, int R, int D, bool PK>
 __global__ __launch_bounds__(256) void gemm_strip_kernel(const bf16_t* __restrict__ A, int64_t lda,
                                                          const bf16_t* __restrict__ W, int64_t ldw,
                                                          void* __restrict__ C, int64_t ldc, int M,
@@ -481,6 +487,13 @@ __global__ __launch_bounds__(256) void gemm_strip_kernel(const bf16_t* __restric
     const int nr = (nk + KR - 1) / KR;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void*)A, (short)0, (int)((int64_t)M * lda * 2), RSRC_WORD3);
+    // packed weights (PK): the runs of this workgroup's strips, nkb k-blocks
+    // of 1 KB each, bounded at the last strip that holds columns < N
+    const int nkb = 2 * nk;
+    const int s0 = n0 / 16, sv = min(FN, (N + 15) / 16 - s0);
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(W) + (int64_t)s0 * nkb * 1024), (short)0,
+        PK ? sv * nkb * 1024 : 0, RSRC_WORD3);
     // this wave's first K-tile of round rd (copying waves only)
     const int cw = wave - CW0;
     auto first_kt = [&](int rd) { return KR * rd + PER * cw; };
@@ -500,6 +513,17 @@ __global__ __launch_bounds__(256) void gemm_strip_kernel(const bf16_t* __restric
             const int kk = k0 + 8 * c;
             const int off = (row < M && kk < K) ? (row * (int)lda + kk) * 2 : OOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(As + u * 1024), 16, off, 0, 0, 0);
+        }
+        if constexpr (PK) {
+            // packed weights: the K-tile of strip s0 + jj is the 2 KB at
+            // k-blocks 2 kt, 2 kt + 1 of that strip's run; strips past N lie
+            // past the buffer's bound and read zero
+#pragma unroll
+            for (int u = 0; u < PW; ++u) {
+                const int off = ((u >> 1) * nkb + 2 * kt + (u & 1)) * 1024 + lane * 16;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void*)(Ws + u * 1024), 16, off, 0, 0, 0);
+            }
+            return;
         }
         const int krows = min(BK, K - k0);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -533,6 +557,7 @@ __global__ __launch_bounds__(256) void gemm_strip_kernel(const bf16_t* __restric
     // fragments of one round, as the computing wave reads them from LDS
     struct Frags {
         u32x2 p0[KR][2][FN], p1[KR][2][FN];
+        u32x4 b[KR][2][FN];                           // packed weights: whole fragments
         u32x4 a[KR][2];
     };
     // read round rd's fragments (stages of K-tiles >= nk hold stale data that
@@ -554,6 +579,14 @@ __global__ __launch_bounds__(256) void gemm_strip_kernel(const bf16_t* __restric
                 const int k_lo = 32 * ks + 8 * g + (r >> 2), k_hi = k_lo + 4;
 #pragma unroll
                 for (int jj = 0; jj < FN; ++jj) {
+                    if constexpr (PK) {
+                        // packed: column r, k 8 g .. 8 g + 7 of the k-block
+                        // are the 16 bytes at r * 64 + g * 16
+                        const char* pb = Ws + jj * 2048 + ks * 1024 + r * 64 + g * 16;
+                        if constexpr (PIPE) f.b[j][ks][jj] = *reinterpret_cast<const u32x4*>(pb);
+                        else f.b[j][ks][jj] = ds_read_b128_asm(pb);
+                        continue;
+                    }
                     const int c = 2 * jj + ((r & 3) >> 1);
                     const char* plo = Ws + wpos(k_lo, c) + 8 * (r & 1);
                     const char* phi = Ws + wpos(k_hi, c) + 8 * (r & 1);
@@ -578,8 +611,12 @@ __global__ __launch_bounds__(256) void gemm_strip_kernel(const bf16_t* __restric
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                    for (int jj = 0; jj < FN; ++jj)
-                        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.p0[j][ks][jj]), "+v"(f.p1[j][ks][jj]) : : "memory");
+                    for (int jj = 0; jj < FN; ++jj) {
+                        if constexpr (PK)
+                            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.b[j][ks][jj]) : : "memory");
+                        else
+                            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.p0[j][ks][jj]), "+v"(f.p1[j][ks][jj]) : : "memory");
+                    }
         }
     };
     // MFMAs of round rd, K-tiles in order, each k-step in order
@@ -588,8 +625,9 @@ __global__ __launch_bounds__(256) void gemm_strip_kernel(const bf16_t* __restric
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int jj = 0; jj < FN; ++jj) {
-                const u32x4 bf = u32x4{f.p0[j][ks][jj][0], f.p0[j][ks][jj][1],
-                                       f.p1[j][ks][jj][0], f.p1[j][ks][jj][1]};
+                const u32x4 bf = PK ? f.b[j][ks][jj]
+                                    : u32x4{f.p0[j][ks][jj][0], f.p0[j][ks][jj][1],
+                                            f.p1[j][ks][jj][0], f.p1[j][ks][jj][1]};
                 acc[jj] = mfma16x16x32(f.a[j][ks], bf, acc[jj]);
             }
     };
@@ -658,13 +696,13 @@ __global__ __launch_bounds__(256) void gemm_strip_kernel(const bf16_t* __restric
     }
 }
 
-template <int FN, int RT, int R, int D>
+template <int FN, int RT, int R, int D, bool PK = false>
 hipError_t launch_strip(const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
                         int64_t ldc, int M, int N, int K, int c_f32, hipStream_t s) {
     const int strips = (N + 16 * FN - 1) / (16 * FN);
     constexpr int GS = (FN >= 8) ? 1 : 8 / FN;
     const int grid = (strips + 8 * GS - 1) / (8 * GS) * (8 * GS);
-    hipLaunchKernelGGL((gemm_strip_kernel<FN, RT, R, D>), dim3((unsigned)grid), dim3(256), 0, s,
+    hipLaunchKernelGGL((gemm_strip_kernel<FN, RT, R, D, PK>), dim3((unsigned)grid), dim3(256), 0, s,
                        (const bf16_t*)A, lda, (const bf16_t*)W, ldw, C, ldc, M, N, K, c_f32);
     return hipGetLastError();
 }
@@ -945,6 +983,25 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, v
         return launch_strip<1, 4, 3, 3>(A, lda, W, ldw, C, ldc, M, N, K, c_f32, s);
     }
     return hipErrorInvalidValue;        // not reached
+}
+
+// Decode batches over packed weights (binv_gemm_bf16_packed): the strip
+// kernel with each DMA one whole 1 KB k-block of one strip (no row pieces),
+// the B fragment one 16-byte LDS read.  The MFMA chain is the one above.
+hipError_t launch_gemm_strips_packed(const void* A, int64_t lda, const void* Wp, void* C,
+                                     int c_f32, int64_t ldc, int M, int N, int K, hipStream_t s) {
+    if (M == 0 || N == 0) return hipSuccess;
+    // Up to 16 rows one row tile: one-strip workgroups, with a ring of 6
+    // rounds (one workgroup per CU) up to 6144 columns, of 3 rounds (two per
+    // CU) beyond.  Up to 64 rows four row tiles, two strips per workgroup
+    // from 6144 columns on.
+    const int fn = (N / 32 >= 192) ? 2 : 1;
+    if (M <= 16) {
+        if (fn == 2) return launch_strip<1, 1, 3, 3, true>(A, lda, Wp, 0, C, ldc, M, N, K, c_f32, s);
+        return launch_strip<1, 1, 6, 6, true>(A, lda, Wp, 0, C, ldc, M, N, K, c_f32, s);
+    }
+    if (fn == 2) return launch_strip<2, 4, 3, 3, true>(A, lda, Wp, 0, C, ldc, M, N, K, c_f32, s);
+    return launch_strip<1, 4, 3, 3, true>(A, lda, Wp, 0, C, ldc, M, N, K, c_f32, s);
 }
 
 // Comparator: split-K whose split count is chosen from the number of output

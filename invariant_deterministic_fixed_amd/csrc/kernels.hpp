@@ -17,6 +17,12 @@ hipError_t launch_rmsnorm_tuned(const void* x, int x_bf16, int64_t ldx, const vo
 
 hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
                        int c_f32, int64_t ldc, int M, int N, int K, hipStream_t s);
+size_t gemm_packed_bytes(int64_t N, int64_t K);
+hipError_t launch_gemm_pack(const void* W, int64_t ldw, int K, int N, void* Wp, hipStream_t s);
+hipError_t launch_gemm_packed(const void* A, int64_t lda, const void* Wp, void* C, int c_f32,
+                              int64_t ldc, int M, int N, int K, hipStream_t s);
+hipError_t launch_gemm_strips_packed(const void* A, int64_t lda, const void* Wp, void* C,
+                                     int c_f32, int64_t ldc, int M, int N, int K, hipStream_t s);
 size_t gemm_tuned_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_tuned(const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
                              int c_f32, int64_t ldc, int M, int N, int K, void* ws,

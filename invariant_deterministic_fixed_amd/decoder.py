@@ -53,6 +53,17 @@ def random_weights(cfg, seed, device, std=0.02):
     return w
 
 
+def pack_weights(w):
+    """Strip-packed copies (binv_gemm_bf16_pack) of every projection and of the
+    LM head, keyed by the row-major tensor's id, for Decoder(packed=...):
+    invariant products of up to Decoder.PACKED_ROWS rows then read them, with
+    the bits of the row-major product (the packed entry point runs the same
+    per-element chain) at a higher weight stream rate, for one more copy of
+    those weights in HBM."""
+    ws = [w["lm_head"]] + [lw[n] for lw in w["layers"] for n in ("wqkv", "wo", "wgu", "wd")]
+    return {id(t): (t, B.gemm_pack(t)) for t in ws}
+
+
 class KVPool:
     """Per-layer paged K/V caches and one host page table shared by all layers.
 
@@ -128,10 +139,13 @@ class Decoder:
     run through the invariant RMSNorm and GEMM, every other row through the
     tuned comparators, and attention stays invariant for all.  A protected
     sequence's bits are then those of an all-invariant run; the others'
-    are not batch-invariant."""
+    are not batch-invariant.
+
+    packed: pack_weights(weights), or None for row-major weights only; the
+    bits are the same either way."""
 
     def __init__(self, weights, cfg, pool, max_tokens, max_seqs, max_kv_len, topk=20,
-                 tuned=False):
+                 tuned=False, packed=None):
         self.w, self.cfg, self.pool, self.topk, self.tuned = weights, cfg, pool, topk, tuned
         dev = pool.device
         H, Hq, Hkv, D, F = (cfg["hidden"], cfg["n_heads"], cfg["n_kv"], cfg["head_dim"],
@@ -153,8 +167,13 @@ class Decoder:
         self.xl = torch.empty((max_seqs, H), dtype=bf, device=dev)
         self.logits = torch.empty((max_seqs, cfg["vocab"]), dtype=torch.float32, device=dev)
         self.max_tokens, self.max_seqs = T, max_seqs
+        self._graphs = {}
+        self._packed = packed if packed is not None else {}
 
-    def step(self, items, protected=None, on_layer=None):
+    # at most this many rows go through the packed-weight products
+    PACKED_ROWS = 16
+
+    def step(self, items, protected=None, on_layer=None, graph=False):
         """items: list of (slot, new token ids, start position).  Returns
         (logits fp32 [n, V], top ids int32 [n, k], top values fp32 [n, k]) for
         the last token of each item, as device tensors, in item order.
@@ -164,17 +183,38 @@ class Decoder:
         layer count, after the last layer -- for tests that check one layer at
         a time.  After the call, self.hl / self.xl hold the last tokens'
         residual rows and their final-norm output (bf16), rows in item order
-        unless `protected` reordered them."""
-        cfg, pool, dev = self.cfg, self.pool, self.pool.device
-        order = None
+        unless `protected` reordered them.
+        graph: run a decode step (one new token per item) as a HIP graph: the
+        step's kernels are captured once per batch signature (sequence count,
+        locked rows) and replayed with the step's inputs copied into the
+        graph's own input buffer; the same kernels with the same arguments,
+        so the same bits as the eager step, without the per-launch host work.
+        The returned tensors then belong to the graph and are overwritten by
+        its next replay."""
+        prep = self._prepare(items, protected)
+        if graph and on_layer is None and prep["max_q"] == 1:
+            out = self._replay(prep)
+        else:
+            dv = torch.from_numpy(prep["host"]).to(self.pool.device)
+            out = self._launch(dv, prep, on_layer)
+        order = prep["order"]
+        if order is not None:                     # back to the caller's item order
+            inv = torch.as_tensor(np.argsort(order), device=self.pool.device)
+            return tuple(t[inv] for t in out)
+        return out
+
+    def _prepare(self, items, protected):
+        """Host side of a step: page allocation and the step's int32 inputs
+        (token ids, token -> sequence, positions, cu, KV lengths, last-token
+        rows, page-table rows) as one array."""
+        pool = self.pool
+        order, n_prot, t_prot = None, 0, 0
         if protected is not None:
             # protected sequences first, so their rows form one leading block
             order = sorted(range(len(items)), key=lambda i: items[i][0] not in protected)
             items = [items[i] for i in order]
             n_prot = sum(1 for slot, _, _ in items if slot in protected)
             t_prot = sum(len(t) for _, t, _ in items[:n_prot])
-        H, Hq, Hkv, D, F = (cfg["hidden"], cfg["n_heads"], cfg["n_kv"], cfg["head_dim"],
-                            cfg["ffn"])
         # sequence b of this step reads row b of the step's page table: the
         # attention entry points and the KV write both address pages by the
         # sequence's index in the call, not by its pool slot
@@ -192,19 +232,27 @@ class Decoder:
         rows = pool.table[[slot for slot, _, _ in items]]
         host = np.concatenate([np.array(ids + tseq + tpos + cu + lens + [c - 1 for c in cu[1:]],
                                         dtype=np.int32), rows.reshape(-1)])
-        dv = torch.from_numpy(host).to(dev)
+        return dict(host=host, T=T, nb=nb, max_q=max(len(t) for _, t, _ in items),
+                    order=order, locked=protected is not None, n_prot=n_prot, t_prot=t_prot)
+
+    def _launch(self, dv, prep, on_layer=None):
+        """Every kernel of a step, on the current stream, reading the step's
+        inputs from the device array dv (laid out as _prepare's host array)."""
+        cfg, pool = self.cfg, self.pool
+        T, nb, max_q = prep["T"], prep["nb"], prep["max_q"]
+        locked, n_prot, t_prot = prep["locked"], prep["n_prot"], prep["t_prot"]
+        H, Hq, Hkv, D, F = (cfg["hidden"], cfg["n_heads"], cfg["n_kv"], cfg["head_dim"],
+                            cfg["ffn"])
         ids_d, tseq_d, tpos_d = dv[:T], dv[T:2 * T], dv[2 * T:3 * T]
         cu_d = dv[3 * T:3 * T + nb + 1]
         lens_d = dv[3 * T + nb + 1:3 * T + 2 * nb + 1]
         last_d = dv[3 * T + 2 * nb + 1:3 * T + 3 * nb + 1]
         table = dv[3 * T + 3 * nb + 1:].view(nb, pool.pps)
-        max_q = max(len(t) for _, t, _ in items)
         h, x, qkv, q, a, o, gu, s = (t[:T] for t in (self.h, self.x, self.qkv, self.q, self.a,
                                                      self.o, self.gu, self.s))
         scale = 1.0 / math.sqrt(D)
         tn = self.tuned
         decode_only = tn and max_q == 1
-        locked = protected is not None
 
         def split(n_lead):
             # (rows, tuned) blocks: leading protected rows invariant, the rest tuned
@@ -221,8 +269,12 @@ class Decoder:
                     B.rmsnorm(src[sl], self.w["norm"], cfg["eps"], out=dst[sl], tuned=t)
 
         def mm(src, wt, dst, blocks):
+            pk = self._packed.get(id(wt))
             for sl, t in blocks:
-                if src[sl].shape[0]:
+                n = src[sl].shape[0]
+                if n and pk is not None and not t and n <= self.PACKED_ROWS:
+                    B.gemm_packed(src[sl], pk[1], out=dst[sl])
+                elif n:
                     B.gemm(src[sl], wt, out=dst[sl], tuned=t)
 
         B.embed(ids_d, self.w["embed"], out=h)
@@ -254,7 +306,33 @@ class Decoder:
         norm(hl, xl, rows_seq)
         mm(xl, self.w["lm_head"], logits, rows_seq)
         top_ids, top_vals = B.topk(logits, self.topk)
-        if order is not None:                     # back to the caller's item order
-            inv = torch.as_tensor(np.argsort(order), device=dev)
-            return logits[inv], top_ids[inv], top_vals[inv]
         return logits, top_ids, top_vals
+
+    def _replay(self, prep):
+        """A decode step as a HIP graph: captured on the first step of its
+        signature (sequence count and locked block; the inputs' layout then
+        has a fixed size), replayed after the step's inputs are copied into
+        the graph's input array."""
+        key = (prep["nb"], prep["locked"], prep["n_prot"], prep["t_prot"])
+        host = torch.from_numpy(prep["host"])
+        g = self._graphs.get(key)
+        if g is None:
+            dv = torch.empty(host.shape, dtype=torch.int32, device=self.pool.device)
+            dv.copy_(host)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):             # one eager run first (lazy set-up)
+                self._launch(dv, prep)
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                outs = self._launch(dv, prep)
+            g = self._graphs[key] = (graph, dv, outs,
+                                     torch.empty(host.shape, dtype=torch.int32).pin_memory())
+        graph, dv, outs, pinned = g
+        # the previous replay has read the pinned array before it is refilled
+        torch.cuda.current_stream().synchronize()
+        pinned.copy_(host)
+        dv.copy_(pinned, non_blocking=True)
+        graph.replay()
+        return outs

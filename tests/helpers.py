@@ -27,6 +27,8 @@ def bits(t):
         return t.view(torch.int16).numpy()
     if t.dtype == torch.float32:
         return t.view(torch.int32).numpy()
+    if t.dtype in (torch.int32, torch.int64):
+        return t.numpy()
     raise TypeError(t.dtype)
 
 

@@ -78,6 +78,27 @@ def test_gemm_validation():
     assert g(FAKE, 4096, FAKE, 4096, FAKE, 1, 4096, 1, 4096, 4096, L, 0, L) == WORKSPACE
 
 
+def test_gemm_packed_validation_and_size():
+    size = _lib().binv_gemm_bf16_packed_bytes
+    # ceil(N / 16) strips x 2 ceil(K / 64) k-blocks x 1 KB
+    assert size(4096, 4096) == 256 * 128 * 1024
+    assert size(200, 72) == 13 * 4 * 1024
+    assert size(8, 0) == 0 and size(-1, 8) == 0
+    pack = _lib().binv_gemm_bf16_pack
+    assert pack(L, 8, 0, 8, L, L) == OK                                   # K = 0
+    assert pack(L, 8, 8, 8, L, L) == INVALID                              # nulls
+    assert pack(FAKE, 8, 8, 16, FAKE, L) == INVALID                       # ldw < N
+    assert pack(FAKE, 16, 12, 16, FAKE, L) == UNSUPPORTED                 # K % 8
+    assert pack(FAKE + 2, 8, 8, 8, FAKE, L) == INVALID                    # misaligned W
+    f = _lib().binv_gemm_bf16_packed
+    assert f(L, 8, L, L, 1, 8, 0, 8, 8, L) == OK                          # M = 0
+    assert f(L, 8, L, L, 1, 8, 4, 8, 8, L) == INVALID                     # nulls
+    assert f(FAKE, 4096, FAKE, FAKE, 1, 4096, 65, 4096, 4096, L) == UNSUPPORTED   # M > 64
+    assert f(FAKE, 16, FAKE, FAKE, 1, 16, 4, 12, 16, L) == UNSUPPORTED    # N % 8
+    assert f(FAKE, 8, FAKE, FAKE, 1, 8, 4, 8, 12, L) == INVALID           # lda < K
+    assert f(FAKE, 8, FAKE + 8, FAKE, 1, 8, 4, 8, 8, L) == INVALID        # misaligned Wp
+
+
 def _dec(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, pt=FAKE, pts=4, kl=FAKE, out=FAKE, B=2, maxl=64, Hq=8,
              Hkv=2, D=128, page=16, scale=0.1, ws=FAKE, wsb=1 << 30, s=L)

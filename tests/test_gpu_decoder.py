@@ -181,6 +181,99 @@ def test_small_decoder_invariance_with_neighbours(small):
         assert harness.same_bits(got, alone), f"trial {trial}: {n} neighbours, budget {budget}"
 
 
+def test_small_decoder_graph_steps_equal_eager(small):
+    # decode steps replayed as HIP graphs give the eager steps' bits: two
+    # decoders with the same weights and pool seeds, one stepping eagerly, one
+    # through graphs; replays of one graph with fresh inputs, eager work and
+    # synchronisations between replays, a locked block (its own graph) and a
+    # smaller batch (another graph)
+    w, _, _, _ = small
+
+    def make():
+        pool = dec.KVPool(SMALL, num_pages=512, max_seqs=8, max_len=512, seed=21, device=DEV)
+        return pool, dec.Decoder(w, SMALL, pool, max_tokens=512, max_seqs=8, max_kv_len=512)
+
+    (p1, d1), (p2, d2) = make(), make()
+    r = np.random.default_rng(31)
+    prompts = [r.integers(0, SMALL["vocab"], n).tolist() for n in (40, 75, 120)]
+    slots = [p1.alloc() for _ in prompts]
+    assert [p2.alloc() for _ in prompts] == slots
+    toks = []
+    for sl, pr in zip(slots, prompts):
+        lg1, id1, _ = d1.step([(sl, pr, 0)])
+        lg2, _, _ = d2.step([(sl, pr, 0)])
+        assert_bitwise_equal(lg2, lg1, "prefill")
+        toks.append(int(id1[0, 0]))
+    pos = [len(p) for p in prompts]
+    replays = 0
+    for k in range(8):
+        live = [0, 1, 2] if k < 6 else [0, 2]
+        prot = {slots[1]} if k in (3, 4) else None
+        items = [(slots[i], [toks[i]], pos[i]) for i in live]
+        eager = d1.step(items, protected=prot)
+        graphed = d2.step(items, protected=prot, graph=True)
+        for name, x, y in zip(("logits", "top ids", "top values"), graphed, eager):
+            assert_bitwise_equal(x, y, f"step {k} {name}")
+        replays += 1
+        ids = eager[1][:, 0].cpu()
+        for j, i in enumerate(live):
+            toks[i] = int(ids[j])
+            pos[i] += 1
+        if k == 1:
+            # eager work between replays: sequence 0 alone, one token, on both
+            e1 = d1.step([(slots[0], [toks[0]], pos[0])])
+            e2 = d2.step([(slots[0], [toks[0]], pos[0])])
+            assert_bitwise_equal(e2[0], e1[0], "eager step between replays")
+            torch.cuda.synchronize()
+            toks[0] = int(e1[1][0, 0])
+            pos[0] += 1
+    assert len(d2._graphs) == 3          # three sequences, locked block, two sequences
+    for sl in slots:
+        p1.release(sl)
+        p2.release(sl)
+
+
+def test_small_decoder_packed_weights_equal_row_major(small):
+    # a decoder reading strip-packed weights for its decode-size products gives
+    # the bits of one reading the row-major weights: prompts (products of 40 to
+    # 120 rows, row-major on both), then decode steps of 1, 3 and 16 rows, the
+    # last also with a locked block
+    w, _, _, _ = small
+    packed = dec.pack_weights(w)
+
+    def make(pk):
+        pool = dec.KVPool(SMALL, num_pages=1024, max_seqs=16, max_len=512, seed=23, device=DEV)
+        return pool, dec.Decoder(w, SMALL, pool, max_tokens=1024, max_seqs=16, max_kv_len=512,
+                                 packed=pk)
+
+    (p1, d1), (p2, d2) = make(None), make(packed)
+    r = np.random.default_rng(37)
+    prompts = [r.integers(0, SMALL["vocab"], int(n)).tolist() for n in r.integers(20, 121, 16)]
+    slots = [p1.alloc() for _ in prompts]
+    assert [p2.alloc() for _ in prompts] == slots
+    toks = []
+    for sl, pr in zip(slots, prompts):
+        lg1, id1, _ = d1.step([(sl, pr, 0)])
+        lg2, _, _ = d2.step([(sl, pr, 0)])
+        assert_bitwise_equal(lg2, lg1, "prefill")
+        toks.append(int(id1[0, 0]))
+    pos = [len(p) for p in prompts]
+    for k, live in enumerate([[0], [0, 5, 9], list(range(16)), list(range(16))]):
+        prot = {slots[3], slots[7]} if k == 3 else None
+        items = [(slots[i], [toks[i]], pos[i]) for i in live]
+        a = d1.step(items, protected=prot)
+        b = d2.step(items, protected=prot)
+        for name, x, y in zip(("logits", "top ids", "top values"), b, a):
+            assert_bitwise_equal(x, y, f"step {k} ({len(live)} rows) {name}")
+        ids = a[1][:, 0].cpu()
+        for j, i in enumerate(live):
+            toks[i] = int(ids[j])
+            pos[i] += 1
+    for sl in slots:
+        p1.release(sl)
+        p2.release(sl)
+
+
 @pytest.fixture(scope="module")
 def full():
     cfg = dec.CONFIG5
@@ -190,7 +283,10 @@ def full():
     # 32768 pages = 524288 tokens = 64 GB of bf16 K/V over 32 layers: room for a
     # 2048-token prefill budget over 200 steps plus 255 decoding neighbours
     pool = dec.KVPool(cfg, num_pages=32768, max_seqs=260, max_len=max_len, seed=11, device=DEV)
-    d = dec.Decoder(w, cfg, pool, max_tokens=2048 + 260 + 64, max_seqs=260, max_kv_len=max_len)
+    # packed weights: the target's decode products alone (one row) read the
+    # strip-packed copies, with 255 neighbours (256 rows) the row-major ones
+    d = dec.Decoder(w, cfg, pool, max_tokens=2048 + 260 + 64, max_seqs=260, max_kv_len=max_len,
+                    packed=dec.pack_weights(w))
     yield cfg, pool, d
     del d, pool, w
     torch.cuda.empty_cache()

@@ -132,6 +132,45 @@ def test_kernels_chosen_by_shape_agree_bitwise(N, K):
         assert_bitwise_equal(binv.gemm(Ad[:M], W), ref16[:M], f"bf16 M={M}")
 
 
+@pytest.mark.parametrize("N,K", [(4096, 4096), (6144, 4096), (4096, 14336), (200, 72),
+                                 (1000, 4104), (24, 8)])
+def test_packed_weights_give_the_plain_entry_points_bits(N, K):
+    # decode batches over weights packed per 16-column strip: every row equals
+    # binv_gemm_bf16's bitwise (bf16 and fp32 out) for M over 1..64, with N and
+    # K that leave partial strips and a partial 64-wide K-tile
+    A = synth.normal((64, K), 1.0, 41, DEV)
+    W = synth.normal((K, N), 0.02, 42, DEV)
+    wp = binv.gemm_pack(W)
+    assert wp.data.numel() == binv.lib().binv_gemm_bf16_packed_bytes(N, K)
+    for M in (1, 2, 5, 15, 16, 17, 31, 32, 33, 48, 63, 64):
+        for dt in (torch.bfloat16, torch.float32):
+            plain = binv.gemm(A[:M], W, out_dtype=dt)
+            packed = binv.gemm_packed(A[:M], wp, out_dtype=dt)
+            assert_bitwise_equal(packed, plain, f"M={M} {dt}")
+    # strided A rows, an output with a leading dimension past N
+    Ab = synth.normal((7, K + 64), 1.0, 43, DEV)
+    out = torch.full((7, N + 8), float("nan"), dtype=torch.float32, device=DEV)
+    binv.gemm_packed(Ab[:, :K], wp, out=out[:, :N])
+    assert_bitwise_equal(out[:, :N], binv.gemm(Ab[:, :K], W, out_dtype=torch.float32), "strided")
+    assert bool(torch.isnan(out[:, N:]).all())
+
+
+def test_packed_weights_exact_integers_and_limits():
+    # exact against the oracle on integer inputs; K = 0 writes zeros; M > 64
+    # is rejected without a launch
+    M, N, K = 9, 136, 264
+    A, W = ints((M, K), 51), ints((K, N), 52)
+    wp = binv.gemm_pack(W.to(DEV))
+    c32 = binv.gemm_packed(A.to(DEV), wp, out_dtype=torch.float32)
+    np.testing.assert_array_equal(f64(c32), oracle.gemm(f64(A), f64(W)))
+    wz = binv.gemm_pack(torch.empty((0, 16), dtype=torch.bfloat16, device=DEV))
+    z = torch.full((3, 16), 7.0, dtype=torch.float32, device=DEV)
+    binv.gemm_packed(torch.empty((3, 0), dtype=torch.bfloat16, device=DEV), wz, out=z)
+    assert bool((z == 0).all())
+    with pytest.raises(binv.BinvError):
+        binv.gemm_packed(torch.zeros((65, K), dtype=torch.bfloat16, device=DEV), wp)
+
+
 def test_target_row_at_every_tile_position():
     # the target lands at every row of a 128-row tile and in several tiles:
     # all copies must carry identical bits
