@@ -89,6 +89,19 @@ int binv_rmsnorm(const void* x, int x_dt, int64_t ldx,
                  void* y, int y_dt, int64_t ldy,
                  int64_t M, int64_t d, float eps, void* stream);
 
+/* The residual update followed by the RMSNorm of its result, in one launch
+ * (a decoder layer's "h += o; x = norm(h)"):
+ *   h[i, j] += float(a[i, j]);  then y = binv_rmsnorm of the updated h (fp32)
+ * with the bits of binv_residual_add followed by binv_rmsnorm(h, BINV_F32, ...)
+ * (the same fp32 adds, and the same per-row reduction).
+ * h fp32 [M, d] (ldh), updated in place; a bf16 [M, d] (lda, a multiple of 4,
+ * 8-byte aligned); gamma, y and the limits as for binv_rmsnorm with fp32 x.
+ * y must not overlap h or a. */
+int binv_add_rmsnorm(float* h, int64_t ldh, const void* a, int64_t lda,
+                     const void* gamma, int g_dt,
+                     void* y, int y_dt, int64_t ldy,
+                     int64_t M, int64_t d, float eps, void* stream);
+
 /* ------------------------------------------------------------------------
  * GEMM with one fixed per-element reduction and no split-K.
  * Defines: devpress.csdn.net explainer, section 3.2 Matmul

@@ -37,6 +37,7 @@ def _declare(lib):
         "binv_version": (ctypes.c_char_p, []),
         "binv_rmsnorm": (ci, [vp, ci, i64, vp, ci, vp, ci, i64, i64, i64, f32, vp]),
         "binv_rmsnorm_tuned": (ci, [vp, ci, i64, vp, ci, vp, ci, i64, i64, i64, f32, vp]),
+        "binv_add_rmsnorm": (ci, [vp, i64, vp, i64, vp, ci, vp, ci, i64, i64, i64, f32, vp]),
         "binv_gemm_bf16": (ci, [vp, i64, vp, i64, vp, ci, i64, i64, i64, i64, vp]),
         "binv_gemm_bf16_tuned_workspace_bytes": (sz, [i64, i64, i64]),
         "binv_gemm_bf16_packed_bytes": (sz, [i64, i64]),
@@ -140,6 +141,22 @@ def rmsnorm(x, gamma, eps=1e-6, out=None, out_dtype=torch.bfloat16, tuned=False)
     fn = lib().binv_rmsnorm_tuned if tuned else lib().binv_rmsnorm
     _check(fn(_ptr(x), _dt(x), ldx, _ptr(gamma), _dt(gamma), _ptr(out), _dt(out), ldy, M, d,
               float(eps), _stream(x)), fn.__name__)
+    return out
+
+
+def add_rmsnorm(h, a, gamma, eps=1e-6, out=None, out_dtype=torch.bfloat16):
+    """h += a (h fp32 [M, d] in place, a bf16), then rmsnorm of the updated h:
+    the bits of residual_add(h, a) followed by rmsnorm(h, ...)."""
+    _dev(h, a, gamma, out)
+    M, ldh = _rows(h)
+    _, lda = _rows(a)
+    d = h.shape[1]
+    assert h.dtype == torch.float32 and a.dtype == torch.bfloat16 and tuple(a.shape) == (M, d)
+    if out is None:
+        out = torch.empty((M, d), dtype=out_dtype, device=h.device)
+    _, ldy = _rows(out)
+    _check(lib().binv_add_rmsnorm(_ptr(h), ldh, _ptr(a), lda, _ptr(gamma), _dt(gamma), _ptr(out),
+                                  _dt(out), ldy, M, d, float(eps), _stream(h)), "binv_add_rmsnorm")
     return out
 
 

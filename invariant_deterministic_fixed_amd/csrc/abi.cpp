@@ -100,6 +100,18 @@ int binv_rmsnorm(const void* x, int x_dt, int64_t ldx, const void* gamma, int g_
                                           (hipStream_t)stream));
 }
 
+int binv_add_rmsnorm(float* h, int64_t ldh, const void* a, int64_t lda, const void* gamma,
+                     int g_dt, void* y, int y_dt, int64_t ldy, int64_t M, int64_t d, float eps,
+                     void* stream) {
+    const int st = check_rmsnorm(h, BINV_F32, ldh, gamma, g_dt, y, y_dt, ldy, M, d);
+    if (st != BINV_OK || M == 0) return st;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return BINV_ERR_INVALID_ARG;
+    if (!a || (reinterpret_cast<uintptr_t>(a) & 7u) || lda % 4 || lda < d) return BINV_ERR_INVALID_ARG;
+    return status_of(binv::launch_add_rmsnorm(h, ldh, a, lda, gamma, g_dt == BINV_BF16, y,
+                                              y_dt == BINV_BF16, ldy, M, (int)d, eps,
+                                              (hipStream_t)stream));
+}
+
 int binv_rmsnorm_tuned(const void* x, int x_dt, int64_t ldx, const void* gamma, int g_dt,
                        void* y, int y_dt, int64_t ldy, int64_t M, int64_t d, float eps,
                        void* stream) {

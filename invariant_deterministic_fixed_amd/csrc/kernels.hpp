@@ -11,6 +11,9 @@ namespace binv {
 hipError_t launch_rmsnorm(const void* x, int x_bf16, int64_t ldx, const void* g, int g_bf16,
                           void* y, int y_bf16, int64_t ldy, int64_t M, int d, float eps,
                           hipStream_t s);
+hipError_t launch_add_rmsnorm(float* h, int64_t ldh, const void* a, int64_t lda, const void* g,
+                              int g_bf16, void* y, int y_bf16, int64_t ldy, int64_t M, int d,
+                              float eps, hipStream_t s);
 hipError_t launch_rmsnorm_tuned(const void* x, int x_bf16, int64_t ldx, const void* g, int g_bf16,
                                 void* y, int y_bf16, int64_t ldy, int64_t M, int d, float eps,
                                 hipStream_t s);

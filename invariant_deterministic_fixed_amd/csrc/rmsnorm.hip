@@ -87,25 +87,17 @@ __device__ __forceinline__ void store_elems(void* p, int64_t e, const float (&f)
     }
 }
 
+// The row's reduction and output from its vectors xv (vector vi = t + v NT of
+// the row held by lane t): sum of squares per lane in vector order, then the
+// wave's butterfly, then the waves' sums in wave order.  One copy of this
+// arithmetic serves every kernel below, so their bits agree.
 template <bool XB, bool GB, bool YB, int NT, int MAXV>
-__global__ __launch_bounds__(NT) void rmsnorm_kernel(const void* __restrict__ x, int64_t ldx,
-                                                     const void* __restrict__ g,
-                                                     void* __restrict__ y, int64_t ldy,
-                                                     int d, float eps) {
-    constexpr int VEC = XB ? 8 : 4;                 // elements per 16-byte vector of x
+__device__ __forceinline__ void norm_row(const u32x4 (&xv)[MAXV], int nvec, const void* g,
+                                         char* yr, int d, float eps) {
+    constexpr int VEC = XB ? 8 : 4;
     constexpr int NW = NT / WAVE;
-    const int64_t row = blockIdx.x;
     const int t = threadIdx.x;
-    const int nvec = d / VEC;
-    const char* xr = reinterpret_cast<const char*>(x) + row * ldx * (XB ? 2 : 4);
-
-    u32x4 xv[MAXV];
     float ss = 0.0f;
-#pragma unroll
-    for (int v = 0; v < MAXV; ++v) {
-        const int vi = t + v * NT;
-        if (vi < nvec) xv[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + (int64_t)vi * 16));
-    }
 #pragma unroll
     for (int v = 0; v < MAXV; ++v) {
         const int vi = t + v * NT;
@@ -127,7 +119,6 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(const void* __restrict__ x,
     for (int w = 1; w < NW; ++w) tot += wsum[w];
     const float r = rsqrtf(tot / (float)d + eps);
 
-    char* yr = reinterpret_cast<char*>(y) + row * ldy * (YB ? 2 : 4);
 #pragma unroll
     for (int v = 0; v < MAXV; ++v) {
         const int vi = t + v * NT;
@@ -140,6 +131,60 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(const void* __restrict__ x,
             store_elems<YB, VEC>(yr, (int64_t)vi * VEC, o);
         }
     }
+}
+
+template <bool XB, bool GB, bool YB, int NT, int MAXV>
+__global__ __launch_bounds__(NT) void rmsnorm_kernel(const void* __restrict__ x, int64_t ldx,
+                                                     const void* __restrict__ g,
+                                                     void* __restrict__ y, int64_t ldy,
+                                                     int d, float eps) {
+    constexpr int VEC = XB ? 8 : 4;                 // elements per 16-byte vector of x
+    const int64_t row = blockIdx.x;
+    const int t = threadIdx.x;
+    const int nvec = d / VEC;
+    const char* xr = reinterpret_cast<const char*>(x) + row * ldx * (XB ? 2 : 4);
+    u32x4 xv[MAXV];
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+        const int vi = t + v * NT;
+        if (vi < nvec) xv[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + (int64_t)vi * 16));
+    }
+    norm_row<XB, GB, YB, NT, MAXV>(xv, nvec, g, reinterpret_cast<char*>(y) + row * ldy * (YB ? 2 : 4),
+                                   d, eps);
+}
+
+// Residual update and the norm of its result in one pass: h[row] += float(a[row])
+// (fp32 adds, written back to h), then the invariant RMSNorm of the updated fp32
+// row -- the bits of the residual add followed by rmsnorm_kernel<false, ...>.
+template <bool GB, bool YB, int NT, int MAXV>
+__global__ __launch_bounds__(NT) void add_rmsnorm_kernel(float* __restrict__ h, int64_t ldh,
+                                                         const bf16_t* __restrict__ a, int64_t lda,
+                                                         const void* __restrict__ g,
+                                                         void* __restrict__ y, int64_t ldy,
+                                                         int d, float eps) {
+    const int64_t row = blockIdx.x;
+    const int t = threadIdx.x;
+    const int nvec = d / 4;
+    float* hr = h + row * ldh;
+    const bf16_t* ar = a + row * lda;
+    u32x4 xv[MAXV];
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+        const int vi = t + v * NT;
+        if (vi < nvec) {
+            const u32x4 hv = *reinterpret_cast<const u32x4*>(hr + 4 * vi);
+            const u32x2 av = *reinterpret_cast<const u32x2*>(ar + 4 * vi);
+            const float s0 = __uint_as_float(hv[0]) + lo_bf16(av[0]);
+            const float s1 = __uint_as_float(hv[1]) + hi_bf16(av[0]);
+            const float s2 = __uint_as_float(hv[2]) + lo_bf16(av[1]);
+            const float s3 = __uint_as_float(hv[3]) + hi_bf16(av[1]);
+            xv[v] = u32x4{__float_as_uint(s0), __float_as_uint(s1), __float_as_uint(s2),
+                          __float_as_uint(s3)};
+            *reinterpret_cast<u32x4*>(hr + 4 * vi) = xv[v];
+        }
+    }
+    norm_row<false, GB, YB, NT, MAXV>(xv, nvec, g, reinterpret_cast<char*>(y) + row * ldy * (YB ? 2 : 4),
+                                      d, eps);
 }
 
 template <int NT, int MAXV>
@@ -165,6 +210,22 @@ hipError_t launch_rmsnorm(const void* x, int xb, int64_t ldx, const void* g, int
                           int yb, int64_t ldy, int64_t M, int d, float eps, hipStream_t s) {
     if (M == 0) return hipSuccess;
     return dispatch<256, 8>(x, xb, ldx, g, gb, y, yb, ldy, M, d, eps, s);
+}
+
+hipError_t launch_add_rmsnorm(float* h, int64_t ldh, const void* a, int64_t lda, const void* g,
+                              int gb, void* y, int yb, int64_t ldy, int64_t M, int d, float eps,
+                              hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    dim3 grid((unsigned)M), block(256);
+#define BINV_ARMS(GB, YB)                                                                        \
+    if (gb == GB && yb == YB) {                                                                  \
+        hipLaunchKernelGGL((add_rmsnorm_kernel<GB, YB, 256, 8>), grid, block, 0, s, h, ldh,      \
+                           (const bf16_t*)a, lda, g, y, ldy, d, eps);                            \
+        return hipGetLastError();                                                                \
+    }
+    BINV_ARMS(1, 1) BINV_ARMS(1, 0) BINV_ARMS(0, 1) BINV_ARMS(0, 0)
+#undef BINV_ARMS
+    return hipErrorInvalidValue;
 }
 
 // Comparator: block size picked from M (more lanes per row when there are few

@@ -277,11 +277,22 @@ class Decoder:
                 elif n:
                     B.gemm(src[sl], wt, out=dst[sl], tuned=t)
 
+        def add_norm(dst, blocks):
+            # h += o, then dst = norm(h): one fused launch when every row is
+            # invariant (the bits of the two separate calls)
+            if len(blocks) == 1 and not blocks[0][1]:
+                B.add_rmsnorm(h, o, self.w["norm"], cfg["eps"], out=dst)
+            else:
+                B.residual_add(h, o)
+                norm(h, dst, blocks)
+
         B.embed(ids_d, self.w["embed"], out=h)
+        n_layers = len(self.w["layers"])
         for li, lw in enumerate(self.w["layers"]):
             if on_layer is not None:
                 on_layer(li, h)
-            norm(h, x, rows_tok)
+            if li == 0:
+                norm(h, x, rows_tok)
             mm(x, lw["wqkv"], qkv, rows_tok)
             B.rope_kv_write(qkv, tseq_d, tpos_d, Hq, Hkv, D, cfg["theta"], pool.k[li], pool.v[li],
                             table, q_out=q)
@@ -292,12 +303,14 @@ class Decoder:
                 B.attn_prefill(q, cu_d, pool.k[li], pool.v[li], table, lens_d, max_q,
                                self.max_kv_len, scale, out=a, workspace=self.ws)
             mm(a.view(T, Hq * D), lw["wo"], o, rows_tok)
-            B.residual_add(h, o)
-            norm(h, x, rows_tok)
+            add_norm(x, rows_tok)
             mm(x, lw["wgu"], gu, rows_tok)
             B.swiglu(gu, out=s)
             mm(s, lw["wd"], o, rows_tok)
-            B.residual_add(h, o)
+            if li + 1 < n_layers:
+                add_norm(x, rows_tok)            # and the next layer's input norm
+            else:
+                B.residual_add(h, o)
         if on_layer is not None:
             on_layer(len(self.w["layers"]), h)
         hl, xl, logits = self.hl[:nb], self.xl[:nb], self.logits[:nb]

@@ -262,6 +262,21 @@ def test_residual_add_validation():
     assert f(FAKE, 8, FAKE, 8, 2, 6, L) == UNSUPPORTED                      # H % 4
 
 
+def test_add_rmsnorm_validation():
+    f = _lib().binv_add_rmsnorm
+    assert f(L, 8, L, 8, L, 1, L, 1, 8, 0, 8, 1e-6, L) == OK                # M = 0: no-op
+    assert f(FAKE, 8, L, 8, FAKE, 1, FAKE, 1, 8, 2, 8, 1e-6, L) == INVALID  # null a
+    assert f(FAKE, 8, FAKE + 2, 8, FAKE, 1, FAKE, 1, 8, 2, 8, 1e-6, L) == INVALID  # a not 8B aligned
+    assert f(FAKE, 8, FAKE, 6, FAKE, 1, FAKE, 1, 8, 2, 8, 1e-6, L) == INVALID  # lda % 4
+    assert f(FAKE, 8, FAKE, 4, FAKE, 1, FAKE, 1, 8, 2, 8, 1e-6, L) == INVALID  # lda < d
+    assert f(FAKE + 4, 8, FAKE, 8, FAKE, 1, FAKE, 1, 8, 2, 8, 1e-6, L) == INVALID  # h misaligned
+    assert f(FAKE, 8, FAKE, 8, FAKE, 1, FAKE, 1, 8, 2, 8, -1.0, L) == INVALID  # negative eps
+    assert f(FAKE, 8, FAKE, 8, FAKE, 7, FAKE, 1, 8, 2, 8, 1e-6, L) == INVALID  # bad dtype
+    assert f(FAKE, 8, FAKE, 8, FAKE, 1, FAKE, 1, 8, 2, 6, 1e-6, L) == UNSUPPORTED  # d % 4
+    assert f(FAKE, 16384, FAKE, 16384, FAKE, 1, FAKE, 1, 16384, 2, 16384, 1e-6,
+             L) == UNSUPPORTED                                              # fp32 rows <= 8192
+
+
 def test_gather_rows_validation():
     f = _lib().binv_gather_rows
     assert f(L, 1, 8, L, 0, L, 8, 8, L) == OK                               # R = 0

@@ -32,6 +32,25 @@ def test_residual_add_is_the_rounded_fp32_sum():
     np.testing.assert_array_equal(h.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("M,d", [(1, 4096), (37, 4096), (300, 256), (5, 8192)])
+@pytest.mark.parametrize("g_dt,y_dt", [(torch.bfloat16, torch.bfloat16),
+                                       (torch.float32, torch.float32)])
+def test_add_rmsnorm_is_residual_add_then_rmsnorm(M, d, g_dt, y_dt):
+    # the fused launch gives the bits of the two separate calls, in h and in y
+    h0 = synth.normal((M, d), 1.0, 11, DEV, dtype=torch.float32)
+    a = synth.normal((M, d), 3.0, 12, DEV)
+    gamma = synth.uniform((d,), 0.5, 1.5, 13, DEV).to(g_dt)
+    h1, h2 = h0.clone(), h0.clone()
+    binv.residual_add(h1, a)
+    want = binv.rmsnorm(h1, gamma, 1e-6, out_dtype=y_dt)
+    got = binv.add_rmsnorm(h2, a, gamma, 1e-6, out_dtype=y_dt)
+    assert_bitwise_equal(h2, h1, "updated residual")
+    assert_bitwise_equal(got, want, "norm output")
+    # and the norm is the fp64 RMSNorm of the updated rows, to bf16/fp32 rounding
+    ref = oracle.rmsnorm(f64(h1), f64(gamma), 1e-6)
+    assert row_rel_err(f64(got), ref).max() <= TOL_BF16
+
+
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 4, 2)])
 def test_rope_and_kv_write(D, Hq, Hkv):
     T = 300
