@@ -609,9 +609,10 @@ def sweep(dev="cuda:0"):
                  ms_B1=round(ms[1], 4), ms_B64=round(ms[64], 4), ms_B1024=round(ms[1024], 4))
 
 
-def gemm_shapes(shapes, reps, dev="cuda:0"):
+def gemm_shapes(shapes, reps, dev="cuda:0", packed=False):
     """The invariant GEMM alone, per shape (M, N, K): weights rotated over
-    enough copies to exceed the last-level cache, R timed launches."""
+    enough copies to exceed the last-level cache, R timed launches.  packed:
+    through binv_gemm_bf16_packed on strip-packed copies (M <= 64)."""
     import torch
     import invariant_deterministic_fixed_amd as binv
     from invariant_deterministic_fixed_amd import synth
@@ -627,11 +628,15 @@ def gemm_shapes(shapes, reps, dev="cuda:0"):
         Ws = [synth.normal((K, N), 0.02, 7 + i, dev) for i in range(_copies(2 * N * K))]
         A = synth.normal((M, K), 1.0, 3, dev)
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        t = _cold_ms([lambda W=W: binv.gemm(A, W, out=C) for W in Ws], reps=reps)
+        if packed:
+            Ws = [binv.gemm_pack(W) for W in Ws]
+            t = _cold_ms([lambda W=W: binv.gemm_packed(A, W, out=C) for W in Ws], reps=reps)
+        else:
+            t = _cold_ms([lambda W=W: binv.gemm(A, W, out=C) for W in Ws], reps=reps)
         flops = 2.0 * M * N * K
         nbytes = 2 * (M * K + K * N + M * N)
         roof_ms = max(flops / PEAK_BF16_TFLOPS / 1e9, nbytes / PEAK_HBM_GBPS / 1e6)
-        print(json.dumps({"gemm": [M, N, K], "us": round(t * 1e3, 2),
+        print(json.dumps({"gemm": [M, N, K], "packed": packed, "us": round(t * 1e3, 2),
                           "TFLOPs": round(flops / t / 1e9, 2), "GBps": round(nbytes / t / 1e6, 1),
                           "roofline_frac": round(roof_ms / t, 4)}), flush=True)
         del Ws, A, C
@@ -650,6 +655,8 @@ def main():
                     help="per-shape figures (one JSON line per case) instead of the bench line")
     ap.add_argument("--gemm", action="append", default=[],
                     help="M,N,K: time the invariant GEMM alone on this shape (repeatable)")
+    ap.add_argument("--packed", action="store_true",
+                    help="with --gemm: the packed-weight entry point (M <= 64)")
     ap.add_argument("--reps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -665,7 +672,8 @@ def main():
         sweep(dev)
         return
     if args.gemm:
-        gemm_shapes([tuple(int(v) for v in g.split(",")) for g in args.gemm], args.reps, dev)
+        gemm_shapes([tuple(int(v) for v in g.split(",")) for g in args.gemm], args.reps, dev,
+                    packed=args.packed)
         return
     w = build_workload(dev)
     work = algorithmic(w)
