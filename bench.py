@@ -34,10 +34,14 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--ramp-seconds S] [-
                                   per case)
        [--profile-copy]   (adds one 1 GiB device copy, the calibration kernel
                            for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
-       python bench.py --gemm M,N,K [--gemm ...] [--reps R]
+       python bench.py --gemm M,N,K [--gemm ...] [--reps R] [--packed]
                           (the invariant GEMM alone on the given shapes, cold
                            operands, one JSON line per shape: for per-shape
-                           kernel traces and counters)
+                           kernel traces and counters; --packed through the
+                           packed-weight entry point)
+       python bench.py --decoder B [--steps K]
+                          (the 8B-class decoder's decode steps at batch B alone:
+                           invariant kernels, packed weights, HIP graphs)
 """
 import argparse
 import hashlib
@@ -536,37 +540,7 @@ def sweep(dev="cuda:0"):
             if mode == "locked" and B == 1:
                 continue
             for graph in (True, False):
-                pool = dec.KVPool(cfg, num_pages=B * (1024 + 64) // 16 + B, max_seqs=B,
-                                  max_len=1024 + 64, seed=11, device=dev)
-                d = dec.Decoder(w, cfg, pool, max_tokens=max(1024, B), max_seqs=B,
-                                max_kv_len=1024 + 64, tuned=(mode == "tuned"),
-                                packed=None if mode == "tuned" else packed)
-                r = np.random.default_rng(42)
-                slots = [pool.alloc() for _ in range(B)]
-                prot = {slots[0]} if mode == "locked" else None
-                toks = {}
-                for sl in slots:                          # prefill, untimed
-                    _, ids, _ = d.step([(sl, r.integers(0, cfg["vocab"], 1024).tolist(), 0)])
-                    toks[sl] = int(ids[0, 0])
-                # one untimed decode step (the graph's capture)
-                _, ids, _ = d.step([(sl, [toks[sl]], 1024) for sl in slots], protected=prot,
-                                   graph=graph)
-                ids = ids.cpu()
-                for i, sl in enumerate(slots):
-                    toks[sl] = int(ids[i, 0])
-                torch.cuda.synchronize()
-                steps = 8
-                t0 = time.perf_counter()
-                for k in range(steps):
-                    _, ids, _ = d.step([(sl, [toks[sl]], 1025 + k) for sl in slots],
-                                       protected=prot, graph=graph)
-                    ids = ids.cpu()
-                    for i, sl in enumerate(slots):
-                        toks[sl] = int(ids[i, 0])
-                torch.cuda.synchronize()
-                res[(mode, graph)] = B * steps / (time.perf_counter() - t0)
-                del d, pool
-                torch.cuda.empty_cache()
+                res[(mode, graph)] = decoder_tokens_per_s(w, packed, B, mode, graph, 8, dev)
         emit(sweep="decoder_8b_decode", B=B, context=1024,
              invariant_tokens_per_s=round(res[("invariant", True)], 1),
              tuned_tokens_per_s=round(res[("tuned", True)], 1),
@@ -607,6 +581,62 @@ def sweep(dev="cuda:0"):
                  kernels="tuned" if tuned else "invariant", d=d, layers=layers,
                  drift_rel=drift, elements_moved=moved,
                  ms_B1=round(ms[1], 4), ms_B64=round(ms[64], 4), ms_B1024=round(ms[1024], 4))
+
+
+def decoder_tokens_per_s(w, packed, B, mode, graph, steps, dev="cuda:0"):
+    """8B-class decoder: B sequences prefilled with 1024 random tokens each
+    (untimed), one untimed decode step (a graph's capture), then `steps` timed
+    decode steps of one token per sequence; returns tokens/s.  mode: invariant,
+    tuned (the comparators), or locked (sequence 0 invariant among tuned ones);
+    invariant products of up to 16 rows read `packed` (not with tuned)."""
+    import numpy as np
+    import torch
+    from invariant_deterministic_fixed_amd import decoder as dec
+
+    cfg = dec.CONFIG5
+    pool = dec.KVPool(cfg, num_pages=B * (1024 + 64) // 16 + B, max_seqs=B,
+                      max_len=1024 + 64, seed=11, device=dev)
+    d = dec.Decoder(w, cfg, pool, max_tokens=max(1024, B), max_seqs=B,
+                    max_kv_len=1024 + 64, tuned=(mode == "tuned"),
+                    packed=None if mode == "tuned" else packed)
+    r = np.random.default_rng(42)
+    slots = [pool.alloc() for _ in range(B)]
+    prot = {slots[0]} if mode == "locked" else None
+    toks = {}
+    for sl in slots:
+        _, ids, _ = d.step([(sl, r.integers(0, cfg["vocab"], 1024).tolist(), 0)])
+        toks[sl] = int(ids[0, 0])
+    _, ids, _ = d.step([(sl, [toks[sl]], 1024) for sl in slots], protected=prot, graph=graph)
+    ids = ids.cpu()
+    for i, sl in enumerate(slots):
+        toks[sl] = int(ids[i, 0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        _, ids, _ = d.step([(sl, [toks[sl]], 1025 + k) for sl in slots], protected=prot,
+                           graph=graph)
+        ids = ids.cpu()
+        for i, sl in enumerate(slots):
+            toks[sl] = int(ids[i, 0])
+    torch.cuda.synchronize()
+    tps = B * steps / (time.perf_counter() - t0)
+    del d, pool
+    torch.cuda.empty_cache()
+    return tps
+
+
+def decoder_only(B, steps, dev="cuda:0"):
+    """The 8B-class decoder's decode steps alone (invariant, packed weights,
+    HIP graphs): one JSON line, for traces of a decode step."""
+    from invariant_deterministic_fixed_amd import decoder as dec
+
+    w = dec.random_weights(dec.CONFIG5, 5, dev)
+    packed = dec.pack_weights(w)
+    tps = decoder_tokens_per_s(w, packed, B, "invariant", True, steps, dev)
+    print(json.dumps({"decoder_8b_decode": {"B": B, "context": 1024, "steps": steps,
+                                            "tokens_per_s": round(tps, 1),
+                                            "ms_per_step": round(B / tps * 1e3, 3)}}),
+          flush=True)
 
 
 def gemm_shapes(shapes, reps, dev="cuda:0", packed=False):
@@ -658,6 +688,9 @@ def main():
     ap.add_argument("--packed", action="store_true",
                     help="with --gemm: the packed-weight entry point (M <= 64)")
     ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--decoder", type=int, default=0, metavar="B",
+                    help="time the 8B-class decoder's decode steps at batch B alone "
+                         "(--steps of them)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -670,6 +703,9 @@ def main():
     torch.cuda.set_device(0)
     if args.sweep:
         sweep(dev)
+        return
+    if args.decoder:
+        decoder_only(args.decoder, args.steps, dev)
         return
     if args.gemm:
         gemm_shapes([tuple(int(v) for v in g.split(",")) for g in args.gemm], args.reps, dev,
