@@ -403,11 +403,13 @@ def sweep(dev="cuda:0"):
         torch.cuda.synchronize()
     del a, b
 
-    # GEMM: invariant vs tuned vs torch.mm, per M and weight shape
+    # GEMM: invariant vs tuned vs torch.mm, per M and weight shape; up to 64
+    # rows also the invariant product over strip-packed weights
     for (N, K, c32) in [(4096, 4096, False), (14336, 4096, False), (4096, 14336, False),
                         (128256, 4096, True)]:
         nw = _copies(2 * N * K)
         Ws = [synth.normal((K, N), 0.02, 7 + i, dev) for i in range(nw)]
+        Wps = [binv.gemm_pack(W) for W in Ws]
         for M in [1, 2, 7, 16, 64, 256, 1024, 2048, 8192]:
             if c32 and M > 256:
                 continue
@@ -419,9 +421,11 @@ def sweep(dev="cuda:0"):
             t_inv = _cold_ms([lambda W=W: binv.gemm(A, W, out=C) for W in Ws])
             t_tun = _cold_ms([lambda W=W: binv.gemm(A, W, out=C, tuned=True, workspace=ws)
                               for W in Ws])
-            t_mm = None
+            t_mm = t_pk = None
             if not c32:
                 t_mm = _cold_ms([lambda W=W: torch.mm(A, W, out=C) for W in Ws])
+            if M <= 64:
+                t_pk = _cold_ms([lambda W=W: binv.gemm_packed(A, W, out=C) for W in Wps])
             flops = 2.0 * M * N * K
             nbytes = 2 * (M * K + K * N) + (4 if c32 else 2) * M * N
             roof_ms = max(flops / PEAK_BF16_TFLOPS / 1e9, nbytes / PEAK_HBM_GBPS / 1e6)
@@ -429,10 +433,12 @@ def sweep(dev="cuda:0"):
                  invariant_TFLOPs=round(flops / t_inv / 1e9, 2),
                  tuned_TFLOPs=round(flops / t_tun / 1e9, 2),
                  torch_mm_TFLOPs=None if t_mm is None else round(flops / t_mm / 1e9, 2),
+                 packed_TFLOPs=None if t_pk is None else round(flops / t_pk / 1e9, 2),
+                 packed_weight_GBps=None if t_pk is None else round(2 * N * K / t_pk / 1e6, 1),
                  roofline_frac=round(roof_ms / t_inv, 4),
                  slowdown_vs_tuned=round(t_inv / t_tun, 3))
             del A, C, ws
-        del Ws
+        del Ws, Wps
         torch.cuda.empty_cache()
 
     # RMSNorm: invariant vs tuned, per M and d

@@ -118,7 +118,12 @@ int binv_add_rmsnorm(float* h, int64_t ldh, const void* a, int64_t lda,
  * k in ascending blocks of 32 (K zero-padded to a multiple of 64), one
  * accumulator per element, whatever M is.  Which lanes and workgroups carry
  * which elements (the output tiling) follows the shape; it never enters an
- * element's arithmetic, so a row's bits do not depend on M.
+ * element's arithmetic, so a row's bits do not depend on M.  (A deviation
+ * from the pages, which keep one tile configuration for every batch size
+ * because there the configuration sets the reduction order: here only the
+ * per-element reduction is fixed, and the invariance rests on the matrix
+ * instruction giving an element the same bits in every lane, tile and
+ * kernel, which tests check across every kernel and M.)
  * K and N must be multiples of 8; M, N, K <= 2^31 - 1; lda < 2^22 and
  * ldw < 1.6e7 elements (tiles are addressed with 32-bit offsets).  M = 0 or
  * N = 0 is a no-op; K = 0 writes zeros.  C must not overlap A or W.

@@ -711,6 +711,7 @@ using BigTile = Tile<256, 256, 2, 4, 8>;
 using MidTile = Tile<128, 128, 2, 2, 8>;         // the comparator's tile
 using MidTile4 = Tile<128, 128, 2, 2, 8, 4>;     // the same with four LDS stages
 using SmallTile = Tile<64, 64, 2, 2, 8, 4>;      // 4 waves of 32 x 32, four stages
+using WideTile = Tile<256, 128, 4, 2, 8, 3>;     // 8 waves of 64 x 64, three stages
 
 // ------------------------------------------------------------------ large M
 // The 256 x 256 tile of BigTile (same LDS stages, same DMA, same fragments,
@@ -937,8 +938,10 @@ hipError_t launch_tile(const void* A, int64_t lda, const void* W, int64_t ldw, v
 
 // Which kernel computes the outputs is chosen from the shape: the 256 x 256
 // tile once it gives at least 192 tiles (fills most of the 256 CUs); else
-// strips for M <= 64; else 128 x 128 tiles if they give at least 192; else
-// 64 x 64 tiles.  All of them run
+// strips for M <= 64; else 256 x 128, then 128 x 128 tiles if they give at
+// least 192; else 64 x 64 tiles.  (Each tile kernel moves about the same
+// bytes per CU per second from L2 into LDS, so the largest tile that still
+// fills the GPU -- the most flops per operand byte -- is the fastest.)  All of them run
 // the same per-element arithmetic -- one accumulator, one MFMA chain over the
 // same ascending 32-wide k-blocks and the same zero-padded K-tiles of 64 --
 // so the choice, and with it M, never reaches the bits.
@@ -953,6 +956,10 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, v
         return hipGetLastError();
     }
     if (M > 64) {
+        const int64_t wide_tiles = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
+        if (wide_tiles >= 192)
+            return launch_tile<WideTile>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,
+                                         c_f32, s);
         const int64_t mid_tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
         if (mid_tiles >= 192)
             return launch_tile<MidTile4>(A, lda, W, ldw, C, ldc, 0, M, N, K, 1, nk > 0 ? nk : 1,

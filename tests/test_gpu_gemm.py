@@ -108,7 +108,7 @@ def test_row0_bitwise_invariant_over_M(N, K):
                                  (14344, 136), (14336, 4096), (4096, 14336)])
 def test_kernels_chosen_by_shape_agree_bitwise(N, K):
     # M <= 64 runs on strips of 16, 32 or 64 columns (by N), mid-size M on
-    # 64 x 64 or 128 x 128 tiles and large M x N on 256 x 256 tiles (the
+    # 64 x 64, 128 x 128 or 256 x 128 tiles and large M x N on 256 x 256 tiles (the
     # two-group schedule for tiles inside C with K a multiple of 64, the
     # one-group schedule on the edges); every element must come out with the
     # same bits on all of them, ragged N and K, zero and negative-zero rows
@@ -126,7 +126,7 @@ def test_kernels_chosen_by_shape_agree_bitwise(N, K):
     ref16 = binv.gemm(Ad, W)
     ms = [1, 7, 16, 17, 32, 33, 64, 65, 130, 300]
     if big_m == 8192:
-        ms += [2, 256, 1024, 2048, 4097]
+        ms += [2, 256, 512, 600, 1024, 2048, 4097]
     for M in ms:
         assert_bitwise_equal(binv.gemm(Ad[:M], W, out_dtype=torch.float32), ref32[:M], f"fp32 M={M}")
         assert_bitwise_equal(binv.gemm(Ad[:M], W), ref16[:M], f"bf16 M={M}")
