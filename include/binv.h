@@ -203,7 +203,11 @@ int binv_gemm_bf16_packed(const void* A, int64_t lda, const void* Wp,
  *   ceil(64 / (Hq / Hkv)) new tokens) keep in memory only the merge tree's
  *   pending subtrees of four or more chunks, max(1, floor(log2(ceil(
  *   max_kv_len / 256))) - 1) per row, so a single-sequence prefill needs
- *   T * Hq * that many * (D + 2) * 4 bytes; rows
+ *   T * Hq * that many * (D + 2) * 4 bytes -- except when a single sequence's
+ *   128-row blocks (times Hkv) number fewer than 256 and max_kv_len spans at
+ *   most 64 chunks: then each workgroup takes an aligned pair of chunks and
+ *   the call keeps one pair node per token, T * Hq * ceil(chunks / 2) *
+ *   (D + 2) * 4 bytes; rows
  *   of short runs keep one partial per chunk, indexed per sequence when that
  *   is smaller than per token.  Both functions return 0 for arguments the
  *   entry points reject.

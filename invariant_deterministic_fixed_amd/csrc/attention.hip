@@ -299,7 +299,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     const int32_t* __restrict__ page_table, int64_t pt_stride,
     const int32_t* __restrict__ kv_lens, bf16_t* __restrict__ out,
     float* __restrict__ st_o, float2* __restrict__ st_ml, int Hq, int Hkv, int st_stride,
-    int max_kv_len, float scale_log2, int q_min, int nqb) {
+    int max_kv_len, float scale_log2, int q_min, int nqb, int node_pair) {
     constexpr int D = 128, KS = D / 32, NKT = CHUNK / 16;
     // sequences with fewer than q_min new tokens belong to the chunk kernel
     if (cu_q[blockIdx.z + 1] - cu_q[blockIdx.z] < q_min) return;
@@ -320,7 +320,13 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     const TileCtx x = tile_ctx<G, PF_WAVES>(b, g, qb, cu_q, kv_lens, pt_stride, max_kv_len);
     if (x.pos_max < 0) return;                        // no row in this block
     const int kv_len = x.kv_len;
-    const int nc = x.pos_max / CHUNK + 1;             // chunks the block's rows see
+    const int nc_all = x.pos_max / CHUNK + 1;         // chunks the block's rows see
+    // node_pair: this workgroup takes the aligned pair of chunks 2 y, 2 y + 1
+    // (y = blockIdx.y) and writes the pair's subtree as a node (level 1 of
+    // the merge tree) for the merge kernel; else every chunk, and the rows
+    const int c_first = node_pair ? 2 * (int)blockIdx.y : 0;
+    if (c_first >= nc_all) return;
+    const int nc = node_pair ? min(nc_all, c_first + 2) : nc_all;
     // The lane index and everything derived from it (LDS and HBM addresses,
     // row maps) are re-derived in every chunk from an opaque copy of the
     // thread index: hoisted out of the chunk loop, the many per-lane addresses
@@ -390,8 +396,8 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     };
     {
         const int lane = lane_id();
-        copy_k(0, lane);
-        copy_v(0, lane);
+        copy_k(c_first, lane);
+        copy_v(c_first, lane);
     }
 
     // ---- the per-row stack of the counter's slots >= 2 (slots 0 and 1 stay in
@@ -432,11 +438,11 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
     PfNode slot0, slot1;
     unsigned count = 0;
 #pragma clang loop unroll(disable)
-    for (int c = 0; c < nc; ++c) {
+    for (int c = c_first; c < nc; ++c) {
         const int j0 = c * CHUNK;
         const bool more = c + 1 < nc;
         const int lane = lane_id(), ar = lane & 15, ag = lane >> 4;
-        if (c > 0) {
+        if (c > c_first) {
             // K(c) and the stack stores landed (only V(c) may be in flight)
             __builtin_amdgcn_s_waitcnt(WAIT_VM8);
             lds_barrier();                                    // every wave's K(c) in LDS
@@ -584,8 +590,19 @@ __global__ __launch_bounds__(64 * PF_WAVES) void attn_prefill_kernel(
             else res = pf_combine(stack_load(sl, lane), res);
         }
     }
-    // out = o / l as bf16, an exact zero written as +0 (the merge kernel's last step)
     const RowInfo ri = row(ar);
+    if (node_pair) {
+        // the pair's node for the rows that reach it: slot (token * st_stride
+        // + y) * Hq + head of the node region (st_o, st_ml), as the chunk
+        // kernel writes its nodes
+        if (ri.token < 0 || ri.pos < c_first * CHUNK) return;
+        const int64_t sl = (ri.token * st_stride + (int)blockIdx.y) * Hq + ri.head;
+#pragma unroll
+        for (int f = 0; f < 8; ++f) *reinterpret_cast<f32x4*>(st_o + sl * D + 16 * f + 4 * ag) = res.o[f];
+        if (ag == 0) st_ml[sl] = make_float2(res.m, res.l);
+        return;
+    }
+    // out = o / l as bf16, an exact zero written as +0 (the merge kernel's last step)
     if (ri.token >= 0) {
         bf16_t* orow = out + (ri.token * Hq + ri.head) * D + 4 * ag;
 #pragma unroll
@@ -630,7 +647,7 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ kv_lens, int64_t B,
     int64_t n_tokens, int Hq, int n_chunks, int max_kv_len,
     const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, bf16_t* __restrict__ out,
-    int q_min, int leaf_seq) {
+    int q_min, int leaf_seq, int node_stride, int pf_level) {
     constexpr int VPL = MERGE_VPL, LPR = D / VPL, RPW = 64 / LPR;
     static_assert(D % VPL == 0 && 64 % LPR == 0, "");
     typedef float Vec __attribute__((ext_vector_type(VPL)));
@@ -669,14 +686,15 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
         return;
     }
     // the row's pos / CHUNK + 1 chunks arrive as nodes of the level the chunk
-    // kernel chose for it (leaves for prefill rows)
+    // kernel chose for it (decode), or of the call's prefill level pf_level
+    // (leaves, or the block kernel's chunk pairs)
     int n_leaf = pos / CHUNK + 1;
     if (n_leaf > n_chunks) n_leaf = n_chunks;
-    const int glog = (GMAX > 0 && !cu_q) ? node_level<GMAX>(n_leaf) : 0;
+    const int glog = cu_q ? pf_level : (GMAX > 0 ? node_level<GMAX>(n_leaf) : 0);
     const int n = ((n_leaf - 1) >> glog) + 1;
 
-    // node c of the row: slot (leaf_row * n_chunks + c) * Hq + head
-    const int64_t slot0 = leaf_row * n_chunks * Hq + (row - token * Hq);
+    // node c of the row: slot (leaf_row * node_stride + c) * Hq + head
+    const int64_t slot0 = leaf_row * node_stride * Hq + (row - token * Hq);
     const float* po = ws_o + slot0 * D + VPL * sub;
     const float2* pml = ws_ml + slot0;
 
@@ -761,6 +779,7 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
 // never both); otherwise the stacks come first, then the compact leaves.
 struct Layout {
     bool block = false;      // long new-token runs go to the block kernel
+    bool pairs = false;      // block kernel in chunk pairs, nodes to the merge kernel
     int q_split = 0x7fffffff;   // fewest new tokens of a sequence the block kernel takes
     bool leaves = true;      // the chunk and merge kernels run
     int leaf_seq = 0;        // 0: leaf row = token; > 0: row b * leaf_seq + i
@@ -786,6 +805,18 @@ Layout layout_of(int64_t B, int64_t n_tokens, int64_t max_q_len, int64_t max_kv_
     // 2 .. floor(log2 C) (at least one slot, so that the layout is never empty)
     int64_t levels = 1;
     while ((int64_t)4 << levels <= C) ++levels;
+    // one sequence whose 128-row blocks number fewer than the CUs (a short
+    // prompt, or a prompt chunk, over a context of at most 64 chunks): a
+    // workgroup per (block, KV head, aligned pair of chunks), the pairs' nodes
+    // ceil(C / 2) per token, merged by the merge kernel -- the same tree, more
+    // workgroups
+    const int64_t blocks = (n_tokens * G + PF_ROWS - 1) / PF_ROWS;
+    if (B == 1 && n_tokens >= L.q_split && blocks * Hkv < 256 && C >= 2 && C <= 64) {
+        L.pairs = true;
+        L.leaf_nodes = n_tokens * ((C + 1) / 2);
+        L.st_stride = (C + 1) / 2;
+        return L;
+    }
     // one sequence of q_split or more tokens: no leaves at all
     if (B == 1 && n_tokens >= L.q_split) {
         L.leaves = false;
@@ -844,8 +875,9 @@ hipError_t launch_chunk(const AttnArgs& a, hipStream_t s, int64_t nqt, int q_ski
 
 template <int D, int GMAX>
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s, const Regions& rg, int q_min,
-                        int leaf_seq) {
+                        int leaf_seq, int pf_level = 0, int node_stride = 0) {
     const int n_chunks = (int)n_chunks_of(a.max_kv_len);
+    if (node_stride == 0) node_stride = n_chunks;
     const int64_t Rows = a.n_tokens * a.Hq;
     constexpr int RPB = (NT / 64) * (64 * MERGE_VPL / D);      // rows per workgroup
     dim3 grid2((unsigned)((Rows + RPB - 1) / RPB));
@@ -854,15 +886,18 @@ hipError_t launch_merge(const AttnArgs& a, hipStream_t s, const Regions& rg, int
     if (n_chunks <= 31)
         hipLaunchKernelGGL((attn_merge_kernel<D, GMAX, 5>), grid2, dim3(NT), 0, s, a.cu_q,
                            a.kv_lens, a.B, a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len,
-                           rg.leaf_o, rg.leaf_ml, (bf16_t*)a.out, q_min, leaf_seq);
+                           rg.leaf_o, rg.leaf_ml, (bf16_t*)a.out, q_min, leaf_seq, node_stride,
+                           pf_level);
     else if (n_chunks <= 255)
         hipLaunchKernelGGL((attn_merge_kernel<D, GMAX, 8>), grid2, dim3(NT), 0, s, a.cu_q,
                            a.kv_lens, a.B, a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len,
-                           rg.leaf_o, rg.leaf_ml, (bf16_t*)a.out, q_min, leaf_seq);
+                           rg.leaf_o, rg.leaf_ml, (bf16_t*)a.out, q_min, leaf_seq, node_stride,
+                           pf_level);
     else
         hipLaunchKernelGGL((attn_merge_kernel<D, GMAX, STACK>), grid2, dim3(NT), 0, s, a.cu_q,
                            a.kv_lens, a.B, a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len,
-                           rg.leaf_o, rg.leaf_ml, (bf16_t*)a.out, q_min, leaf_seq);
+                           rg.leaf_o, rg.leaf_ml, (bf16_t*)a.out, q_min, leaf_seq, node_stride,
+                           pf_level);
     return hipGetLastError();
 }
 
@@ -884,12 +919,24 @@ template <int G>
 hipError_t launch_prefill128(const AttnArgs& a, hipStream_t s, const Layout& L, const Regions& rg) {
     constexpr int TQ = PF_ROWS / G, TQ1 = ROWS / G;
     const int64_t nqb = (a.max_q_len + TQ - 1) / TQ;
+    if (L.pairs) {
+        // chunk pairs: nodes into the leaf region, [token][pair][head]
+        dim3 grid1((unsigned)(nqb * a.Hkv), (unsigned)L.st_stride, (unsigned)a.B);
+        hipLaunchKernelGGL((attn_prefill_kernel<G>), grid1, dim3(64 * PF_WAVES), 0, s,
+                           (const bf16_t*)a.q, a.cu_q, (const bf16_t*)a.k_cache,
+                           (const bf16_t*)a.v_cache, a.page_table, a.pt_stride, a.kv_lens,
+                           (bf16_t*)a.out, rg.leaf_o, rg.leaf_ml, a.Hq, a.Hkv, (int)L.st_stride,
+                           (int)a.max_kv_len, a.scale_log2, L.q_split, (int)nqb, 1);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_merge<128, 0>(a, s, rg, 0x7fffffff, 0, 1, (int)L.st_stride);
+    }
     dim3 grid1((unsigned)(nqb * a.Hkv), 1, (unsigned)a.B);
     hipLaunchKernelGGL((attn_prefill_kernel<G>), grid1, dim3(64 * PF_WAVES), 0, s,
                        (const bf16_t*)a.q, a.cu_q, (const bf16_t*)a.k_cache,
                        (const bf16_t*)a.v_cache, a.page_table, a.pt_stride, a.kv_lens,
                        (bf16_t*)a.out, rg.st_o, rg.st_ml, a.Hq, a.Hkv, (int)L.st_stride,
-                       (int)a.max_kv_len, a.scale_log2, L.q_split, (int)nqb);
+                       (int)a.max_kv_len, a.scale_log2, L.q_split, (int)nqb, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !L.leaves) return e;
     // max_q_len only bounds the runs: any sequence may be short

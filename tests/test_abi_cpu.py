@@ -179,7 +179,14 @@ def test_prefill_workspace_sizes():
     assert f(1, 4096, 4096, 4096, 32, 8, 128) == 4096 * 3 * node
     assert f(1, 4096, 4096, 32768, 32, 8, 128) == 4096 * 6 * node
     assert f(1, 64, 64, 256, 32, 8, 128) == 64 * 1 * node
-    assert f(1, 64, 64, 1024, 32, 8, 128) == 64 * 1 * node
+    assert f(1, 2048, 2048, 4096, 32, 8, 128) == 2048 * 3 * node
+    # one sequence whose 128-row blocks (x KV heads) number fewer than the 256
+    # CUs, over at most 64 chunks: a node per aligned pair of chunks and token
+    assert f(1, 64, 64, 1024, 32, 8, 128) == 64 * 2 * node
+    assert f(1, 512, 512, 4096, 32, 8, 128) == 512 * 8 * node
+    assert f(1, 256, 256, 16384, 32, 8, 128) == 256 * 32 * node
+    # ... and over more than 64 chunks the looping kernel's stacks again
+    assert f(1, 512, 512, 32768, 32, 8, 128) == 512 * 6 * node
     # four long sequences: stacks per token plus leaves for at most 15 short
     # tokens per sequence (the block kernel takes runs of 16 or more at G = 4)
     assert f(4, 4096, 1024, 4096, 32, 8, 128) == (4096 * 3 + 4 * 15 * 16) * node

@@ -300,6 +300,9 @@ def test_prefill_head_groups_parity_and_decode_bitwise(Hq, Hkv):
 
 @pytest.mark.parametrize("lens,qlens", [
     ([2000], [700]),                            # one sequence: pending subtrees only
+    ([3000], [300]),                            # one sequence, few blocks: chunk-pair nodes
+    ([700], [700]),                             # the same with a lone last chunk
+    ([20000], [500]),                           # few blocks over 79 chunks: stacks again
     ([1500, 900, 300], [400, 7, 300]),          # leaves of short runs indexed per sequence
     ([1024] * 40, [100] + [1] * 39),            # leaves indexed per token, stacks among them
 ])
