@@ -18,23 +18,12 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_floa
 // fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN
 // (bits 31..16 with the quiet bit set).  gfx950 converts in one instruction
 // (v_cvt_pk_bf16_f32, two values at a time), which gives exactly those bits for
-// all 2^32 inputs (checked exhaustively on the GPU against the integer
-// formulation u + 0x7fff + ((u >> 16) & 1), NaNs included).  The integer form
+// all 2^32 inputs (a GPU test checks it exhaustively against the integer rule
+// u + 0x7fff + ((u >> 16) & 1), NaNs included).  The integer form
 // cost up to seven vector instructions per value and, written with an early
 // return for NaN, a branch with exec-mask save / restore around each one.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
-}
-
-// The integer formulation of the same function, with the NaN case as a
-// branch.  The decode chunk kernel sits at its 128-VGPR budget, and with the
-// hardware conversion (or a branch-free integer one) its register allocation
-// spills; with this form it does not.
-__device__ __forceinline__ uint32_t f32_to_bf16_branch(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
 }
 
 // two fp32 -> packed pair of bf16 (lo in bits 0..15)

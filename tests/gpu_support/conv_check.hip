@@ -1,18 +1,19 @@
 // conv_check.hip -- test-only kernel: the two fp32 -> bf16 conversions of the
-// library (csrc/common.hpp) over every one of the 2^32 fp32 bit patterns.
+// library over every one of the 2^32 fp32 bit patterns.
 //
-// f32_to_bf16 (gfx950's v_cvt_pk_bf16_f32) is what the prefill block kernel,
-// the GEMM and RMSNorm use; f32_to_bf16_branch (integer round to nearest even,
-// NaN quieted) is what the decode chunk kernel uses for p.  Prefill rows equal
-// decode rows bit for bit only if the two agree on every input.  Each is also
-// compared with the rule written out here from the format's definition:
+// f32_to_bf16 (csrc/common.hpp, one value) is how the GEMM, RMSNorm, the glue
+// and the attention outputs round; p_pack (csrc/attn_chunk.hpp, a pair, gfx950's
+// v_cvt_pk_bf16_f32) is how every attention kernel rounds its softmax weights.
+// Both must be round to nearest even on every input -- the rounding the oracle
+// applies -- and the pair's two halves must agree.  Each is compared with the
+// rule written out here from the format's definition:
 //   NaN (exponent all ones, mantissa != 0) -> top 16 bits with the quiet bit set;
 //   otherwise add 0x7fff plus the lowest kept bit, keep the top 16 bits.
 // Built into its own library by the package build; never linked into libbinv.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../invariant_deterministic_fixed_amd/csrc/common.hpp"
+#include "../../invariant_deterministic_fixed_amd/csrc/attn_chunk.hpp"
 
 namespace {
 
@@ -26,9 +27,9 @@ __device__ __forceinline__ uint32_t spec_bf16(uint32_t u) {
 constexpr int THREADS = 256;
 constexpr int PER_THREAD = 256;          // 2^32 = 65536 blocks x 256 threads x 256
 
-// counts[3 * block + k]: mismatches of (hw vs branch, hw vs spec, branch vs
-// spec) among the block's 65536 inputs; first[block]: the lowest input of the
-// block where any of them differ (0xffffffff if none)
+// counts[3 * block + k]: mismatches of (pair low half vs scalar, scalar vs
+// spec, pair high half vs spec) among the block's 65536 inputs; first[block]:
+// the lowest input of the block where any of them differ (0xffffffff if none)
 __global__ __launch_bounds__(THREADS) void conv_check_kernel(uint32_t* counts, uint32_t* first) {
     __shared__ uint32_t c_hw_br[THREADS], c_hw_sp[THREADS], c_br_sp[THREADS], f_min[THREADS];
     const uint32_t base = (uint32_t)blockIdx.x * (THREADS * PER_THREAD);
@@ -37,9 +38,9 @@ __global__ __launch_bounds__(THREADS) void conv_check_kernel(uint32_t* counts, u
         const uint32_t u = base + (uint32_t)i * THREADS + threadIdx.x;
         const float f = __uint_as_float(u);
         const uint32_t hw = binv::f32_to_bf16(f) & 0xffffu;
-        const uint32_t br = binv::f32_to_bf16_branch(f) & 0xffffu;
+        const uint32_t pk = binv::attn::p_pack(f, f);
         const uint32_t sp = spec_bf16(u);
-        const bool d1 = hw != br, d2 = hw != sp, d3 = br != sp;
+        const bool d1 = (pk & 0xffffu) != hw, d2 = hw != sp, d3 = (pk >> 16) != sp;
         a += d1; b += d2; c += d3;
         if ((d1 || d2 || d3) && u < fm) fm = u;
     }

@@ -1,14 +1,15 @@
-"""The two fp32 -> bf16 conversions the kernels use agree on every input.
+"""The two fp32 -> bf16 conversions the kernels use are round to nearest even
+on every input.
 
-The decode chunk kernel rounds p with the integer formulation
-(f32_to_bf16_branch) and the prefill block kernel, GEMM and RMSNorm with
-gfx950's conversion instruction (f32_to_bf16); a prefill row equals the
-decode of the same position bit for bit only if the two give the same bits
-for every fp32 value (tom-jerr.github.io "Batch-Invariant Kernel", Flash
-Attention: prefill and decode intermediates bit-identical).  A test-only
-kernel (tests/gpu_support/conv_check.hip, built by the package build) runs
-both, and the round-to-nearest-even rule written out from the format's
-definition, over all 2^32 bit patterns, NaNs included."""
+The GEMM, RMSNorm, glue and attention outputs round with f32_to_bf16 (one
+value); every attention kernel rounds its softmax weights with p_pack (a pair,
+gfx950's v_cvt_pk_bf16_f32).  Decode and prefill form the same intermediates
+only with the same rounding everywhere (tom-jerr.github.io "Batch-Invariant
+Kernel", Flash Attention: prefill and decode intermediates bit-identical), and
+the oracle rounds to nearest even.  A test-only kernel
+(tests/gpu_support/conv_check.hip, built by the package build) runs both, and
+the round-to-nearest-even rule written out from the format's definition, over
+all 2^32 bit patterns, NaNs included."""
 import ctypes
 import os
 
@@ -34,10 +35,10 @@ def test_bf16_conversions_agree_on_all_2_32_inputs():
     assert st == 0
     torch.cuda.synchronize()
     c = counts.cpu().numpy().astype(np.int64).reshape(-1, 3)
-    hw_vs_branch, hw_vs_rule, branch_vs_rule = (int(x) for x in c.sum(axis=0))
+    pair_vs_scalar, scalar_vs_rule, pair_hi_vs_rule = (int(x) for x in c.sum(axis=0))
     f = first.cpu().numpy().view(np.uint32)
     bad = f[f != 0xFFFFFFFF]
-    print(f"mismatches over 2^32 inputs: hw vs branch {hw_vs_branch}, hw vs rule {hw_vs_rule}, "
-          f"branch vs rule {branch_vs_rule}", flush=True)
-    assert (hw_vs_branch, hw_vs_rule, branch_vs_rule) == (0, 0, 0), \
+    print(f"mismatches over 2^32 inputs: pair (low half) vs scalar {pair_vs_scalar}, scalar vs "
+          f"rule {scalar_vs_rule}, pair (high half) vs rule {pair_hi_vs_rule}", flush=True)
+    assert (pair_vs_scalar, scalar_vs_rule, pair_hi_vs_rule) == (0, 0, 0), \
         f"first differing inputs: {[hex(int(x)) for x in bad[:8]]}"
