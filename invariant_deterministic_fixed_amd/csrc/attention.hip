@@ -56,22 +56,37 @@ namespace binv {
 namespace {
 using namespace attn;
 
-// workgroups per (query tile, KV head) of a decode sequence; they loop over
-// the sequence's nodes
+// workgroups per (query tile, KV head) of a sequence; they loop over the
+// sequence's nodes (decode) or chunks (prefill)
 constexpr int CHUNK_LANES = 32;
 
+// Decode scheduling, from the batch size only (neither reaches a row's bits):
+// from 4 sequences on a workgroup computes at least a pair of chunks (its
+// start -- page-table entries, then K and V -- costs about two chunks' worth
+// of compute, and with many rows in flight fewer, longer chains stream the
+// cache faster); from 128 on, at most 16 workgroups per sequence.  Measured
+// at B = 256 (log-uniform lengths 128..32768): 5.09 -> 5.35 TB/s.
+struct DecodeSched {
+    int lanes, lmin;
+};
+DecodeSched decode_sched(int64_t B) {
+    return DecodeSched{B >= 128 ? 16 : CHUNK_LANES, B >= 4 ? 1 : 0};
+}
+
 // Level of the merge tree at which a decode row's partials are handed from
-// the chunk kernel to the merge kernel, from the row's chunk count n: the
-// level that keeps the longest chain of chunks one workgroup computes in
-// sequence, ceil(n / (CHUNK_LANES 2^L)) 2^L, shortest, and among those the
-// highest (fewest partials).  Both kernels evaluate it for the row; the root
-// is the same for every level.
+// the chunk kernel to the merge kernel, from the row's chunk count n and the
+// call's workgroups per sequence (lanes) and lowest level (lmin, 0 or 1): the
+// level from lmin up that keeps the longest chain of chunks one workgroup
+// computes in sequence, ceil(n / (lanes 2^L)) 2^L, shortest, and among those
+// the highest (fewest partials).  Both kernels evaluate it for the row; the
+// root is the same for every level, so lanes and lmin are scheduling only.
 template <int GMAX>
-__device__ __forceinline__ int node_level(int n) {
-    int best = 0, best_chain = (n + CHUNK_LANES - 1) / CHUNK_LANES;
+__device__ __forceinline__ int node_level(int n, int lanes, int lmin) {
+    int best = lmin, best_chain = ((n + (lanes << lmin) - 1) / (lanes << lmin)) << lmin;
 #pragma unroll
     for (int L = 1; L <= GMAX; ++L) {
-        const int per = CHUNK_LANES << L;
+        if (L <= lmin) continue;
+        const int per = lanes << L;
         const int chain = ((n + per - 1) / per) << L;
         if (chain <= best_chain) { best = L; best_chain = chain; }
     }
@@ -89,7 +104,7 @@ __device__ __forceinline__ int node_level(int n) {
 // node's chunks past the sequence end are identity leaves, which leave a
 // subtree unchanged).  Which workgroup takes a node, and the level at which
 // the tree is handed over, do not enter any row's arithmetic; a higher level
-// writes and re-reads fewer partials.  gridDim.y is capped at CHUNK_LANES, so
+// writes and re-reads fewer partials.  gridDim.y is capped at the call's lanes, so
 // a grid sized for the longest allowed sequence does not spend a workgroup
 // per empty node slot of every short sequence.
 // Prefill (cu_q given; R = 1, looping): leaves (L = 0), for the sequences of
@@ -110,7 +125,7 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     const int32_t* __restrict__ page_table, int64_t pt_stride,
     const int32_t* __restrict__ kv_lens, float* __restrict__ ws_o,
     float2* __restrict__ ws_ml, int Hq, int Hkv, int n_chunks, int max_kv_len,
-    float scale_log2, int q_skip, int leaf_seq) {
+    float scale_log2, int q_skip, int leaf_seq, int lanes, int lmin) {
     // prefill: sequences with q_skip or more new tokens belong to the block kernel
     if (cu_q && cu_q[blockIdx.z + 1] - cu_q[blockIdx.z] >= q_skip) return;
     static_assert(LOOP || GMAX == 0, "workgroups that take one chunk write leaves");
@@ -119,7 +134,8 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     const int kv_len_b = kv_lens[blockIdx.z];          // read once, kept in a register
     const int pos_max = tile_ctx_len<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
                                            kv_len_b, pt_stride, max_kv_len).pos_max;
-    const int glog = (GMAX > 0 && !cu_q && pos_max >= 0) ? node_level<GMAX>(pos_max / CHUNK + 1) : 0;
+    const int glog =
+        (GMAX > 0 && !cu_q && pos_max >= 0) ? node_level<GMAX>(pos_max / CHUNK + 1, lanes, lmin) : 0;
     const int gs = 1 << glog;
     int phys_next[JT];
     // K of the workgroup's current chunk: the first chunk's requested here,
@@ -647,7 +663,7 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ kv_lens, int64_t B,
     int64_t n_tokens, int Hq, int n_chunks, int max_kv_len,
     const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, bf16_t* __restrict__ out,
-    int q_min, int leaf_seq, int node_stride, int pf_level) {
+    int q_min, int leaf_seq, int node_stride, int pf_level, int lanes, int lmin) {
     constexpr int VPL = MERGE_VPL, LPR = D / VPL, RPW = 64 / LPR;
     static_assert(D % VPL == 0 && 64 % LPR == 0, "");
     typedef float Vec __attribute__((ext_vector_type(VPL)));
@@ -690,7 +706,7 @@ __global__ __launch_bounds__(NT) void attn_merge_kernel(
     // (leaves, or the block kernel's chunk pairs)
     int n_leaf = pos / CHUNK + 1;
     if (n_leaf > n_chunks) n_leaf = n_chunks;
-    const int glog = cu_q ? pf_level : (GMAX > 0 ? node_level<GMAX>(n_leaf) : 0);
+    const int glog = cu_q ? pf_level : (GMAX > 0 ? node_level<GMAX>(n_leaf, lanes, lmin) : 0);
     const int n = ((n_leaf - 1) >> glog) + 1;
 
     // node c of the row: slot (leaf_row * node_stride + c) * Hq + head
@@ -861,21 +877,24 @@ Regions regions_of(const Layout& L, float* ws, int Hq, int D) {
 // with q_skip or more new tokens are left to the block kernel
 template <int D, int G, int R, bool LOOP, int GMAX>
 hipError_t launch_chunk(const AttnArgs& a, hipStream_t s, int64_t nqt, int q_skip,
-                        const Regions& rg, int leaf_seq) {
+                        const Regions& rg, int leaf_seq,
+                        DecodeSched ds = DecodeSched{CHUNK_LANES, 0}) {
     const int n_chunks = (int)n_chunks_of(a.max_kv_len);
     dim3 grid1((unsigned)(nqt * a.Hkv),
-               (unsigned)(LOOP && n_chunks > CHUNK_LANES ? CHUNK_LANES : n_chunks), (unsigned)a.B);
+               (unsigned)(LOOP && n_chunks > ds.lanes ? ds.lanes : n_chunks), (unsigned)a.B);
     hipLaunchKernelGGL((attn_chunk_kernel<D, G, R, LOOP, GMAX>), grid1, dim3(ChunkShape<D>::NTH),
                        0, s, (const bf16_t*)a.q, a.cu_q, (const bf16_t*)a.k_cache,
                        (const bf16_t*)a.v_cache, a.page_table, a.pt_stride, a.kv_lens, rg.leaf_o,
                        rg.leaf_ml, a.Hq, a.Hkv, n_chunks, (int)a.max_kv_len, a.scale_log2, q_skip,
-                       leaf_seq);
+                       leaf_seq, ds.lanes, ds.lmin);
     return hipGetLastError();
 }
 
 template <int D, int GMAX>
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s, const Regions& rg, int q_min,
-                        int leaf_seq, int pf_level = 0, int node_stride = 0) {
+                        int leaf_seq, int pf_level = 0, int node_stride = 0,
+                        DecodeSched ds = DecodeSched{CHUNK_LANES, 0}) {
+    const int lanes = ds.lanes, lmin = ds.lmin;
     const int n_chunks = (int)n_chunks_of(a.max_kv_len);
     if (node_stride == 0) node_stride = n_chunks;
     const int64_t Rows = a.n_tokens * a.Hq;
@@ -887,17 +906,17 @@ hipError_t launch_merge(const AttnArgs& a, hipStream_t s, const Regions& rg, int
         hipLaunchKernelGGL((attn_merge_kernel<D, GMAX, 5>), grid2, dim3(NT), 0, s, a.cu_q,
                            a.kv_lens, a.B, a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len,
                            rg.leaf_o, rg.leaf_ml, (bf16_t*)a.out, q_min, leaf_seq, node_stride,
-                           pf_level);
+                           pf_level, lanes, lmin);
     else if (n_chunks <= 255)
         hipLaunchKernelGGL((attn_merge_kernel<D, GMAX, 8>), grid2, dim3(NT), 0, s, a.cu_q,
                            a.kv_lens, a.B, a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len,
                            rg.leaf_o, rg.leaf_ml, (bf16_t*)a.out, q_min, leaf_seq, node_stride,
-                           pf_level);
+                           pf_level, lanes, lmin);
     else
         hipLaunchKernelGGL((attn_merge_kernel<D, GMAX, STACK>), grid2, dim3(NT), 0, s, a.cu_q,
                            a.kv_lens, a.B, a.n_tokens, a.Hq, n_chunks, (int)a.max_kv_len,
                            rg.leaf_o, rg.leaf_ml, (bf16_t*)a.out, q_min, leaf_seq, node_stride,
-                           pf_level);
+                           pf_level, lanes, lmin);
     return hipGetLastError();
 }
 
@@ -905,9 +924,11 @@ template <int D, int G, int R, bool LOOP, int GMAX>
 hipError_t launch_dgr(const AttnArgs& a, hipStream_t s, const Regions& rg) {
     constexpr int TQ = ROWS * R / G;
     const int64_t nqt = a.cu_q ? (a.max_q_len + TQ - 1) / TQ : 1;
-    hipError_t e = launch_chunk<D, G, R, LOOP, GMAX>(a, s, nqt, 0x7fffffff, rg, 0);
+    // decode calls take the batch-size schedule; prefill calls (leaves) the default
+    const DecodeSched ds = a.cu_q ? DecodeSched{CHUNK_LANES, 0} : decode_sched(a.B);
+    hipError_t e = launch_chunk<D, G, R, LOOP, GMAX>(a, s, nqt, 0x7fffffff, rg, 0, ds);
     if (e != hipSuccess) return e;
-    return launch_merge<D, GMAX>(a, s, rg, 0x7fffffff, 0);
+    return launch_merge<D, GMAX>(a, s, rg, 0x7fffffff, 0, 0, 0, ds);
 }
 
 // Prefill at D = 128 with long new-token runs: sequences with at least
