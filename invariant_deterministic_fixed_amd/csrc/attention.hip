@@ -131,6 +131,18 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     static_assert(LOOP || GMAX == 0, "workgroups that take one chunk write leaves");
     __shared__ ChunkLds<D, R> sh;
     constexpr int JT = ChunkShape<D>::JT;
+    // the page-table entries of the first node at the call's lowest level,
+    // requested before the sequence's length (which fixes the level) arrives:
+    // entries within the row may be read ahead, and they are used only if the
+    // row's level turns out to be that one (every prefill row; decode rows of
+    // up to 2 lanes chunks at lmin = 1)
+    const int c_spec = (GMAX > 0 && !cu_q) ? ((int)blockIdx.y << lmin) : (int)blockIdx.y;
+    int phys_spec[JT];
+    {
+        TileCtx xs;
+        xs.pt_row = (int64_t)blockIdx.z * pt_stride;
+        load_phys<D>(xs, c_spec, page_table, pt_stride, phys_spec, threadIdx.x);
+    }
     const int kv_len_b = kv_lens[blockIdx.z];          // read once, kept in a register
     const int pos_max = tile_ctx_len<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv, cu_q,
                                            kv_len_b, pt_stride, max_kv_len).pos_max;
@@ -144,7 +156,12 @@ __global__ __launch_bounds__(ChunkShape<D>::NTH, D == 128 ? 4 : 3) void attn_chu
     {
         TileCtx x0;
         x0.pt_row = (int64_t)blockIdx.z * pt_stride;
-        load_phys<D>(x0, blockIdx.y * gs, page_table, pt_stride, phys_next, threadIdx.x);
+        if ((int)blockIdx.y * gs == c_spec) {
+#pragma unroll
+            for (int u = 0; u < JT; ++u) phys_next[u] = phys_spec[u];
+        } else {
+            load_phys<D>(x0, blockIdx.y * gs, page_table, pt_stride, phys_next, threadIdx.x);
+        }
         if (blockIdx.y * gs * CHUNK <= pos_max) {
             const TileCtx x1 = tile_ctx_len<G, R>(blockIdx.z, blockIdx.x % Hkv, blockIdx.x / Hkv,
                                                   cu_q, kv_len_b, pt_stride, max_kv_len);
