@@ -535,8 +535,8 @@ def sweep(dev="cuda:0"):
     # 8B-class decoder: decode tokens/s at batch B with 1024-token contexts, all
     # invariant, all tuned, and one locked request among tuned neighbours; each
     # step replayed as a HIP graph (the serving configuration) and issued
-    # eagerly (every kernel launched from Python).  The invariant products of
-    # up to 16 rows read strip-packed weights (same bits as row-major)
+    # eagerly (every kernel launched from Python).  The invariant decode-size
+    # products read strip-packed weights (decoder.PACKED_ROWS; same bits)
     cfg = dec.CONFIG5
     w = dec.random_weights(cfg, 5, dev)
     packed = dec.pack_weights(w)
@@ -594,7 +594,7 @@ def decoder_tokens_per_s(w, packed, B, mode, graph, steps, dev="cuda:0"):
     (untimed), one untimed decode step (a graph's capture), then `steps` timed
     decode steps of one token per sequence; returns tokens/s.  mode: invariant,
     tuned (the comparators), or locked (sequence 0 invariant among tuned ones);
-    invariant products of up to 16 rows read `packed` (not with tuned)."""
+    invariant decode-size products read `packed` (not with tuned)."""
     import numpy as np
     import torch
     from invariant_deterministic_fixed_amd import decoder as dec

@@ -53,15 +53,24 @@ def random_weights(cfg, seed, device, std=0.02):
     return w
 
 
+# Rows up to which an invariant product reads the packed copy of a weight
+# (measured per shape: the packed product is faster up to 64 rows for the
+# QKV, output and down projections, up to 16 for the 28672-wide gate-up
+# projection and the LM head, whose many strips favour the row-major kernels
+# beyond that).  The bits are the same either way.
+PACKED_ROWS = {"wqkv": 64, "wo": 64, "wd": 64, "wgu": 16, "lm_head": 16}
+
+
 def pack_weights(w):
     """Strip-packed copies (binv_gemm_bf16_pack) of every projection and of the
     LM head, keyed by the row-major tensor's id, for Decoder(packed=...):
-    invariant products of up to Decoder.PACKED_ROWS rows then read them, with
+    invariant products of up to PACKED_ROWS[name] rows then read them, with
     the bits of the row-major product (the packed entry point runs the same
     per-element chain) at a higher weight stream rate, for one more copy of
     those weights in HBM."""
-    ws = [w["lm_head"]] + [lw[n] for lw in w["layers"] for n in ("wqkv", "wo", "wgu", "wd")]
-    return {id(t): (t, B.gemm_pack(t)) for t in ws}
+    ws = [("lm_head", w["lm_head"])] + [(n, lw[n]) for lw in w["layers"]
+                                        for n in ("wqkv", "wo", "wgu", "wd")]
+    return {id(t): (t, B.gemm_pack(t), PACKED_ROWS[n]) for n, t in ws}
 
 
 class KVPool:
@@ -142,7 +151,8 @@ class Decoder:
     are not batch-invariant.
 
     packed: pack_weights(weights), or None for row-major weights only; the
-    bits are the same either way."""
+    bits are the same either way (products of more than a weight's
+    PACKED_ROWS rows read the row-major weights)."""
 
     def __init__(self, weights, cfg, pool, max_tokens, max_seqs, max_kv_len, topk=20,
                  tuned=False, packed=None):
@@ -169,9 +179,6 @@ class Decoder:
         self.max_tokens, self.max_seqs = T, max_seqs
         self._graphs = {}
         self._packed = packed if packed is not None else {}
-
-    # at most this many rows go through the packed-weight products
-    PACKED_ROWS = 16
 
     def step(self, items, protected=None, on_layer=None, graph=False):
         """items: list of (slot, new token ids, start position).  Returns
@@ -272,7 +279,7 @@ class Decoder:
             pk = self._packed.get(id(wt))
             for sl, t in blocks:
                 n = src[sl].shape[0]
-                if n and pk is not None and not t and n <= self.PACKED_ROWS:
+                if n and pk is not None and not t and n <= pk[2]:
                     B.gemm_packed(src[sl], pk[1], out=dst[sl])
                 elif n:
                     B.gemm(src[sl], wt, out=dst[sl], tuned=t)

@@ -235,9 +235,10 @@ def test_small_decoder_graph_steps_equal_eager(small):
 
 def test_small_decoder_packed_weights_equal_row_major(small):
     # a decoder reading strip-packed weights for its decode-size products gives
-    # the bits of one reading the row-major weights: prompts (products of 40 to
-    # 120 rows, row-major on both), then decode steps of 1, 3 and 16 rows, the
-    # last also with a locked block
+    # the bits of one reading the row-major weights: prompts of 20 to 120 rows
+    # (up to 64 of them the QKV, output and down projections read the packed
+    # copies), then decode steps of 1, 3 and 16 rows, the last also with a
+    # locked block
     w, _, _, _ = small
     packed = dec.pack_weights(w)
 
