@@ -272,6 +272,31 @@ def test_longest_rows_and_max_kv_len_bound_change_no_bits():
         assert row_rel_err(f64(outs[0][i:i + 1]), ref).max() <= TOL_BF16, p
 
 
+def test_rows_at_the_maximum_kv_length():
+    # A sequence of the library's maximum length fills all 512 leaves of the
+    # merge tree.  Its last 128 positions as one prefill run (block kernel,
+    # the deepest stack of pending subtrees) and as decode rows (nodes of up
+    # to four chunks, then the merge over every level) give the same bits;
+    # a middle row and the last row of the run against the oracle.
+    Hq, Hkv, D = 32, 8, 128
+    L = bd.MAX_KV_LEN
+    scale = 1 / math.sqrt(D)
+    k, v = synth.random_kv(L, Hkv, D, 141, DEV)
+    cache, _ = make_cache([L], Hkv, D, 142, seqs=[(k, v)])
+    n = 128
+    q = synth.normal((n, Hq, D), 1.0, 143, DEV)
+    pre = _prefill(cache, q, np.array([0, n], dtype=np.int32), [L], n, L, scale)
+    pos = np.arange(L - n, L, dtype=np.int64)
+    pt = cache.page_table[:1].expand(n, -1).contiguous()
+    kv = torch.as_tensor(pos + 1, dtype=torch.int32, device=DEV)
+    dec = binv.attn_decode(q, cache.k_cache, cache.v_cache, pt, kv, L, scale)
+    assert_bitwise_equal(dec, pre, "decode vs prefill at the maximum length")
+    kd, vd = f64(k), f64(v)
+    for i in (n // 2, n - 1):
+        ref = oracle.attention(f64(q[i:i + 1]), [int(pos[i])], kd, vd, scale)
+        assert row_rel_err(f64(pre[i:i + 1]), ref).max() <= TOL_BF16, i
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (32, 2)])
 def test_prefill_head_groups_parity_and_decode_bitwise(Hq, Hkv):
     # D = 128 prefill blocks hold 128 / G tokens: G = 1, 8 and 16 besides the
