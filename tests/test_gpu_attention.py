@@ -272,6 +272,31 @@ def test_longest_rows_and_max_kv_len_bound_change_no_bits():
         assert row_rel_err(f64(outs[0][i:i + 1]), ref).max() <= TOL_BF16, p
 
 
+def test_decode_at_the_maximum_batch():
+    # B = 65535, the largest batch the decode entry point takes: 48 distinct
+    # sequences of 1 .. 48 keys, each shared by the page-table rows of ~1365
+    # batch rows.  Sampled rows against the oracle, and against the same row
+    # decoded alone, bit for bit.
+    Hq, Hkv, D = 32, 8, 128
+    B = 65535
+    base_lens = list(range(1, 49))
+    cache, seqs = make_cache(base_lens, Hkv, D, 151)
+    s_of = np.arange(B) % len(base_lens)
+    pt = cache.page_table[torch.as_tensor(s_of, device=DEV)].contiguous()
+    kv = torch.as_tensor(np.array(base_lens)[s_of], dtype=torch.int32, device=DEV)
+    q = synth.normal((B, Hq, D), 1.0, 152, DEV)
+    scale = 1 / math.sqrt(D)
+    out = binv.attn_decode(q, cache.k_cache, cache.v_cache, pt, kv, 48, scale)
+    for b in (0, 1, 47, 48, 12345, 40000, B - 2, B - 1):
+        s = int(s_of[b])
+        k, v = seqs[s]
+        ref = oracle.attention(f64(q[b:b + 1]), [base_lens[s] - 1], f64(k), f64(v), scale)
+        assert row_rel_err(f64(out[b:b + 1]), ref).max() <= TOL_BF16, b
+        alone = binv.attn_decode(q[b:b + 1].contiguous(), cache.k_cache, cache.v_cache,
+                                 pt[b:b + 1].contiguous(), kv[b:b + 1].contiguous(), 48, scale)
+        assert_bitwise_equal(alone, out[b:b + 1], f"row {b} alone vs in the batch")
+
+
 def test_rows_at_the_maximum_kv_length():
     # A sequence of the library's maximum length fills all 512 leaves of the
     # merge tree.  Its last 128 positions as one prefill run (block kernel,
