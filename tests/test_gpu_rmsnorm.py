@@ -51,6 +51,21 @@ def test_parity_bf16_rows_with_outliers(M, d):
     assert row_rel_err(f64(yf), ref).max() <= 1e-5
 
 
+@pytest.mark.parametrize("x_dtype,d", [(torch.bfloat16, 8), (torch.bfloat16, 16384),
+                                       (torch.float32, 4), (torch.float32, 8192)])
+def test_parity_smallest_and_largest_feature_size(x_dtype, d):
+    # the feature sizes at the ends of the supported range (d a multiple of 8
+    # for bf16 rows, of 4 for fp32, up to 16384 / 8192): against the oracle,
+    # and a row's bits the same alone and in a batch of 300
+    M = 300
+    x, g = rms_case(M, d, synth.seed_for(3) + d, x_dtype)
+    y = binv.rmsnorm(x.to(DEV), g.to(DEV), EPS, out_dtype=torch.float32)
+    assert row_rel_err(f64(y), oracle_rms(x, g)).max() <= 1e-5
+    for r in (0, 151, M - 1):
+        alone = binv.rmsnorm(x[r:r + 1].to(DEV), g.to(DEV), EPS, out_dtype=torch.float32)
+        assert_bitwise_equal(alone, y[r:r + 1], f"row {r} alone vs in the batch, d = {d}")
+
+
 def test_parity_full_size_sampled_rows():
     M, d = 16384, 4096
     x, g = rms_case(M, d, synth.seed_for(3))
