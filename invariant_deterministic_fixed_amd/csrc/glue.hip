@@ -200,11 +200,15 @@ __global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ x
 //   more than TOPK_EQ_MAX entries equal to T, or fewer than K non-NaN entries:
 //   one index-ordered pass over the row (ballots and wave prefix counts) takes
 //   the keys > T and the first keys == T, stopping once all are placed.
+// A row longer than TOPK_SEG entries runs steps 1-3 over its first TOPK_SEG
+// entries and then reads the rest once (topk_kernel), so it is read about
+// once instead of twice.
 // The <= 32 winners are then ranked by (value desc, index asc).
 constexpr int TOPK_MAX = 32;
 constexpr int TOPK_NT = 1024;
 constexpr int TOPK_NW = TOPK_NT / 64;
 constexpr int TOPK_CAND = 4096;
+constexpr int TOPK_SEG = 16384;       // prefix of a long row selected first
 
 __device__ __forceinline__ uint32_t order_key(float v) {
     uint32_t b = __float_as_uint(v);
@@ -433,14 +437,10 @@ __device__ void rank_equal(TopkShared& sh, const float* row, uint32_t n_eq_all, 
     }
 }
 
-__global__ __launch_bounds__(TOPK_NT) void topk_kernel(const float* __restrict__ x, int64_t ldx,
-                                                       int64_t n, int K,
-                                                       int32_t* __restrict__ ids,
-                                                       float* __restrict__ vals) {
-    __shared__ TopkShared sh;
-    const int64_t r = blockIdx.x;
-    const float* row = x + r * ldx;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+// Steps 1-3 above over entries 0 .. n-1 of `row`: the K winners into sel
+// (slot order arbitrary; slots of missing entries hold index -1).
+__device__ void topk_select(TopkShared& sh, const float* row, int64_t n, int K) {
+    const int t = threadIdx.x;
     auto from_row = [&](int64_t j) { return row[j]; };
     // values 4i .. 4i+3 of the row, NaN past n; one 16-byte read when the row
     // is 16-byte aligned and the four are inside it
@@ -459,7 +459,8 @@ __global__ __launch_bounds__(TOPK_NT) void topk_kernel(const float* __restrict__
     uint32_t prefix = 0u, mask = 0u, need = (uint32_t)K;
     const bool ok1 = radix_select<4, TOPK_HB>(sh, row4, row4_vec, row_vec, n, 32 - TOPK_HB,
                                               32 - TOPK_HB, prefix, mask, need);
-    const uint32_t top = prefix >> (32 - TOPK_HB), gt1 = (uint32_t)K - need;
+    const uint32_t top = prefix >> (32 - TOPK_HB);
+    [[maybe_unused]] const uint32_t gt1 = (uint32_t)K - need;     // winners above bucket `top`
 
     // ---- 2. one pass over the row: entries above the bucket go to sel slots
     // [0, gt1), the bucket's entries to the candidate list.  Each wave reserves
@@ -547,6 +548,106 @@ __global__ __launch_bounds__(TOPK_NT) void topk_kernel(const float* __restrict__
         collect(sh, from_row, n, [&](uint32_t k) { return found && k > Tc; },
                 [&](uint32_t k) { return found ? k == Tc : k >= Tc; }, 0u, eq_base, n_eq,
                 (uint32_t)K - n_eq);
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(TOPK_NT) void topk_kernel(const float* __restrict__ x, int64_t ldx,
+                                                       int64_t n, int K,
+                                                       int32_t* __restrict__ ids,
+                                                       float* __restrict__ vals) {
+    __shared__ TopkShared sh;
+    const int64_t r = blockIdx.x;
+    const float* row = x + r * ldx;
+    const int t = threadIdx.x;
+    // A long row is read once, not twice: the winners of its first TOPK_SEG
+    // entries (two passes over 64 KB, the second from the cache) fix the key
+    // T0 of the prefix's K-th entry.  An entry past the prefix can only be a
+    // winner if its key is above T0 (an entry with key T0 there has a higher
+    // index than the prefix's K winners, and loses to all of them), so one pass
+    // over the rest lists those entries as candidates beside the prefix's
+    // winners, and the K winners of the row are the K winners among the
+    // candidates, found as in step 3 (the K-th key by three radix digits, the
+    // entries above it, the lowest indices among those equal to it).  A prefix
+    // with fewer than K non-NaN entries, more candidates than the list holds,
+    // or more entries equal to the K-th key than are ranked in LDS: the whole
+    // row through steps 1-3.
+    const int64_t n1 = n > TOPK_SEG ? (int64_t)TOPK_SEG : n;
+    topk_select(sh, row, n1, K);
+    if (n > n1) {
+        __syncthreads();
+        if (t == 0) { sh.s_prefix = 0xffffffffu; sh.s_need = 1u; sh.n_cand = (uint32_t)K; }
+        __syncthreads();
+        if (t < K) {
+            if (sh.sel_i[t] < 0) atomicAnd(&sh.s_need, 0u);
+            else atomicMin(&sh.s_prefix, order_key(sh.sel_v[t]));
+            sh.cand_v[t] = sh.sel_v[t];
+            sh.cand_i[t] = sh.sel_i[t];
+        }
+        __syncthreads();
+        const bool full = sh.s_need != 0u;
+        const uint32_t T0 = sh.s_prefix;
+        bool done = false;
+        if (full) {
+            const float* rest = row + n1;
+            const int64_t m = n - n1;
+            const bool rest_vec = (reinterpret_cast<uintptr_t>(rest) & 15u) == 0u;
+            auto rest4 = [&](int64_t i) -> f32x4 {
+                const int64_t j = 4 * i;
+                f32x4 v;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = j + q < m ? rest[j + q] : NAN;
+                return v;
+            };
+            auto rest4_vec = [&](int64_t i) -> f32x4 { return *reinterpret_cast<const f32x4*>(rest + 4 * i); };
+            if (t == 0) sh.n_eq = 0u;
+            __syncthreads();
+            row_pass<2>(rest4, rest4_vec, rest_vec, m, [&](uint32_t key, float v, int64_t j,
+                                                          bool take, bool, uint32_t base, uint32_t,
+                                                          uint32_t rk, uint32_t) {
+                if (take && base + rk < (uint32_t)TOPK_CAND) {
+                    sh.cand_v[base + rk] = v;
+                    sh.cand_i[base + rk] = (int)(j + n1);
+                }
+            }, [&](uint32_t key) { return key > T0; }, [&](uint32_t) { return false; },
+               &sh.n_cand, &sh.n_eq);
+            __syncthreads();
+            const uint32_t nc = sh.n_cand;
+            if (nc <= (uint32_t)TOPK_CAND) {
+                auto cand4 = [&](int64_t i) -> f32x4 {
+                    f32x4 v;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = 4 * i + q < (int64_t)nc ? sh.cand_v[4 * i + q] : NAN;
+                    return v;
+                };
+                uint32_t prefix = 0u, mask = 0u, need = (uint32_t)K;
+                // at least K candidates (the prefix's winners): the K-th key exists
+                radix_select<1, 8>(sh, cand4, cand4, false, (int64_t)nc, 24, 0, prefix, mask, need);
+                const uint32_t T = prefix;
+                if (t < TOPK_MAX) { sh.sel_v[t] = -INFINITY; sh.sel_i[t] = -1; }
+                if (t == 0) { sh.n_gt = 0u; sh.n_eq = 0u; }
+                __syncthreads();
+                for (int64_t c = t; c < (int64_t)nc; c += TOPK_NT) {
+                    const uint32_t key = order_key(sh.cand_v[c]);
+                    if (key > T) {
+                        const uint32_t slot = atomicAdd(&sh.n_gt, 1u);
+                        if (slot < TOPK_MAX) { sh.sel_v[slot] = sh.cand_v[c]; sh.sel_i[slot] = sh.cand_i[c]; }
+                    } else if (key == T) {
+                        const uint32_t k = atomicAdd(&sh.n_eq, 1u);
+                        if (k < (uint32_t)TOPK_EQ_MAX) sh.eq_i[k] = sh.cand_i[c];
+                    }
+                }
+                __syncthreads();
+                if (sh.n_eq <= (uint32_t)TOPK_EQ_MAX) {
+                    rank_equal(sh, row, sh.n_eq, (uint32_t)K - need, need);
+                    done = true;
+                }
+            }
+        }
+        if (!done) {
+            __syncthreads();
+            topk_select(sh, row, n, K);
+        }
     }
     __syncthreads();
 

@@ -156,6 +156,39 @@ def test_topk_matches_oracle_across_paths(n, ldx):
         np.testing.assert_array_equal(vals[r].cpu().numpy(), want_vals.astype(np.float32))
 
 
+def test_topk_long_rows_prefix_then_rest():
+    # Rows longer than the kernel's 16384-entry prefix: the prefix's winners and
+    # the later entries above their K-th key decide, except where the kernel
+    # must fall back to the whole row -- every such case against the oracle.
+    n, K, P = 128256, 20, 16384
+    g = torch.Generator(device=DEV).manual_seed(77)
+    x = torch.randn((7, n), generator=g, device=DEV)
+    x[0, P + 5:P + 25] = 50.0                # all 20 winners past the prefix
+    x[1, :P] = float("nan")                  # prefix without K valid entries
+    x[2] = torch.arange(n, device=DEV, dtype=torch.float32)   # rising: too many candidates
+    x[3, :P] = 0.0                           # 300 ties past the prefix at the K-th key
+    x[3, 100:120] = 1.0
+    x[3, P:] = 0.0
+    perm = np.random.default_rng(5).permutation(n - P)[:300] + P
+    x[3, torch.as_tensor(perm, device=DEV)] = 2.0
+    x[4, :] = 0.0                            # the K-th key of the prefix, again later
+    x[4, 3:28] = 7.0
+    x[4, P + 1000:P + 1100] = 7.0
+    x[5, 17] = 9.0                           # one winner in the prefix, the rest later
+    x[5, P + 17::4000] = 8.0
+    x[6, n - 1] = 100.0                      # the last entry wins
+    ids, vals = binv.topk(x, K)
+    xc = x.cpu().numpy()
+    for r in range(7):
+        row = np.where(np.isnan(xc[r]), -np.inf, xc[r])
+        want_ids, want_vals = od.topk(row, K)
+        np.testing.assert_array_equal(ids[r].cpu().numpy(), want_ids, err_msg=f"row {r}")
+        np.testing.assert_array_equal(vals[r].cpu().numpy(), want_vals.astype(np.float32))
+    assert ids[0].tolist() == list(range(P + 5, P + 25))
+    assert ids[3].tolist() == sorted(perm.tolist())[:K]
+    assert ids[4].tolist() == list(range(3, 23))
+
+
 def test_topk_signed_zero_and_short_rows():
     x = torch.full((2, 64), float("nan"), device=DEV)
     x[0, :5] = torch.tensor([0.0, -0.0, 1.0, -0.0, 0.0], device=DEV)
