@@ -438,7 +438,9 @@ __device__ void rank_equal(TopkShared& sh, const float* row, uint32_t n_eq_all, 
 }
 
 // Steps 1-3 above over entries 0 .. n-1 of `row`: the K winners into sel
-// (slot order arbitrary; slots of missing entries hold index -1).
+// (slot order arbitrary; slots of missing entries hold index -1).  Left to
+// the compiler as a call: inlined at the kernel's two call sites (or at one,
+// inside a loop) it spilled registers in every pass over the row.
 __device__ void topk_select(TopkShared& sh, const float* row, int64_t n, int K) {
     const int t = threadIdx.x;
     auto from_row = [&](int64_t j) { return row[j]; };
