@@ -8,6 +8,9 @@ fp32 by the caller); every result is fp64.
 
 The arithmetic lives in ``oracle.c`` (plain C, fp64, reductions in ascending
 index order) and is loaded with ctypes; ``build()`` compiles it with gcc.
+``tiny.py`` is a second implementation of the same definitions, pure Python
+with exactly rounded sums and nothing shared with ``oracle.c``, against which
+the tests check this one on tiny inputs.
 """
 import ctypes
 import os
